@@ -1,0 +1,329 @@
+"""CPU oracle for single-request (batch-1) greedy transformer decode.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call this
+module: only the tests, the smoke check and the benchmark's CPU-baseline leg
+do. It shares no code with the device path; the two meet only in the seeded
+inputs of the ``synth`` package.
+
+What it computes follows the pages' statement of the problem:
+
+* agentlenshq.com article, "The memory-bandwidth bottleneck": each generated
+  token needs every active weight once; decode is batch 1.
+* paper-digest.app digest, "Core Mechanics": batch-1 decode of one request,
+  speed bounded by bandwidth / (active weight bytes + KV cache bytes).
+* news.creeta.com monokernel article, "Inside the monokernel": RMSNorm,
+  Q/K/V projections, rotary position embedding, attention over the cached
+  keys and values, and on-device greedy token sampling.
+
+The pages name the method's ingredients but not the block structure. The
+plainest reading, used here and listed with every other reading in the
+design notes, is a pre-norm residual decoder without biases::
+
+    x = E[t]
+    per layer:  h = rmsnorm(x) * g_attn
+                q, k, v = Wq h, Wk h, Wv h;  rotate q, k by position p
+                append k, v to the cache;  o = causal GQA attention
+                x = x + Wo o
+                h = rmsnorm(x) * g_ffn
+                x = x + Wd (silu(Wg h) * Wu h)      (MoE: sum over top-k experts)
+    logits = W_lm (rmsnorm(x) * g_final);  next token = argmax(logits)
+
+Arithmetic is float32 on the fp16 weights (fp16 -> fp32 is exact) unless a
+caller asks for float64; rotary angles are formed in float64.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Building blocks. Each is the plain definition, written out.
+# --------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis (eps inside the root).
+
+    Folded into the next projection on the device ("Inside the monokernel",
+    RMSNorm folding); here it is a separate step.
+    """
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return (x / np.sqrt(ms + x.dtype.type(eps))) * g.astype(x.dtype)
+
+
+def rope_angles(positions: Sequence[int] | np.ndarray, head_dim: int,
+                theta: float) -> Tuple[np.ndarray, np.ndarray]:
+    """cos and sin of p * theta^(-2i/head_dim), i < head_dim/2, in float64.
+
+    Rotary embedding is precomputed rather than recomputed per step on the
+    device ("Inside the monokernel", RoPE precompute); the oracle forms the
+    same angles directly. Shapes: [len(positions), head_dim/2].
+    """
+    half = head_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = np.power(np.float64(theta), -2.0 * i / head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(v: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate-half rotary embedding on the last axis.
+
+    Element i is paired with element i + head_dim/2:
+    (a, b) -> (a cos - b sin, b cos + a sin). ``cos``/``sin`` broadcast against
+    v[..., :head_dim/2].
+    """
+    half = v.shape[-1] // 2
+    a, b = v[..., :half], v[..., half:]
+    c = cos.astype(v.dtype)
+    s = sin.astype(v.dtype)
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """exp(s - max s) / sum(exp(s - max s)) over the last axis."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Grouped-query attention of one query position over c cached positions.
+
+    q: [H, hd]; K, V: [c, Hkv, hd] (positions 0..p, the current one included).
+    Query head j reads kv head j // (H / Hkv). Scores are scaled by 1/sqrt(hd).
+    Returns o: [H, hd].
+    """
+    H, hd = q.shape
+    Hkv = K.shape[1]
+    group = H // Hkv
+    scale = q.dtype.type(1.0 / np.sqrt(hd))
+    o = np.empty_like(q)
+    for j in range(H):
+        g = j // group
+        s = (K[:, g, :] @ q[j]) * scale
+        p = softmax(s)
+        o[j] = p @ V[:, g, :]
+    return o
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (z.dtype.type(1.0) + np.exp(-z))
+
+
+def swiglu_ffn(h: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> np.ndarray:
+    """Wd (silu(Wg h) * (Wu h))."""
+    return Wd @ (silu(Wg @ h) * (Wu @ h))
+
+
+def topk_experts(probs: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest router probabilities, ties to the lower index."""
+    order = np.argsort(-probs, kind="stable")
+    return order[:k]
+
+
+def greedy_argmax(logits: np.ndarray) -> int:
+    """Greedy sampling: the index of the largest logit, ties to the lowest index."""
+    return int(np.argmax(logits))
+
+
+def gemv_f64(A: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y = A x in float64 (the probe's reference: fp16 inputs are exact in f64)."""
+    return A.astype(np.float64) @ x.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# The decoder.
+# --------------------------------------------------------------------------
+
+class Decoder:
+    """Incremental batch-1 decoder with a KV cache, plus a full causal forward.
+
+    ``tensors`` is the canonical list from ``synth.make_weights``. State is a
+    position ``pos`` and a ``pending`` token, so that ``prefill``/``decode``
+    have the same meaning as the device library's calls:
+
+    * ``prefill(prompt)`` runs one pass per prompt token at positions
+      0..P-1 and returns the first generated token.
+    * ``decode(n, force)`` runs exactly n passes. Pass i feeds the pending
+      token at the current position and records argmax(logits) as output i;
+      the next pending token is that output, or ``force[i]`` when teacher
+      forcing.
+    """
+
+    def __init__(self, cfg, tensors: List[np.ndarray], dtype=np.float32,
+                 cache_experts: bool = False):
+        self.cfg = cfg
+        self.dtype = np.dtype(dtype)
+        self._raw = tensors
+        self._cache_experts = cache_experts
+        self._conv: Dict[int, np.ndarray] = {}
+        self._index = self._build_index()
+        L, S, Hkv, hd = cfg.n_layers, cfg.max_seq, cfg.n_kv_heads, cfg.head_dim
+        self.K = np.zeros((L, S, Hkv, hd), dtype=self.dtype)
+        self.V = np.zeros((L, S, Hkv, hd), dtype=self.dtype)
+        self.pos = 0
+        self.pending: Optional[int] = None
+        self.last_experts: List[np.ndarray] = []
+
+    # ---- weights ---------------------------------------------------------
+    def _build_index(self) -> Dict[str, int]:
+        from synth import tensor_specs  # shapes and order only, no arithmetic
+        specs = tensor_specs(self.cfg)
+        if len(specs) != len(self._raw):
+            raise ValueError("tensor list does not match the configuration")
+        for (name, shape, _), t in zip(specs, self._raw):
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name}: shape {t.shape} != {shape}")
+        return {name: i for i, (name, _, _) in enumerate(specs)}
+
+    def w(self, name: str) -> np.ndarray:
+        i = self._index[name]
+        hit = self._conv.get(i)
+        if hit is not None:
+            return hit
+        a = self._raw[i].astype(self.dtype)
+        if self._cache_experts or ".e" not in name:
+            self._conv[i] = a
+        return a
+
+    # ---- state -----------------------------------------------------------
+    def reset(self) -> None:
+        self.K[:] = 0
+        self.V[:] = 0
+        self.pos = 0
+        self.pending = None
+
+    def set_kv(self, K: np.ndarray, V: np.ndarray, pending_token: int) -> None:
+        """Store already-rotated keys and values at positions 0..n-1."""
+        n = K.shape[1]
+        self.K[:, :n] = K.astype(self.dtype)
+        self.V[:, :n] = V.astype(self.dtype)
+        self.K[:, n:] = 0
+        self.V[:, n:] = 0
+        self.pos = n
+        self.pending = int(pending_token)
+
+    # ---- one pass ----------------------------------------------------------
+    def _ffn(self, l: int, h: np.ndarray,
+             override: Optional[np.ndarray]) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+        cfg = self.cfg
+        if not cfg.n_experts:
+            return swiglu_ffn(h, self.w(f"l{l}.Wg"), self.w(f"l{l}.Wu"), self.w(f"l{l}.Wd")), None
+        probs = softmax(self.w(f"l{l}.Wr") @ h)
+        sel = topk_experts(probs, cfg.top_k) if override is None else np.asarray(override)
+        out = np.zeros(cfg.d_model, dtype=self.dtype)
+        for e in sel:
+            e = int(e)
+            y = swiglu_ffn(h, self.w(f"l{l}.e{e}.Wg"), self.w(f"l{l}.e{e}.Wu"),
+                           self.w(f"l{l}.e{e}.Wd"))
+            out = out + probs[e] * y
+        return out, sel
+
+    def step(self, token: int,
+             expert_override: Optional[Sequence[Optional[Sequence[int]]]] = None) -> np.ndarray:
+        """One forward pass of ``token`` at position ``pos``; returns logits."""
+        cfg, dt = self.cfg, self.dtype
+        p = self.pos
+        if p >= cfg.max_seq:
+            raise ValueError("KV cache full")
+        H, Hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+        cos, sin = rope_angles([p], hd, cfg.rope_theta)
+        x = self.w("E")[token].copy()
+        experts = []
+        for l in range(cfg.n_layers):
+            h = rmsnorm(x, self.w(f"l{l}.g_attn"), cfg.rms_eps)
+            q = (self.w(f"l{l}.Wq") @ h).reshape(H, hd)
+            k = (self.w(f"l{l}.Wk") @ h).reshape(Hkv, hd)
+            v = (self.w(f"l{l}.Wv") @ h).reshape(Hkv, hd)
+            q = apply_rope(q, cos, sin)
+            k = apply_rope(k, cos, sin)
+            self.K[l, p] = k
+            self.V[l, p] = v
+            o = attention_decode(q, self.K[l, :p + 1], self.V[l, :p + 1])
+            x = x + self.w(f"l{l}.Wo") @ o.reshape(-1)
+            h = rmsnorm(x, self.w(f"l{l}.g_ffn"), cfg.rms_eps)
+            ov = None if expert_override is None else expert_override[l]
+            y, sel = self._ffn(l, h, ov)
+            if sel is not None:
+                experts.append(np.asarray(sel, dtype=np.int32))
+            x = x + y
+        self.last_experts = experts
+        self.pos = p + 1
+        return self.w("W_lm") @ rmsnorm(x, self.w("g_final"), cfg.rms_eps)
+
+    # ---- request-level calls ----------------------------------------------
+    def prefill(self, prompt: Sequence[int]):
+        """Passes at positions 0..P-1; returns (first token, last logits)."""
+        self.reset()
+        logits = None
+        for t in prompt:
+            logits = self.step(int(t))
+        first = greedy_argmax(logits)
+        self.pending = first
+        return first, logits
+
+    def decode(self, n: int, force: Optional[Sequence[int]] = None,
+               keep_logits: bool = False, expert_overrides=None):
+        """n passes; returns (ids, logits rows or None, experts per pass)."""
+        if self.pending is None:
+            raise ValueError("no pending token: call prefill or set_kv first")
+        ids, rows, exps = [], [], []
+        for i in range(n):
+            ov = None if expert_overrides is None else expert_overrides[i]
+            logits = self.step(self.pending, ov)
+            nxt = greedy_argmax(logits)
+            ids.append(nxt)
+            exps.append(self.last_experts)
+            if keep_logits:
+                rows.append(logits)
+            self.pending = int(force[i]) if force is not None else nxt
+        return np.asarray(ids, dtype=np.int32), (np.stack(rows) if keep_logits else None), exps
+
+    # ---- non-incremental reference ----------------------------------------
+    def forward_full(self, tokens: Sequence[int]) -> np.ndarray:
+        """Logits at every position of ``tokens`` by a full causal recompute.
+
+        No KV cache: all positions are projected at once and attention applies
+        an explicit causal mask. Used to check the incremental path.
+        """
+        cfg, dt = self.cfg, self.dtype
+        T = len(tokens)
+        H, Hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+        group = H // Hkv
+        cos, sin = rope_angles(np.arange(T), hd, cfg.rope_theta)   # [T, hd/2]
+        X = self.w("E")[np.asarray(tokens)].astype(dt)              # [T, d]
+        mask = np.triu(np.ones((T, T), dtype=bool), k=1)            # True above diagonal
+        for l in range(cfg.n_layers):
+            Hn = rmsnorm(X, self.w(f"l{l}.g_attn"), cfg.rms_eps)
+            Q = (Hn @ self.w(f"l{l}.Wq").T).reshape(T, H, hd)
+            Kf = (Hn @ self.w(f"l{l}.Wk").T).reshape(T, Hkv, hd)
+            Vf = (Hn @ self.w(f"l{l}.Wv").T).reshape(T, Hkv, hd)
+            Q = apply_rope(Q, cos[:, None, :], sin[:, None, :])
+            Kf = apply_rope(Kf, cos[:, None, :], sin[:, None, :])
+            O = np.empty((T, H, hd), dtype=dt)
+            for j in range(H):
+                g = j // group
+                S = (Q[:, j, :] @ Kf[:, g, :].T) / dt.type(np.sqrt(hd))   # [T, T]
+                S = np.where(mask, -np.inf, S)
+                O[:, j, :] = softmax(S) @ Vf[:, g, :]
+            X = X + O.reshape(T, H * hd) @ self.w(f"l{l}.Wo").T
+            Hn = rmsnorm(X, self.w(f"l{l}.g_ffn"), cfg.rms_eps)
+            if cfg.n_experts:
+                Y = np.stack([self._ffn(l, Hn[t], None)[0] for t in range(T)])
+            else:
+                G = Hn @ self.w(f"l{l}.Wg").T
+                U = Hn @ self.w(f"l{l}.Wu").T
+                Y = (silu(G) * U) @ self.w(f"l{l}.Wd").T
+            X = X + Y
+        return rmsnorm(X, self.w("g_final"), cfg.rms_eps) @ self.w("W_lm").T
+
+
+def greedy_generate(cfg, tensors, prompt, n, dtype=np.float32):
+    """Free-running greedy decode: prefill, then n passes. Returns (first, ids)."""
+    dec = Decoder(cfg, tensors, dtype=dtype)
+    first, _ = dec.prefill(prompt)
+    ids, _, _ = dec.decode(n)
+    return first, ids
