@@ -1,0 +1,211 @@
+/*
+ * kie.h - C ABI of the batch-1 decode library for MI355X (gfx950).
+ *
+ * The library runs single-request (batch 1) greedy decode of a pre-norm
+ * transformer decoder as ONE persistent kernel launch per call, with sampling
+ * on the device and no host in the token loop. This is the method of the
+ * news.creeta.com monokernel article ("Inside the monokernel": one resident
+ * grid for the whole decode loop, on-device sampling, no relaunch or CPU
+ * wake-up between tokens) and of the agentlenshq.com article ("Core technical
+ * innovations": a single persistent program for the whole decode path). The
+ * metric is per-request decode speed at batch 1 (paper-digest.app digest,
+ * "Core Mechanics"); prefill is not part of it.
+ *
+ * Conventions for every call:
+ *  - Every int-returning call returns KIE_OK (0) or a negative KIE_ERR_* code.
+ *    No exception crosses the ABI. kie_last_error() gives a message.
+ *  - Host pointers are plain CPU memory owned by the caller. Device pointers
+ *    are device memory owned by the caller (for example a torch tensor); the
+ *    library never allocates or frees device memory.
+ *  - All device work is enqueued on the HIP stream given to kie_load (NULL =
+ *    the default stream). Calls that return data to host buffers synchronise
+ *    that stream before returning.
+ *  - A model is used by one host thread at a time.
+ *  - After KIE_ERR_TIMEOUT the device state is undefined: call kie_reset
+ *    before further use, or kie_free.
+ */
+#ifndef KIE_H
+#define KIE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KIE_OK = 0,
+    KIE_ERR_ARG = -1,        /* null pointer, negative count, token out of range */
+    KIE_ERR_CONFIG = -2,     /* dimensions the kernels do not support */
+    KIE_ERR_CAPACITY = -3,   /* position + tokens would exceed max_seq */
+    KIE_ERR_WORKSPACE = -4,  /* workspace smaller than kie_workspace_bytes() */
+    KIE_ERR_DEVICE = -5,     /* not gfx950, or the persistent grid cannot be co-resident */
+    KIE_ERR_HIP = -6,        /* a HIP runtime call failed */
+    KIE_ERR_TIMEOUT = -7,    /* a device-side wait hit its spin limit; the kernel exited */
+    KIE_ERR_STATE = -8       /* call order violated (e.g. decode before prefill) */
+};
+
+/*
+ * Decoder shape. The block is the plain pre-norm decoder the pages imply
+ * (RMSNorm, Q/K/V projections with rotary embedding, grouped-query attention
+ * over a KV cache, output projection, RMSNorm, SwiGLU FFN or top-k MoE;
+ * final RMSNorm and an untied LM head; no biases).
+ *  n_experts = 0 selects a dense SwiGLU FFN of width ffn_dim; otherwise each
+ *  layer has n_experts SwiGLU experts of width ffn_dim, a softmax router, and
+ *  the top_k experts by router probability are mixed with those
+ *  probabilities (ties to the lower expert index, no renormalisation).
+ * Supported (KIE_ERR_CONFIG otherwise): head_dim in {64, 128}; n_heads a
+ * multiple of n_kv_heads with at most 8 query heads per KV head; d_model,
+ * ffn_dim and n_heads*head_dim multiples of 256 and each either a multiple of
+ * 512 or a divisor of 512; max_seq <= 65536; vocab >= 2.
+ */
+typedef struct kie_config {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t ffn_dim;
+    int32_t vocab;
+    int32_t n_experts;   /* 0 = dense */
+    int32_t top_k;       /* experts per token (MoE only) */
+    float rms_eps;       /* RMSNorm: x / sqrt(mean(x^2) + eps) * g */
+    float rope_theta;    /* rotary base; pairs (i, i + head_dim/2) */
+    int32_t max_seq;     /* KV-cache capacity in positions */
+} kie_config;
+
+/*
+ * Optional per-call debug outputs and teacher forcing (all host memory).
+ *  force_ids: if non-NULL, [n] tokens; pass i is still sampled greedily
+ *             (its argmax is returned in out_ids[i]) but the token fed to pass
+ *             i+1 is force_ids[i].
+ *  logits:    if non-NULL, [n][vocab] fp32 logits of every pass.
+ *  experts:   if non-NULL (MoE only), [n][n_layers][top_k] selected expert
+ *             ids of every pass, in descending router probability.
+ * Debug outputs add device-to-host copies; they are for tests, not timing.
+ */
+typedef struct kie_debug {
+    const int32_t* force_ids;
+    float* logits;
+    int32_t* experts;
+} kie_debug;
+
+typedef struct kie_model kie_model;   /* opaque, owned by the library */
+
+/* Device bytes the caller must allocate for kie_load's workspace (weights in
+ * the streaming layout, KV cache, activations, barrier words). 0 if the
+ * configuration is invalid. Pure host computation. */
+size_t kie_workspace_bytes(const kie_config* cfg);
+
+/* Number of fp16 tensors kie_load expects for this configuration. */
+int32_t kie_tensor_count(const kie_config* cfg);
+
+/*
+ * Load a model. host_tensors[i] points to the i-th fp16 tensor in the
+ * canonical order, each row-major [out][in]:
+ *   E[vocab][d];
+ *   per layer: g_attn[d], Wq[H*hd][d], Wk[Hkv*hd][d], Wv[Hkv*hd][d],
+ *              Wo[d][H*hd], g_ffn[d], then either Wg[F][d], Wu[F][d], Wd[d][F]
+ *              or Wr[n_experts][d] followed by (Wg, Wu, Wd) per expert;
+ *   g_final[d]; W_lm[vocab][d].
+ * The host repacks them once (offline preparation in the sense of the
+ * monokernel article's fused, precomputed steps: RMSNorm gains folded into
+ * the following projection, Q/K/V fused into one streamable matrix, a rotary
+ * cos/sin table built in double precision) and copies them into
+ * dev_workspace, which must stay allocated until kie_free.
+ * hip_stream is a hipStream_t (NULL = default stream). On success *out is a
+ * new model at position 0 with no pending token.
+ */
+int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_tensors,
+             void* dev_workspace, size_t ws_bytes, void* hip_stream, kie_model** out);
+
+/*
+ * Prefill: run one forward pass per prompt token at positions 0..n-1 (the
+ * cache is reset first) and return the greedy first generated token, which
+ * becomes the pending token. One kernel launch. Not part of the decode metric.
+ * dbg may be NULL; dbg->logits, if set, receives [n][vocab].
+ */
+int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_token,
+                const kie_debug* dbg);
+
+/*
+ * Store already-rotated keys and values for positions 0..n_pos-1 directly in
+ * the cache (host fp16 arrays [n_layers][n_pos][n_kv_heads][head_dim]), set
+ * the position to n_pos and the pending token to pending_token. Used to start
+ * decoding at long context without a prefill.
+ */
+int kie_set_kv(kie_model* m, const void* k_fp16, const void* v_fp16, int32_t n_pos,
+               int32_t pending_token);
+
+/*
+ * Decode: exactly n_tokens forward passes in ONE kernel launch, starting at
+ * the current position with the pending token. out_ids[i] (host, [n_tokens])
+ * is the greedy token of pass i; the last one becomes the new pending token
+ * (or the last forced one when teacher forcing). The position advances by
+ * n_tokens. Returns KIE_ERR_CAPACITY if position + n_tokens > max_seq.
+ */
+int kie_decode(kie_model* m, int32_t n_tokens, int32_t* out_ids, const kie_debug* dbg);
+
+/* Move back to an earlier position pos (0 <= pos <= current) with the given
+ * pending token; cache entries at positions >= pos are overwritten by later
+ * passes. Lets a benchmark repeat the same decode request. */
+int kie_rewind(kie_model* m, int32_t pos, int32_t pending_token);
+
+/* Clear the KV cache and device state; position 0, no pending token. */
+int kie_reset(kie_model* m);
+
+/* Current position and pending token (-1 if none). */
+int kie_state(const kie_model* m, int32_t* pos, int32_t* pending_token);
+
+/* Device time in milliseconds of the last kernel launch made by
+ * kie_decode/kie_prefill, measured with HIP events on the model's stream
+ * around that one launch. */
+float kie_last_kernel_ms(const kie_model* m);
+
+/* Workgroups of the persistent grid (one per compute unit). */
+int32_t kie_grid_size(const kie_model* m);
+
+void kie_free(kie_model* m);
+const char* kie_last_error(const kie_model* m);   /* m may be NULL: last global error */
+const char* kie_status_str(int status);
+
+/*
+ * GEMV bandwidth probe: y[r][i] = sum_k A_r[i][k] x[k] for r < copies, where
+ * A_r = A + r*M*K (fp16, row-major, device), x fp16 [K] (device), y fp32
+ * [copies][M] (device), products accumulated in fp32 with v_dot2.
+ * variant 0: one launch of the persistent 256-workgroup streaming GEMV the
+ *            decode kernel uses (LDS-ring weight streamer + compute waves),
+ *            each workgroup streaming its rows of every copy in turn;
+ *            requires ceil(M/256) * K/512 <= 1024.
+ * variant 1: a plain many-wave GEMV (4 rows per wave, all loads in flight).
+ * K must be a multiple of 512, at most 65536. *ms_out (host, may be NULL)
+ * receives the device time of the launch. Used to measure achieved HBM
+ * bandwidth per shape (the pages' statement that batch-1 decode is a
+ * bandwidth-bound matrix-vector product: paper-digest.app digest,
+ * "Core Mechanics").
+ */
+int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K, int32_t copies,
+                   int32_t variant, void* hip_stream, float* ms_out);
+
+/*
+ * Grid-barrier probe: one persistent launch that runs `rounds` grid-wide
+ * barriers across all workgroups, each barrier also all-gathering an 8-byte
+ * value per workgroup. scratch is device memory of at least
+ * kie_barrier_probe_bytes() bytes. *us_per_barrier receives the mean time of
+ * one barrier; *errors the number of rounds whose gathered values were wrong
+ * (must be 0).
+ */
+size_t kie_barrier_probe_bytes(void);
+int kie_barrier_probe(void* scratch, int32_t rounds, void* hip_stream, float* us_per_barrier,
+                      int32_t* errors);
+
+/* Launch-overhead probe: `launches` back-to-back launches of an empty kernel;
+ * *us_per_launch receives host wall time per launch including completion. */
+int kie_launch_probe(int32_t launches, void* hip_stream, float* us_per_launch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIE_H */

@@ -1,0 +1,467 @@
+// kie_api.hip - the C ABI of include/kie.h: argument checks, model state,
+// uploads into the caller's workspace, and one cooperative launch per
+// kie_decode / kie_prefill call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <chrono>
+#include <string>
+#include <vector>
+
+#include "../../include/kie.h"
+#include "kie_host.h"
+#include "kie_kernels.h"
+
+using namespace kie;
+
+struct kie_model {
+    kie_config cfg;
+    Layout lay;
+    uint8_t* ws;
+    hipStream_t stream;
+    int pos;
+    int pending;   // -1: none
+    hipEvent_t ev0, ev1;
+    float last_ms;
+    std::string err;
+};
+
+static thread_local std::string g_err;
+
+static int fail(kie_model* m, int code, const std::string& msg) {
+    if (m) m->err = msg;
+    g_err = msg;
+    return code;
+}
+
+static int hip_fail(kie_model* m, hipError_t e, const char* what) {
+    std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+    int code = (e == hipErrorCooperativeLaunchTooLarge) ? KIE_ERR_DEVICE : KIE_ERR_HIP;
+    return fail(m, code, msg);
+}
+
+#define HIP_TRY(m, call)                                  \
+    do {                                                  \
+        hipError_t e_ = (call);                           \
+        if (e_ != hipSuccess) return hip_fail(m, e_, #call); \
+    } while (0)
+
+extern "C" {
+
+const char* kie_status_str(int s) {
+    switch (s) {
+    case KIE_OK: return "ok";
+    case KIE_ERR_ARG: return "invalid argument";
+    case KIE_ERR_CONFIG: return "unsupported configuration";
+    case KIE_ERR_CAPACITY: return "KV cache capacity exceeded";
+    case KIE_ERR_WORKSPACE: return "workspace too small";
+    case KIE_ERR_DEVICE: return "unsupported device or grid not co-resident";
+    case KIE_ERR_HIP: return "HIP runtime error";
+    case KIE_ERR_TIMEOUT: return "device wait timed out";
+    case KIE_ERR_STATE: return "invalid call order";
+    default: return "unknown status";
+    }
+}
+
+const char* kie_last_error(const kie_model* m) { return m ? m->err.c_str() : g_err.c_str(); }
+
+size_t kie_workspace_bytes(const kie_config* cfg) {
+    if (!cfg) return 0;
+    std::string err;
+    if (validate_config(*cfg, &err) != KIE_OK) {
+        g_err = err;
+        return 0;
+    }
+    Layout* lay = new Layout;
+    make_layout(*cfg, lay);
+    size_t t = lay->total;
+    delete lay;
+    return t;
+}
+
+int32_t kie_tensor_count(const kie_config* cfg) {
+    if (!cfg) return 0;
+    return tensor_count(*cfg);
+}
+
+static int check_device(kie_model* m) {
+    int dev = 0;
+    HIP_TRY(m, hipGetDevice(&dev));
+    hipDeviceProp_t p;
+    HIP_TRY(m, hipGetDeviceProperties(&p, dev));
+    if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+        return fail(m, KIE_ERR_DEVICE, std::string("device is ") + p.gcnArchName + ", kernels are built for gfx950");
+    if (p.multiProcessorCount < kGrid)
+        return fail(m, KIE_ERR_DEVICE, "device has fewer compute units than the 256-workgroup persistent grid");
+    if (!p.cooperativeLaunch) return fail(m, KIE_ERR_DEVICE, "cooperative launch not supported");
+    static bool attr_done = false;
+    if (!attr_done) {
+        HIP_TRY(m, decode_kernel_setup());
+        attr_done = true;
+    }
+    return KIE_OK;
+}
+
+static int upload(kie_model* m, size_t off, const void* src, size_t bytes) {
+    HIP_TRY(m, hipMemcpyAsync(m->ws + off, src, bytes, hipMemcpyHostToDevice, m->stream));
+    HIP_TRY(m, hipStreamSynchronize(m->stream));
+    return KIE_OK;
+}
+
+static int clear_state(kie_model* m, bool kv) {
+    const Layout& L = m->lay;
+    if (kv) {
+        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_k, 0, L.kv_bytes, m->stream));
+        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_v, 0, L.kv_bytes, m->stream));
+    }
+    HIP_TRY(m, hipMemsetAsync(m->ws + L.off_x, 0, L.off_dbg_logits - L.off_x, m->stream));
+    HIP_TRY(m, hipStreamSynchronize(m->stream));
+    return KIE_OK;
+}
+
+int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_tensors, void* dev_workspace,
+             size_t ws_bytes, void* hip_stream, kie_model** out) {
+    if (!cfg || !host_tensors || !dev_workspace || !out) return fail(nullptr, KIE_ERR_ARG, "null argument");
+    *out = nullptr;
+    std::string err;
+    int rc = validate_config(*cfg, &err);
+    if (rc != KIE_OK) return fail(nullptr, rc, err);
+    if (n_tensors != tensor_count(*cfg))
+        return fail(nullptr, KIE_ERR_ARG, "tensor count does not match the configuration");
+    for (int i = 0; i < n_tensors; ++i)
+        if (!host_tensors[i]) return fail(nullptr, KIE_ERR_ARG, "null tensor pointer");
+    kie_model* m = new kie_model;
+    m->cfg = *cfg;
+    make_layout(*cfg, &m->lay);
+    m->ws = (uint8_t*)dev_workspace;
+    m->stream = (hipStream_t)hip_stream;
+    m->pos = 0;
+    m->pending = -1;
+    m->last_ms = 0.f;
+    m->ev0 = m->ev1 = nullptr;
+    if (ws_bytes < m->lay.total) {
+        rc = fail(nullptr, KIE_ERR_WORKSPACE, "workspace smaller than kie_workspace_bytes()");
+        delete m;
+        return rc;
+    }
+    if ((rc = check_device(m)) != KIE_OK) {
+        g_err = m->err;
+        delete m;
+        return rc;
+    }
+    const Layout& L = m->lay;
+    const Dims& D = L.D;
+    const uint16_t* const* T = (const uint16_t* const*)host_tensors;
+    size_t stage_bytes = L.layer_bytes;
+    if (L.lm_bytes > stage_bytes) stage_bytes = L.lm_bytes;
+    if (L.expert_bytes > stage_bytes) stage_bytes = L.expert_bytes;
+    size_t rope_bytes = (size_t)D.max_seq * (D.hd / 2) * 8;
+    if (rope_bytes > stage_bytes) stage_bytes = rope_bytes;
+    std::vector<uint8_t> stage(stage_bytes);
+    auto bail = [&](int code) {
+        g_err = m->err;
+        delete m;
+        return code;
+    };
+    for (int l = 0; l < D.L; ++l) {
+        repack_layer(*cfg, L, T, l, (uint16_t*)stage.data());
+        if ((rc = upload(m, L.off_layers + (size_t)l * L.layer_bytes, stage.data(), L.layer_bytes)) != KIE_OK)
+            return bail(rc);
+        if (D.E) {
+            for (int e = 0; e < D.E; ++e) {
+                repack_expert(*cfg, L, T, l, e, (uint16_t*)stage.data());
+                size_t off = L.off_experts + ((size_t)l * D.E + e) * L.expert_bytes;
+                if ((rc = upload(m, off, stage.data(), L.expert_bytes)) != KIE_OK) return bail(rc);
+            }
+        }
+    }
+    repack_lm(*cfg, L, T, (uint16_t*)stage.data());
+    if ((rc = upload(m, L.off_lm, stage.data(), L.lm_bytes)) != KIE_OK) return bail(rc);
+    if ((rc = upload(m, L.off_emb, T[tidx_emb()], (size_t)D.V * D.d * 2)) != KIE_OK) return bail(rc);
+    rope_table(*cfg, (float*)stage.data());
+    if ((rc = upload(m, L.off_rope, stage.data(), rope_bytes)) != KIE_OK) return bail(rc);
+    std::vector<int32_t> plan(2 * (kGrid + 1));
+    for (int w = 0; w <= kGrid; ++w) {
+        plan[w] = L.piece_off[w];
+        plan[kGrid + 1 + w] = L.lm_off[w];
+    }
+    if ((rc = upload(m, L.off_plan, plan.data(), plan.size() * 4)) != KIE_OK) return bail(rc);
+    if ((rc = clear_state(m, true)) != KIE_OK) return bail(rc);
+    hipError_t e = hipEventCreate(&m->ev0);
+    if (e == hipSuccess) e = hipEventCreate(&m->ev1);
+    if (e != hipSuccess) {
+        hip_fail(m, e, "hipEventCreate");
+        return bail(KIE_ERR_HIP);
+    }
+    *out = m;
+    return KIE_OK;
+}
+
+// n passes from the current position. force (host, may be null): next input
+// of pass i where force[i] >= 0. One launch unless debug rows are requested,
+// then launches of at most kDebugRows passes.
+static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_ids, float* dbg_logits,
+                      int32_t* dbg_experts, bool skip_lm) {
+    const Layout& L = m->lay;
+    const Dims& D = L.D;
+    const bool debug = dbg_logits || dbg_experts;
+    const int chunk = debug ? kDebugRows : n;
+    int tok = m->pending;
+    for (int s0 = 0; s0 < n; s0 += chunk) {
+        int nc = (n - s0 < chunk) ? n - s0 : chunk;
+        // reset the barrier words, status, attention counters for this launch
+        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_attn_cnt, 0, (size_t)D.Hkv * 64, m->stream));
+        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_bar, 0, (size_t)kGrid * 4, m->stream));
+        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_status, 0, 256, m->stream));
+        if (force)
+            HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_force, force + s0, (size_t)nc * 4, hipMemcpyHostToDevice,
+                                      m->stream));
+        DecodeArgs a;
+        memset(&a, 0, sizeof(a));
+        a.D = D;
+        a.eps = m->cfg.rms_eps;
+        a.items_per_head = L.attn_items_per_head;
+        a.spin_lds = 1u << 24;
+        a.spin_grid = 1u << 21;
+        a.layers = m->ws + L.off_layers;
+        a.layer_bytes = L.layer_bytes;
+        a.lm = m->ws + L.off_lm;
+        a.emb = (const uint16_t*)(m->ws + L.off_emb);
+        a.experts = m->ws + L.off_experts;
+        a.expert_bytes = L.expert_bytes;
+        a.rope = (const float*)(m->ws + L.off_rope);
+        a.kc = (uint16_t*)(m->ws + L.off_k);
+        a.vc = (uint16_t*)(m->ws + L.off_v);
+        a.x = (float*)(m->ws + L.off_x);
+        a.q = (float*)(m->ws + L.off_q);
+        a.o16 = (uint16_t*)(m->ws + L.off_o);
+        a.h16 = (uint16_t*)(m->ws + L.off_h);
+        a.router = (float*)(m->ws + L.off_router);
+        a.attn_part = (float*)(m->ws + L.off_attn_part);
+        a.attn_cnt = (uint32_t*)(m->ws + L.off_attn_cnt);
+        a.argmax = (float*)(m->ws + L.off_argmax);
+        a.bar = (uint32_t*)(m->ws + L.off_bar);
+        a.status = (uint32_t*)(m->ws + L.off_status);
+        a.out_ids = (int32_t*)(m->ws + L.off_out);
+        a.force_ids = (const int32_t*)(m->ws + L.off_force);
+        a.dbg_logits = (float*)(m->ws + L.off_dbg_logits);
+        a.dbg_experts = (int32_t*)(m->ws + L.off_dbg_experts);
+        a.plan = (const int32_t*)(m->ws + L.off_plan);
+        a.pos0 = m->pos + s0;
+        a.pending = tok;
+        a.n_steps = nc;
+        a.flags = (force ? F_FORCE : 0) | (dbg_logits ? F_DBG_LOGITS : 0) | (dbg_experts ? F_DBG_EXPERTS : 0) |
+                  ((skip_lm && !debug) ? F_SKIP_LM : 0);
+        a.epoch0 = 0;
+        static_assert(sizeof(DecodeArgs) <= 4096, "argument block");
+        HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
+        HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
+        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, kGrid, m->stream));
+        HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
+        HIP_TRY(m, hipEventSynchronize(m->ev1));
+        HIP_TRY(m, hipEventElapsedTime(&m->last_ms, m->ev0, m->ev1));
+        uint32_t status = 0;
+        HIP_TRY(m, hipMemcpy(&status, m->ws + L.off_status, 4, hipMemcpyDeviceToHost));
+        if (status != 0) {
+            m->pending = -1;
+            return fail(m, KIE_ERR_TIMEOUT, "a grid barrier or ring wait hit its spin limit");
+        }
+        HIP_TRY(m, hipMemcpy(out_ids + s0, m->ws + L.off_out, (size_t)nc * 4, hipMemcpyDeviceToHost));
+        if (dbg_logits)
+            HIP_TRY(m, hipMemcpy(dbg_logits + (size_t)s0 * D.V, m->ws + L.off_dbg_logits, (size_t)nc * D.V * 4,
+                                 hipMemcpyDeviceToHost));
+        if (dbg_experts)
+            HIP_TRY(m, hipMemcpy(dbg_experts + (size_t)s0 * D.L * D.topk, m->ws + L.off_dbg_experts,
+                                 (size_t)nc * D.L * D.topk * 4, hipMemcpyDeviceToHost));
+        int last = nc - 1;
+        tok = (force && force[s0 + last] >= 0) ? force[s0 + last] : out_ids[s0 + last];
+    }
+    m->pos += n;
+    m->pending = tok;
+    return KIE_OK;
+}
+
+int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_token, const kie_debug* dbg) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    if (!tokens || !first_token || n < 1) return fail(m, KIE_ERR_ARG, "need at least one prompt token");
+    if (n > m->cfg.max_seq) return fail(m, KIE_ERR_CAPACITY, "prompt longer than max_seq");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "prompt token out of range");
+    if (dbg && dbg->experts && m->cfg.n_experts == 0) return fail(m, KIE_ERR_ARG, "experts requested for a dense model");
+    std::vector<int32_t> force(n);
+    for (int i = 0; i + 1 < n; ++i) force[i] = tokens[i + 1];
+    force[n - 1] = -1;
+    std::vector<int32_t> ids(n);
+    m->pos = 0;
+    m->pending = tokens[0];
+    int rc = run_passes(m, n, force.data(), ids.data(), dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr,
+                        true);
+    if (rc != KIE_OK) return rc;
+    *first_token = ids[n - 1];
+    return KIE_OK;
+}
+
+int kie_decode(kie_model* m, int32_t n, int32_t* out_ids, const kie_debug* dbg) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    if (!out_ids || n < 1) return fail(m, KIE_ERR_ARG, "need n_tokens >= 1 and an output buffer");
+    if (m->pending < 0) return fail(m, KIE_ERR_STATE, "no pending token: call kie_prefill or kie_set_kv first");
+    if ((long)m->pos + n > m->cfg.max_seq) return fail(m, KIE_ERR_CAPACITY, "position + n_tokens exceeds max_seq");
+    if (dbg && dbg->experts && m->cfg.n_experts == 0) return fail(m, KIE_ERR_ARG, "experts requested for a dense model");
+    const int32_t* force = dbg ? dbg->force_ids : nullptr;
+    if (force)
+        for (int i = 0; i < n; ++i)
+            if (force[i] >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "forced token out of range");
+    return run_passes(m, n, force, out_ids, dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr, false);
+}
+
+int kie_set_kv(kie_model* m, const void* k, const void* v, int32_t n_pos, int32_t pending) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    if (!k || !v || n_pos < 0) return fail(m, KIE_ERR_ARG, "null cache or negative length");
+    if (n_pos > m->cfg.max_seq) return fail(m, KIE_ERR_CAPACITY, "n_pos exceeds max_seq");
+    if (pending < 0 || pending >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "pending token out of range");
+    const Layout& L = m->lay;
+    const Dims& D = L.D;
+    int rc = clear_state(m, true);
+    if (rc != KIE_OK) return rc;
+    // host [L][n_pos][Hkv][hd] -> device [L][Hkv][max_seq][hd]
+    size_t blk = (size_t)n_pos * D.hd;   // halves per (layer, head)
+    std::vector<uint16_t> stage((size_t)D.Hkv * blk);
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t* src = (const uint16_t*)(which ? v : k);
+        size_t base = which ? L.off_v : L.off_k;
+        for (int l = 0; l < D.L; ++l) {
+            for (int p = 0; p < n_pos; ++p)
+                for (int g = 0; g < D.Hkv; ++g)
+                    memcpy(&stage[(size_t)g * blk + (size_t)p * D.hd],
+                           src + (((size_t)l * n_pos + p) * D.Hkv + g) * D.hd, (size_t)D.hd * 2);
+            for (int g = 0; g < D.Hkv; ++g) {
+                size_t off = base + (((size_t)l * D.Hkv + g) * D.max_seq) * D.hd * 2;
+                if ((rc = upload(m, off, &stage[(size_t)g * blk], blk * 2)) != KIE_OK) return rc;
+            }
+        }
+    }
+    m->pos = n_pos;
+    m->pending = pending;
+    return KIE_OK;
+}
+
+int kie_rewind(kie_model* m, int32_t pos, int32_t pending) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    if (pos < 0 || pos > m->pos) return fail(m, KIE_ERR_ARG, "can only rewind to an earlier position");
+    if (pending < 0 || pending >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "pending token out of range");
+    m->pos = pos;
+    m->pending = pending;
+    return KIE_OK;
+}
+
+int kie_reset(kie_model* m) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    int rc = clear_state(m, true);
+    if (rc != KIE_OK) return rc;
+    m->pos = 0;
+    m->pending = -1;
+    return KIE_OK;
+}
+
+int kie_state(const kie_model* m, int32_t* pos, int32_t* pending) {
+    if (!m || !pos || !pending) return fail(nullptr, KIE_ERR_ARG, "null argument");
+    *pos = m->pos;
+    *pending = m->pending;
+    return KIE_OK;
+}
+
+float kie_last_kernel_ms(const kie_model* m) { return m ? m->last_ms : 0.f; }
+int32_t kie_grid_size(const kie_model* m) { return m ? kGrid : 0; }
+
+void kie_free(kie_model* m) {
+    if (!m) return;
+    if (m->ev0) (void)hipEventDestroy(m->ev0);
+    if (m->ev1) (void)hipEventDestroy(m->ev1);
+    delete m;
+}
+
+// ---------------------------------------------------------------- probes --
+int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K, int32_t copies,
+                   int32_t variant, void* hip_stream, float* ms_out) {
+    if (!A || !x || !y) return fail(nullptr, KIE_ERR_ARG, "null pointer");
+    if (M < 1 || copies < 1 || K < 512 || K % 512 || K > 65536)
+        return fail(nullptr, KIE_ERR_ARG, "need M >= 1, copies >= 1, K a multiple of 512 up to 65536");
+    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (ring) or 1 (direct)");
+    if (variant == 0 && (long)ceil_div(M, kGrid) * (K / 512) > kPartFloats)
+        return fail(nullptr, KIE_ERR_ARG, "rows per workgroup x K/512 must be at most 1024");
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (variant == 0) {
+        static bool attr_done = false;
+        if (!attr_done) {
+            hipError_t e = decode_kernel_setup();
+            if (e != hipSuccess) return hip_fail(nullptr, e, "decode_kernel_setup");
+            attr_done = true;
+        }
+    }
+    hipEvent_t e0, e1;
+    HIP_TRY(nullptr, hipEventCreate(&e0));
+    HIP_TRY(nullptr, hipEventCreate(&e1));
+    GemvArgs a;
+    a.A = (const uint8_t*)A;
+    a.x = (const uint16_t*)x;
+    a.y = y;
+    a.M = M;
+    a.K = K;
+    a.copies = copies;
+    a.spin_lds = 1u << 24;
+    HIP_TRY(nullptr, hipEventRecord(e0, s));
+    hipError_t le = variant == 0 ? launch_gemv_ring(a, kGrid, s) : launch_gemv_direct(a, s);
+    if (le != hipSuccess) return hip_fail(nullptr, le, "gemv probe launch");
+    HIP_TRY(nullptr, hipEventRecord(e1, s));
+    HIP_TRY(nullptr, hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIP_TRY(nullptr, hipEventElapsedTime(&ms, e0, e1));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (ms_out) *ms_out = ms;
+    return KIE_OK;
+}
+
+size_t kie_barrier_probe_bytes(void) { return 16384; }
+
+int kie_barrier_probe(void* scratch, int32_t rounds, void* hip_stream, float* us_per_barrier, int32_t* errors) {
+    if (!scratch || !us_per_barrier || !errors || rounds < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    hipStream_t s = (hipStream_t)hip_stream;
+    uint8_t* b = (uint8_t*)scratch;
+    uint32_t* bar = (uint32_t*)b;                 // 1 KiB
+    uint32_t* status = (uint32_t*)(b + 4096);
+    int32_t* err = (int32_t*)(b + 4096 + 256);
+    float* vals = (float*)(b + 8192);             // 2 x 256 x 2 floats = 4 KiB
+    HIP_TRY(nullptr, hipMemsetAsync(scratch, 0, kie_barrier_probe_bytes(), s));
+    hipEvent_t e0, e1;
+    HIP_TRY(nullptr, hipEventCreate(&e0));
+    HIP_TRY(nullptr, hipEventCreate(&e1));
+    HIP_TRY(nullptr, hipEventRecord(e0, s));
+    hipError_t le = launch_barrier_probe(bar, status, vals, err, rounds, kGrid, s);
+    if (le != hipSuccess) return hip_fail(nullptr, le, "barrier probe launch");
+    HIP_TRY(nullptr, hipEventRecord(e1, s));
+    HIP_TRY(nullptr, hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIP_TRY(nullptr, hipEventElapsedTime(&ms, e0, e1));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    HIP_TRY(nullptr, hipMemcpy(errors, err, 4, hipMemcpyDeviceToHost));
+    *us_per_barrier = ms * 1000.f / (float)rounds;
+    return KIE_OK;
+}
+
+int kie_launch_probe(int32_t launches, void* hip_stream, float* us_per_launch) {
+    if (launches < 1 || !us_per_launch) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    hipStream_t s = (hipStream_t)hip_stream;
+    HIP_TRY(nullptr, launch_empty(s));
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    auto t0 = std::chrono::steady_clock::now();
+    for (int i = 0; i < launches; ++i) HIP_TRY(nullptr, launch_empty(s));
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    auto t1 = std::chrono::steady_clock::now();
+    *us_per_launch = (float)(std::chrono::duration<double, std::micro>(t1 - t0).count() / launches);
+    return KIE_OK;
+}
+
+}  // extern "C"

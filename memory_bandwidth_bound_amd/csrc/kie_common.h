@@ -1,0 +1,149 @@
+// kie_common.h - layout rules shared by the host repacker and the device kernels.
+//
+// Everything here is plain integer arithmetic on shapes, usable from host C++
+// (g++) and from HIP device code. It fixes:
+//  * the phase matrices of one decoder layer and their row order,
+//  * how each phase's rows are split over the workgroups of the persistent
+//    grid (the same split for the output projection and the FFN down
+//    projection, so each residual element has exactly one owner),
+//  * the streaming unit: 1 KiB = one wave-wide 16-byte-per-lane load,
+//  * the per-workgroup weight stream: for every layer, one contiguous piece
+//    holding that workgroup's rows of every phase in phase order, then its
+//    rows of the LM head.
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+
+#if defined(__HIPCC__)
+#define KIE_HD __host__ __device__ inline
+#else
+#define KIE_HD inline
+#endif
+
+namespace kie {
+
+constexpr int kGrid = 256;                 // persistent workgroups: one per MI355X compute unit
+constexpr int kUnitBytes = 1024;           // one global_load_lds_dwordx4 of a wave
+constexpr int kUnitHalves = 512;           // fp16 elements per unit
+constexpr int kMaxGroup = 8;               // query heads per KV head supported
+constexpr int kAttnChunkMax = 1024;        // positions per attention work item
+constexpr int kAttnChunkMin = 32;
+constexpr int kMaxSeq = 65536;
+
+// Phase kinds of the per-layer pipeline.
+enum Phase : int {
+    PH_QKV = 0,    // fused [Wq;Wk;Wv], rotary pairs adjacent, gains folded
+    PH_WO = 1,     // output projection, residual add
+    PH_GU = 2,     // fused gate/up, rows interleaved (g_j, u_j), gains folded
+    PH_DOWN = 3,   // down projection, residual add
+    PH_ROUTER = 4, // MoE router rows, gains folded
+    PH_LM = 5,     // LM head, gains folded
+    PH_EGU = 6,    // selected experts' gate/up rows (virtual matrix top_k*2F x d)
+    PH_EDOWN = 7,  // selected experts' down rows (virtual matrix d x top_k*F)
+    PH_COUNT = 8
+};
+
+struct Dims {
+    int L, d, H, Hkv, hd, F, V, E, topk, max_seq;
+};
+
+struct RowSplit {
+    int row0;
+    int nrows;
+};
+
+// Even split of M rows in groups of `gran` over nwg workgroups; the first
+// (M/gran) % nwg workgroups get one extra group.
+KIE_HD RowSplit split_rows(int M, int gran, int nwg, int w) {
+    int groups = M / gran;
+    int base = groups / nwg, rem = groups % nwg;
+    int g0 = w * base + (w < rem ? w : rem);
+    int ng = base + (w < rem ? 1 : 0);
+    RowSplit r;
+    r.row0 = g0 * gran;
+    r.nrows = ng * gran;
+    return r;
+}
+
+KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Units of a slab of nrows rows of K fp16 each, padded to whole units.
+KIE_HD int slab_units(int nrows, int K) { return ceil_div(nrows * K, kUnitHalves); }
+
+// Shape of a phase matrix: rows M, row length K (fp16), split granularity.
+struct PhaseShape {
+    int M, K, gran;
+};
+
+KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
+    PhaseShape s;
+    switch (ph) {
+    case PH_QKV: s.M = (D.H + 2 * D.Hkv) * D.hd; s.K = D.d; s.gran = 2; break;
+    case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = 1; break;
+    case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 2; break;
+    case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = 1; break;
+    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = 1; break;
+    case PH_LM: s.M = D.V; s.K = D.d; s.gran = 1; break;
+    case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 2; break;
+    case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 1; break;   // K per selected expert
+    default: s.M = 0; s.K = 0; s.gran = 1; break;
+    }
+    return s;
+}
+
+// Units of workgroup w in phase ph (for PH_EDOWN: all top_k segments).
+KIE_HD int phase_units(const Dims& D, int ph, int nwg, int w) {
+    PhaseShape s = phase_shape(D, ph);
+    RowSplit r = split_rows(s.M, s.gran, nwg, w);
+    if (ph == PH_EDOWN) return D.topk * slab_units(r.nrows, s.K);
+    if (ph == PH_EGU) {
+        // the workgroup's virtual rows may span several experts; each expert
+        // segment is padded on its own
+        int per = 2 * D.F;
+        int u = 0;
+        int a = r.row0, end = r.row0 + r.nrows;
+        while (a < end) {
+            int seg_end = (a / per + 1) * per;
+            if (seg_end > end) seg_end = end;
+            u += slab_units(seg_end - a, s.K);
+            a = seg_end;
+        }
+        return u;
+    }
+    return slab_units(r.nrows, s.K);
+}
+
+// Phases whose weights sit in the per-layer streaming block, in stream order.
+KIE_HD int layer_block_phase_count(const Dims& D) { return D.E ? 3 : 4; }
+KIE_HD int layer_block_phase(const Dims& D, int i) {
+    if (D.E) {
+        const int p[3] = {PH_QKV, PH_WO, PH_ROUTER};
+        return p[i];
+    }
+    const int p[4] = {PH_QKV, PH_WO, PH_GU, PH_DOWN};
+    return p[i];
+}
+
+// Units of workgroup w's piece of one layer block.
+KIE_HD int piece_units(const Dims& D, int nwg, int w) {
+    int u = 0;
+    for (int i = 0; i < layer_block_phase_count(D); ++i)
+        u += phase_units(D, layer_block_phase(D, i), nwg, w);
+    return u;
+}
+
+// Virtual QKV row -> original (matrix 0=q 1=k 2=v, row in that matrix).
+// q and k heads store each rotary pair (i, i + hd/2) as adjacent rows
+// (2i, 2i+1) of the head; v keeps its natural order.
+KIE_HD void qkv_row_source(const Dims& D, int r, int* mat, int* row) {
+    int qd = D.H * D.hd, kd = D.Hkv * D.hd;
+    int m = 0;
+    if (r >= qd + kd) { *mat = 2; *row = r - qd - kd; return; }
+    if (r >= qd) { m = 1; r -= qd; }
+    int head = r / D.hd, w = r % D.hd;
+    int pair = w >> 1, which = w & 1;
+    *mat = m;
+    *row = head * D.hd + pair + which * (D.hd / 2);
+}
+
+}  // namespace kie

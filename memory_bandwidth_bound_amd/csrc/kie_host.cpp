@@ -1,0 +1,307 @@
+// kie_host.cpp - host-only preparation (no HIP): configuration checks, the
+// workspace layout, the offline weight repack and the rotary table.
+//
+// The repack is the offline preparation the news.creeta.com monokernel
+// article lists under "Inside the monokernel": RMSNorm is folded into the
+// adjacent projection (gains multiply the columns of the next matrix), the
+// Q/K/V projections are repacked into one streamable matrix, and the rotary
+// embedding is precomputed as a table. On top of that every phase's rows are
+// cut per workgroup and laid out so that one workgroup's weights for a whole
+// layer are one contiguous run of memory in the order it consumes them.
+#include "kie_host.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace kie {
+
+Dims dims_of(const kie_config& c) {
+    Dims D;
+    D.L = c.n_layers;
+    D.d = c.d_model;
+    D.H = c.n_heads;
+    D.Hkv = c.n_kv_heads;
+    D.hd = c.head_dim;
+    D.F = c.ffn_dim;
+    D.V = c.vocab;
+    D.E = c.n_experts;
+    D.topk = c.n_experts ? c.top_k : 0;
+    D.max_seq = c.max_seq;
+    return D;
+}
+
+static int per_layer_tensors(const kie_config& c) {
+    return 6 + (c.n_experts ? 1 + 3 * c.n_experts : 3);
+}
+int tidx_emb() { return 0; }
+int tidx_layer(const kie_config& c, int layer, int which) {
+    return 1 + layer * per_layer_tensors(c) + which;
+}
+int tidx_expert(const kie_config& c, int layer, int expert, int which) {
+    return 1 + layer * per_layer_tensors(c) + 7 + 3 * expert + which;
+}
+int tidx_gfinal(const kie_config& c) { return 1 + c.n_layers * per_layer_tensors(c); }
+int tidx_lm(const kie_config& c) { return 2 + c.n_layers * per_layer_tensors(c); }
+int tensor_count(const kie_config& c) { return 3 + c.n_layers * per_layer_tensors(c); }
+
+static bool width_ok(int x) { return x == 256 || (x > 0 && x % 512 == 0); }
+
+int validate_config(const kie_config& c, std::string* err) {
+    auto fail = [&](const char* m) {
+        if (err) *err = m;
+        return (int)KIE_ERR_CONFIG;
+    };
+    if (c.n_layers < 1 || c.n_layers > 4096) return fail("n_layers must be in [1, 4096]");
+    if (c.head_dim != 64 && c.head_dim != 128) return fail("head_dim must be 64 or 128");
+    if (c.n_heads < 1 || c.n_kv_heads < 1 || c.n_heads % c.n_kv_heads)
+        return fail("n_heads must be a positive multiple of n_kv_heads");
+    if (c.n_heads / c.n_kv_heads > kMaxGroup) return fail("at most 8 query heads per KV head");
+    if (c.n_kv_heads > kGrid) return fail("too many KV heads");
+    if (!width_ok(c.d_model)) return fail("d_model must be 256 or a multiple of 512");
+    if (!width_ok(c.ffn_dim)) return fail("ffn_dim must be 256 or a multiple of 512");
+    if (!width_ok(c.n_heads * c.head_dim)) return fail("n_heads*head_dim must be 256 or a multiple of 512");
+    if (c.vocab < 2 || c.vocab > (1 << 24)) return fail("vocab must be in [2, 2^24]");
+    if (c.max_seq < 1 || c.max_seq > kMaxSeq) return fail("max_seq must be in [1, 65536]");
+    if (!(c.rms_eps > 0.f) || !(c.rope_theta > 1.f)) return fail("rms_eps must be > 0 and rope_theta > 1");
+    if (c.n_experts < 0) return fail("n_experts must be >= 0");
+    if (c.n_experts) {
+        if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 16)
+            return fail("top_k must be in [1, min(n_experts, 16)]");
+        if (c.n_experts > 1024) return fail("at most 1024 experts");
+        if (c.d_model % 512 || c.ffn_dim % 512) return fail("MoE needs d_model and ffn_dim multiples of 512");
+    }
+    Dims D = dims_of(c);
+    int items = kGrid / c.n_kv_heads;
+    if ((long)items * kAttnChunkMax < c.max_seq) return fail("max_seq too long for the attention split");
+    // LDS budget: input vector and per-phase partial sums
+    int max_in = c.d_model;
+    if (c.n_heads * c.head_dim > max_in) max_in = c.n_heads * c.head_dim;
+    int kdown = c.n_experts ? c.top_k * c.ffn_dim : c.ffn_dim;
+    if (kdown > max_in) max_in = kdown;
+    if (max_in > 8192) return fail("largest GEMV input must be at most 8192 elements");
+    for (int ph = 0; ph < PH_COUNT; ++ph) {
+        if (c.n_experts == 0 && (ph == PH_ROUTER || ph == PH_EGU || ph == PH_EDOWN)) continue;
+        if (c.n_experts != 0 && (ph == PH_GU || ph == PH_DOWN)) continue;
+        for (int w = 0; w < kGrid; ++w) {
+            PhaseShape s = phase_shape(D, ph);
+            RowSplit r = split_rows(s.M, s.gran, kGrid, w);
+            int parts = (ph == PH_EDOWN ? c.top_k : 1) * r.nrows * (s.K >= 512 ? s.K / 512 : 1);
+            if (parts > 1024) return fail("a workgroup's share of a phase exceeds 1024 partial sums");
+        }
+    }
+    if (err) err->clear();
+    return KIE_OK;
+}
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+void make_layout(const kie_config& c, Layout* lay) {
+    Dims D = dims_of(c);
+    Layout& Y = *lay;
+    std::memset(&Y, 0, sizeof(Y));
+    Y.D = D;
+    int acc = 0;
+    for (int w = 0; w < kGrid; ++w) {
+        Y.piece_off[w] = acc;
+        acc += piece_units(D, kGrid, w);
+    }
+    Y.piece_off[kGrid] = acc;
+    Y.layer_bytes = (size_t)acc * kUnitBytes;
+    acc = 0;
+    for (int w = 0; w < kGrid; ++w) {
+        Y.lm_off[w] = acc;
+        acc += phase_units(D, PH_LM, kGrid, w);
+    }
+    Y.lm_off[kGrid] = acc;
+    Y.lm_bytes = (size_t)acc * kUnitBytes;
+    Y.attn_items_per_head = kGrid / D.Hkv;
+
+    const size_t A = 4096;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes, A);
+        return o;
+    };
+    Y.off_layers = take(Y.layer_bytes * D.L);
+    Y.off_lm = take(Y.lm_bytes);
+    Y.off_emb = take((size_t)D.V * D.d * 2);
+    Y.expert_bytes = D.E ? (size_t)(2 * D.F * D.d + D.d * D.F) * 2 : 0;
+    Y.off_experts = take(Y.expert_bytes * D.E * D.L);
+    Y.off_rope = take((size_t)D.max_seq * (D.hd / 2) * 8);
+    Y.kv_bytes = (size_t)D.L * D.Hkv * D.max_seq * D.hd * 2;
+    Y.off_k = take(Y.kv_bytes);
+    Y.off_v = take(Y.kv_bytes);
+    Y.off_x = take((size_t)D.d * 4);
+    Y.off_q = take((size_t)D.H * D.hd * 4);
+    Y.off_o = take((size_t)D.H * D.hd * 2);
+    size_t hlen = D.E ? (size_t)D.topk * D.F : (size_t)D.F;
+    Y.off_h = take(hlen * 2);
+    Y.off_router = take((size_t)(D.E ? D.E : 1) * 4);
+    Y.off_attn_part = take((size_t)D.H * Y.attn_items_per_head * (D.hd + 2) * 4);
+    Y.off_attn_cnt = take((size_t)D.Hkv * 64);
+    Y.off_argmax = take((size_t)kGrid * 8);
+    Y.off_bar = take((size_t)kGrid * 4);
+    Y.off_status = take(64 * 4);
+    Y.off_out = take((size_t)D.max_seq * 4);
+    Y.off_force = take((size_t)D.max_seq * 4);
+    Y.off_dbg_logits = take((size_t)kDebugRows * D.V * 4);
+    Y.off_dbg_experts = take((size_t)kDebugRows * D.L * (D.topk ? D.topk : 1) * 4);
+    Y.off_plan = take((size_t)2 * (kGrid + 1) * 4);
+    Y.off_args = take(4096);
+    Y.total = off;
+}
+
+uint16_t f32_to_f16(float f) {
+    uint32_t x;
+    std::memcpy(&x, &f, 4);
+    uint32_t sign = (x >> 16) & 0x8000u;
+    uint32_t exp = (x >> 23) & 0xffu;
+    uint32_t man = x & 0x7fffffu;
+    if (exp == 0xff) return (uint16_t)(sign | 0x7c00u | (man ? 0x200u : 0u));   // inf / nan
+    int e = (int)exp - 127 + 15;
+    if (e >= 31) return (uint16_t)(sign | 0x7c00u);                           // overflow -> inf
+    if (e <= 0) {                                                              // subnormal or zero
+        if (e < -10) return (uint16_t)sign;
+        man |= 0x800000u;
+        int shift = 14 - e;
+        uint32_t h = man >> shift;
+        uint32_t rem = man & ((1u << shift) - 1u);
+        uint32_t half = 1u << (shift - 1);
+        if (rem > half || (rem == half && (h & 1u))) h++;
+        return (uint16_t)(sign | h);
+    }
+    uint32_t h = ((uint32_t)e << 10) | (man >> 13);
+    uint32_t rem = man & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h++;   // may carry into the exponent: correct
+    return (uint16_t)(sign | h);
+}
+
+float f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t exp = (h >> 10) & 0x1fu;
+    uint32_t man = h & 0x3ffu;
+    uint32_t x;
+    if (exp == 0) {
+        if (man == 0) {
+            x = sign;
+        } else {
+            int e = -1;
+            do { man <<= 1; ++e; } while (!(man & 0x400u));
+            x = sign | ((uint32_t)(127 - 15 - e) << 23) | ((man & 0x3ffu) << 13);
+        }
+    } else if (exp == 31) {
+        x = sign | 0x7f800000u | (man << 13);
+    } else {
+        x = sign | ((exp - 15 + 127) << 23) | (man << 13);
+    }
+    float f;
+    std::memcpy(&f, &x, 4);
+    return f;
+}
+
+// Copy one row of K fp16 values, multiplying column k by gain[k] in fp32 and
+// rounding back to fp16 (exact copy when every gain is 1).
+static void put_row(uint16_t* dst, const uint16_t* src, int K, const uint16_t* gain, bool unit_gain) {
+    if (!gain || unit_gain) {
+        std::memcpy(dst, src, (size_t)K * 2);
+        return;
+    }
+    for (int k = 0; k < K; ++k) dst[k] = f32_to_f16(f16_to_f32(src[k]) * f16_to_f32(gain[k]));
+}
+
+static bool all_one(const uint16_t* g, int n) {
+    for (int i = 0; i < n; ++i)
+        if (g[i] != 0x3c00u) return false;
+    return true;
+}
+
+void repack_layer(const kie_config& c, const Layout& lay, const uint16_t* const* t, int l,
+                  uint16_t* dst) {
+    const Dims& D = lay.D;
+    const uint16_t* g_attn = t[tidx_layer(c, l, 0)];
+    const uint16_t* g_ffn = t[tidx_layer(c, l, 5)];
+    bool ga1 = all_one(g_attn, D.d), gf1 = all_one(g_ffn, D.d);
+    const uint16_t* Wq = t[tidx_layer(c, l, 1)];
+    const uint16_t* Wk = t[tidx_layer(c, l, 2)];
+    const uint16_t* Wv = t[tidx_layer(c, l, 3)];
+    const uint16_t* Wo = t[tidx_layer(c, l, 4)];
+    std::memset(dst, 0, lay.layer_bytes);
+    for (int w = 0; w < kGrid; ++w) {
+        uint16_t* p = dst + (size_t)lay.piece_off[w] * kUnitHalves;
+        for (int i = 0; i < layer_block_phase_count(D); ++i) {
+            int ph = layer_block_phase(D, i);
+            PhaseShape s = phase_shape(D, ph);
+            RowSplit r = split_rows(s.M, s.gran, kGrid, w);
+            for (int j = 0; j < r.nrows; ++j) {
+                int row = r.row0 + j;
+                uint16_t* out = p + (size_t)j * s.K;
+                switch (ph) {
+                case PH_QKV: {
+                    int mat, src;
+                    qkv_row_source(D, row, &mat, &src);
+                    const uint16_t* W = mat == 0 ? Wq : (mat == 1 ? Wk : Wv);
+                    put_row(out, W + (size_t)src * D.d, D.d, g_attn, ga1);
+                    break;
+                }
+                case PH_WO:
+                    put_row(out, Wo + (size_t)row * s.K, s.K, nullptr, true);
+                    break;
+                case PH_GU: {
+                    const uint16_t* W = t[tidx_layer(c, l, (row & 1) ? 7 : 6)];
+                    put_row(out, W + (size_t)(row >> 1) * D.d, D.d, g_ffn, gf1);
+                    break;
+                }
+                case PH_DOWN:
+                    put_row(out, t[tidx_layer(c, l, 8)] + (size_t)row * s.K, s.K, nullptr, true);
+                    break;
+                case PH_ROUTER:
+                    put_row(out, t[tidx_layer(c, l, 6)] + (size_t)row * D.d, D.d, g_ffn, gf1);
+                    break;
+                }
+            }
+            p += (size_t)slab_units(r.nrows, s.K) * kUnitHalves;
+        }
+    }
+}
+
+void repack_lm(const kie_config& c, const Layout& lay, const uint16_t* const* t, uint16_t* dst) {
+    const Dims& D = lay.D;
+    const uint16_t* g = t[tidx_gfinal(c)];
+    bool g1 = all_one(g, D.d);
+    const uint16_t* W = t[tidx_lm(c)];
+    std::memset(dst, 0, lay.lm_bytes);
+    for (int w = 0; w < kGrid; ++w) {
+        RowSplit r = split_rows(D.V, 1, kGrid, w);
+        uint16_t* p = dst + (size_t)lay.lm_off[w] * kUnitHalves;
+        for (int j = 0; j < r.nrows; ++j)
+            put_row(p + (size_t)j * D.d, W + (size_t)(r.row0 + j) * D.d, D.d, g, g1);
+    }
+}
+
+void repack_expert(const kie_config& c, const Layout& lay, const uint16_t* const* t, int l, int e,
+                   uint16_t* dst) {
+    const Dims& D = lay.D;
+    const uint16_t* g = t[tidx_layer(c, l, 5)];
+    bool g1 = all_one(g, D.d);
+    const uint16_t* Wg = t[tidx_expert(c, l, e, 0)];
+    const uint16_t* Wu = t[tidx_expert(c, l, e, 1)];
+    const uint16_t* Wd = t[tidx_expert(c, l, e, 2)];
+    for (int r = 0; r < 2 * D.F; ++r)
+        put_row(dst + (size_t)r * D.d, ((r & 1) ? Wu : Wg) + (size_t)(r >> 1) * D.d, D.d, g, g1);
+    std::memcpy(dst + (size_t)2 * D.F * D.d, Wd, (size_t)D.d * D.F * 2);
+}
+
+void rope_table(const kie_config& c, float* dst) {
+    int half = c.head_dim / 2;
+    for (int p = 0; p < c.max_seq; ++p) {
+        for (int i = 0; i < half; ++i) {
+            double inv = std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
+            double a = (double)p * inv;
+            dst[((size_t)p * half + i) * 2 + 0] = (float)std::cos(a);
+            dst[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
+        }
+    }
+}
+
+}  // namespace kie

@@ -1,0 +1,80 @@
+// kie_host.h - host-only preparation: validation, workspace layout, weight
+// repacking and the rotary table. No HIP in here, so it builds with g++ too.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/kie.h"
+#include "kie_common.h"
+
+namespace kie {
+
+constexpr int kDebugRows = 64;    // logits rows buffered on the device per launch
+
+// Byte offsets of every region of the caller's device workspace.
+struct Layout {
+    Dims D;
+    size_t layer_bytes;           // one layer's streaming block
+    size_t off_layers;            // L blocks
+    size_t off_lm;                // LM head block
+    size_t lm_bytes;
+    size_t off_emb;               // embedding table [V][d] fp16
+    size_t off_experts;           // MoE: per layer, per expert [GU interleaved 2F x d][Wd d x F]
+    size_t expert_bytes;          // one expert block
+    size_t off_rope;              // float2 [max_seq][hd/2] (cos, sin)
+    size_t off_k, off_v;          // fp16 [L][Hkv][max_seq][hd]
+    size_t kv_bytes;              // one of K or V
+    size_t off_x;                 // fp32 [d] residual
+    size_t off_q;                 // fp32 [H*hd]
+    size_t off_o;                 // fp16 [H*hd]
+    size_t off_h;                 // fp16 [max(F, topk*F)]
+    size_t off_router;            // fp32 [E]
+    size_t off_attn_part;         // fp32 [H][items per kv head][hd + 2]
+    size_t off_attn_cnt;          // u32 [Hkv] (padded)
+    size_t off_argmax;            // {f32, i32} [kGrid]
+    size_t off_bar;               // u32 [kGrid] barrier slots
+    size_t off_status;            // u32 [64]
+    size_t off_out;               // i32 [max_seq]
+    size_t off_force;             // i32 [max_seq]
+    size_t off_dbg_logits;        // f32 [kDebugRows][V]
+    size_t off_dbg_experts;       // i32 [kDebugRows][L][topk]
+    size_t off_plan;              // i32 piece_off[kGrid+1], lm_off[kGrid+1]
+    size_t off_args;              // kernel argument block (4 KiB)
+    size_t total;
+    int piece_off[kGrid + 1];     // units: start of workgroup w's piece in a layer block
+    int lm_off[kGrid + 1];        // units: start of workgroup w's LM slab
+    int attn_items_per_head;
+};
+
+Dims dims_of(const kie_config& c);
+// Returns KIE_OK or an error code with a message.
+int validate_config(const kie_config& c, std::string* err);
+int tensor_count(const kie_config& c);
+void make_layout(const kie_config& c, Layout* lay);
+
+// fp16 <-> fp32 (IEEE binary16, round to nearest even).
+uint16_t f32_to_f16(float f);
+float f16_to_f32(uint16_t h);
+
+// Fill one layer's streaming block (layer_bytes bytes) from the canonical tensors.
+void repack_layer(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer,
+                  uint16_t* dst);
+// Fill the LM head block (lm_bytes bytes).
+void repack_lm(const kie_config& c, const Layout& lay, const uint16_t* const* t, uint16_t* dst);
+// Fill one expert block (expert_bytes bytes).
+void repack_expert(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer,
+                   int expert, uint16_t* dst);
+// cos/sin table, angles formed in double precision. dst: float [max_seq][hd/2][2].
+void rope_table(const kie_config& c, float* dst);
+
+// Canonical tensor index helpers (same order as kie.h documents).
+int tidx_emb();
+int tidx_layer(const kie_config& c, int layer, int which);   // which: 0 g_attn,1 Wq,2 Wk,3 Wv,4 Wo,5 g_ffn,6 Wg|Wr,7 Wu,8 Wd
+int tidx_expert(const kie_config& c, int layer, int expert, int which);  // which: 0 Wg, 1 Wu, 2 Wd
+int tidx_gfinal(const kie_config& c);
+int tidx_lm(const kie_config& c);
+
+}  // namespace kie

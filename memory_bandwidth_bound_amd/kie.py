@@ -1,0 +1,274 @@
+"""Python binding of libkie.so (include/kie.h): argument marshalling only.
+
+Every step of decode runs in the library's HIP kernels. PyTorch is used only
+to allocate the device workspace and to name the stream the library enqueues
+on. If the shared library is missing this module raises at import of the
+library: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
+from typing import Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkie.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kie.h")
+
+KIE_OK = 0
+STATUS = {0: "KIE_OK", -1: "KIE_ERR_ARG", -2: "KIE_ERR_CONFIG", -3: "KIE_ERR_CAPACITY",
+          -4: "KIE_ERR_WORKSPACE", -5: "KIE_ERR_DEVICE", -6: "KIE_ERR_HIP", -7: "KIE_ERR_TIMEOUT",
+          -8: "KIE_ERR_STATE"}
+
+
+class KieConfig(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_heads", c_int32),
+                ("n_kv_heads", c_int32), ("head_dim", c_int32), ("ffn_dim", c_int32),
+                ("vocab", c_int32), ("n_experts", c_int32), ("top_k", c_int32),
+                ("rms_eps", c_float), ("rope_theta", c_float), ("max_seq", c_int32)]
+
+
+class KieDebug(ctypes.Structure):
+    _fields_ = [("force_ids", POINTER(c_int32)), ("logits", POINTER(c_float)),
+                ("experts", POINTER(c_int32))]
+
+
+class KieError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkie.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m memory_bandwidth_bound_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "kie_workspace_bytes": (c_size_t, [POINTER(KieConfig)]),
+        "kie_tensor_count": (c_int32, [POINTER(KieConfig)]),
+        "kie_load": (c_int32, [POINTER(KieConfig), POINTER(c_void_p), c_int32, c_void_p, c_size_t,
+                               c_void_p, POINTER(c_void_p)]),
+        "kie_prefill": (c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32), POINTER(KieDebug)]),
+        "kie_set_kv": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32]),
+        "kie_decode": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(KieDebug)]),
+        "kie_rewind": (c_int32, [c_void_p, c_int32, c_int32]),
+        "kie_reset": (c_int32, [c_void_p]),
+        "kie_state": (c_int32, [c_void_p, POINTER(c_int32), POINTER(c_int32)]),
+        "kie_last_kernel_ms": (c_float, [c_void_p]),
+        "kie_grid_size": (c_int32, [c_void_p]),
+        "kie_free": (None, [c_void_p]),
+        "kie_last_error": (ctypes.c_char_p, [c_void_p]),
+        "kie_status_str": (ctypes.c_char_p, [c_int32]),
+        "kie_gemv_probe": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                     c_void_p, POINTER(c_float)]),
+        "kie_barrier_probe_bytes": (c_size_t, []),
+        "kie_barrier_probe": (c_int32, [c_void_p, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
+        "kie_launch_probe": (c_int32, [c_int32, c_void_p, POINTER(c_float)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_symbols(path: str = HEADER):
+    """Function names declared in include/kie.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kie_\w+)\s*\(", text)))
+
+
+def make_config(cfg) -> KieConfig:
+    """kie_config from a synth.DecoderConfig (or anything with the same fields)."""
+    return KieConfig(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
+                     cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k if cfg.n_experts else 0,
+                     cfg.rms_eps, cfg.rope_theta, cfg.max_seq)
+
+
+def workspace_bytes(cfg) -> int:
+    return int(load_library().kie_workspace_bytes(ctypes.byref(make_config(cfg))))
+
+
+def _check(code: int, model_ptr=None):
+    if code != KIE_OK:
+        msg = load_library().kie_last_error(model_ptr)
+        raise KieError(code, msg.decode() if msg else "")
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(POINTER(c_int32))
+
+
+def _stream_handle(torch, device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return c_void_p(s.cuda_stream)
+
+
+class Model:
+    """One loaded decoder: a device workspace plus the library's model handle."""
+
+    def __init__(self, cfg, tensors: Sequence[np.ndarray], device: str = "cuda:0", stream=None):
+        import torch
+        lib = load_library()
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self._torch = torch
+        kc = make_config(cfg)
+        self._kc = kc
+        nbytes = int(lib.kie_workspace_bytes(ctypes.byref(kc)))
+        if nbytes == 0:
+            raise KieError(-2, lib.kie_last_error(None).decode())
+        n = int(lib.kie_tensor_count(ctypes.byref(kc)))
+        if n != len(tensors):
+            raise KieError(-1, f"expected {n} tensors, got {len(tensors)}")
+        host = [np.ascontiguousarray(t, dtype=np.float16) for t in tensors]
+        ptrs = (c_void_p * n)(*[t.ctypes.data for t in host])
+        with torch.cuda.device(self.device):
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._stream = stream
+            handle = c_void_p()
+            rc = lib.kie_load(ctypes.byref(kc), ptrs, n, c_void_p(self.workspace.data_ptr()), nbytes,
+                              _stream_handle(torch, self.device, stream), ctypes.byref(handle))
+        _check(rc)
+        self._h = handle
+        self._lib = lib
+
+    # ---- calls -------------------------------------------------------------
+    def _dbg(self, n, force, logits, experts):
+        dbg = KieDebug()
+        keep = {}
+        if force is not None:
+            f = np.ascontiguousarray(force, dtype=np.int32)
+            keep["force"] = f
+            dbg.force_ids = _i32p(f)
+        if logits:
+            lg = np.zeros((n, self.cfg.vocab), dtype=np.float32)
+            keep["logits"] = lg
+            dbg.logits = lg.ctypes.data_as(POINTER(c_float))
+        if experts:
+            ex = np.zeros((n, self.cfg.n_layers, self.cfg.top_k), dtype=np.int32)
+            keep["experts"] = ex
+            dbg.experts = _i32p(ex)
+        return dbg, keep
+
+    def prefill(self, tokens, logits: bool = False, experts: bool = False):
+        """Returns (first token, logits [n][vocab] or None, experts or None)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        first = c_int32()
+        dbg, keep = self._dbg(len(t), None, logits, experts)
+        with self._torch.cuda.device(self.device):
+            rc = self._lib.kie_prefill(self._h, _i32p(t), len(t), ctypes.byref(first),
+                                       ctypes.byref(dbg) if keep else None)
+        _check(rc, self._h)
+        return first.value, keep.get("logits"), keep.get("experts")
+
+    def decode(self, n: int, force=None, logits: bool = False, experts: bool = False):
+        """Returns (ids [n], logits [n][vocab] or None, experts or None)."""
+        out = np.zeros(n, dtype=np.int32)
+        dbg, keep = self._dbg(n, force, logits, experts)
+        with self._torch.cuda.device(self.device):
+            rc = self._lib.kie_decode(self._h, n, _i32p(out), ctypes.byref(dbg) if keep else None)
+        _check(rc, self._h)
+        return out, keep.get("logits"), keep.get("experts")
+
+    def set_kv(self, K: np.ndarray, V: np.ndarray, pending: int):
+        K = np.ascontiguousarray(K, dtype=np.float16)
+        V = np.ascontiguousarray(V, dtype=np.float16)
+        with self._torch.cuda.device(self.device):
+            rc = self._lib.kie_set_kv(self._h, c_void_p(K.ctypes.data), c_void_p(V.ctypes.data),
+                                      K.shape[1], int(pending))
+        _check(rc, self._h)
+
+    def rewind(self, pos: int, pending: int):
+        _check(self._lib.kie_rewind(self._h, int(pos), int(pending)), self._h)
+
+    def reset(self):
+        with self._torch.cuda.device(self.device):
+            _check(self._lib.kie_reset(self._h), self._h)
+
+    def state(self):
+        p, t = c_int32(), c_int32()
+        _check(self._lib.kie_state(self._h, ctypes.byref(p), ctypes.byref(t)), self._h)
+        return p.value, t.value
+
+    @property
+    def last_kernel_ms(self) -> float:
+        return float(self._lib.kie_last_kernel_ms(self._h))
+
+    @property
+    def grid_size(self) -> int:
+        return int(self._lib.kie_grid_size(self._h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.kie_free(self._h)
+            self._h = None
+            self.workspace = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---- probes -----------------------------------------------------------------
+
+def gemv_probe(A, x, variant: int = 0, stream=None):
+    """y[c] = A[c] @ x for a device fp16 tensor A [copies, M, K] and x [K].
+
+    Returns (y float32 [copies, M], device milliseconds of the one launch).
+    """
+    import torch
+    lib = load_library()
+    assert A.dtype == torch.float16 and x.dtype == torch.float16 and A.is_cuda and x.is_cuda
+    A = A.contiguous()
+    x = x.contiguous()
+    copies, M, K = A.shape
+    y = torch.empty((copies, M), dtype=torch.float32, device=A.device)
+    ms = c_float()
+    with torch.cuda.device(A.device):
+        rc = lib.kie_gemv_probe(c_void_p(A.data_ptr()), c_void_p(x.data_ptr()), c_void_p(y.data_ptr()),
+                                M, K, copies, variant, _stream_handle(torch, A.device, stream),
+                                ctypes.byref(ms))
+    _check(rc)
+    return y, float(ms.value)
+
+
+def barrier_probe(rounds: int, device: str = "cuda:0"):
+    """Mean microseconds per grid barrier across the 256-workgroup grid, and
+    the number of rounds whose all-gathered values were wrong."""
+    import torch
+    lib = load_library()
+    scratch = torch.zeros(int(lib.kie_barrier_probe_bytes()), dtype=torch.uint8, device=device)
+    us, err = c_float(), c_int32()
+    with torch.cuda.device(scratch.device):
+        rc = lib.kie_barrier_probe(c_void_p(scratch.data_ptr()), rounds,
+                                   _stream_handle(torch, scratch.device, None), ctypes.byref(us),
+                                   ctypes.byref(err))
+    _check(rc)
+    return float(us.value), int(err.value)
+
+
+def launch_probe(launches: int, device: str = "cuda:0"):
+    """Host wall-clock microseconds per back-to-back launch of an empty kernel."""
+    import torch
+    lib = load_library()
+    us = c_float()
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        rc = lib.kie_launch_probe(launches, _stream_handle(torch, dev, None), ctypes.byref(us))
+    _check(rc)
+    return float(us.value)

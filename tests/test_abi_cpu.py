@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments and configurations before touching HIP."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import synth
+from memory_bandwidth_bound_amd import kie
+
+LIB = kie.LIB_PATH
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libkie.so not built")
+    return kie.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = kie.header_symbols()
+    assert len(declared) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert hasattr(lib, s)
+
+
+def test_status_strings(lib):
+    for code in range(0, -9, -1):
+        s = lib.kie_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.kie_status_str(-99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("name", ["tiny", "2b", "2b_32k", "moe"])
+def test_workspace_bytes_cover_weights_and_cache(lib, name):
+    cfg = synth.get_config(name)
+    n = kie.workspace_bytes(cfg)
+    from memory_bandwidth_bound_amd import roofline
+    weights = 2 * sum(int(np.prod(s)) for _, s, k in synth.tensor_specs(cfg) if k != "gain")
+    kv = 2 * roofline.kv_bytes_per_position(cfg) * cfg.max_seq // 2 * 2
+    assert n >= weights + kv // 2
+    assert n < 1.2 * (weights + kv) + (64 << 20)
+    assert lib.kie_tensor_count(ctypes.byref(kie.make_config(cfg))) == len(synth.tensor_specs(cfg))
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=96), dict(n_heads=6, n_kv_heads=4), dict(n_heads=36, n_kv_heads=4),
+    dict(d_model=768), dict(ffn_dim=300), dict(max_seq=0), dict(max_seq=70000), dict(vocab=1),
+    dict(n_layers=0), dict(rms_eps=0.0), dict(n_experts=4, top_k=5), dict(n_experts=4, top_k=2, d_model=256),
+])
+def test_invalid_configs_rejected(lib, bad):
+    kc = kie.make_config(synth.get_config("tiny"))
+    for k, v in bad.items():
+        setattr(kc, k, v)
+    assert lib.kie_workspace_bytes(ctypes.byref(kc)) == 0
+    assert lib.kie_last_error(None).decode()
+    h = ctypes.c_void_p()
+    ptrs = (ctypes.c_void_p * 1)(1)
+    rc = lib.kie_load(ctypes.byref(kc), ptrs, 1, ctypes.c_void_p(1), 1 << 40, None, ctypes.byref(h))
+    assert rc == -2 and not h.value
+
+
+def test_load_argument_errors_before_any_device_call(lib):
+    cfg = synth.get_config("tiny")
+    kc = kie.make_config(cfg)
+    h = ctypes.c_void_p()
+    n = lib.kie_tensor_count(ctypes.byref(kc))
+    ptrs = (ctypes.c_void_p * n)(*([1] * n))
+    # null workspace
+    assert lib.kie_load(ctypes.byref(kc), ptrs, n, None, 1 << 30, None, ctypes.byref(h)) == -1
+    # wrong tensor count
+    assert lib.kie_load(ctypes.byref(kc), ptrs, n - 1, ctypes.c_void_p(1), 1 << 30, None, ctypes.byref(h)) == -1
+    # a null tensor
+    ptrs0 = (ctypes.c_void_p * n)(*([1] * (n - 1) + [0]))
+    assert lib.kie_load(ctypes.byref(kc), ptrs0, n, ctypes.c_void_p(1), 1 << 30, None, ctypes.byref(h)) == -1
+    # workspace too small
+    ws = kie.workspace_bytes(cfg)
+    assert lib.kie_load(ctypes.byref(kc), ptrs, n, ctypes.c_void_p(1), ws - 1, None, ctypes.byref(h)) == -4
+    assert not h.value
+
+
+def test_null_model_calls(lib):
+    out = np.zeros(4, dtype=np.int32)
+    assert lib.kie_decode(None, 4, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None) == -1
+    assert lib.kie_reset(None) == -1
+    assert lib.kie_rewind(None, 0, 0) == -1
+    assert lib.kie_last_kernel_ms(None) == 0.0
+    lib.kie_free(None)
+
+
+def test_probe_argument_errors(lib):
+    ms = ctypes.c_float()
+    # K not a multiple of 512
+    assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 300, 1, 0, None,
+                              ctypes.byref(ms)) == -1
+    # too many rows per workgroup for the ring variant
+    assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 1 << 20, 8192, 1, 0,
+                              None, ctypes.byref(ms)) == -1
+    assert lib.kie_gemv_probe(None, ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 512, 1, 0, None, None) == -1
+    assert lib.kie_barrier_probe(None, 10, None, ctypes.byref(ms), None) == -1
+    assert lib.kie_launch_probe(0, None, ctypes.byref(ms)) == -1

@@ -1,0 +1,98 @@
+"""GEMV bandwidth probe, grid-barrier probe and launch probe on the GPU.
+
+Parity: the probe GEMV against the oracle's float64 GEMV within the fp32
+accumulation bound, bit-exact on integer-valued inputs, and x = e_j returns
+column j exactly."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.parity import gemv_bound, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from memory_bandwidth_bound_amd import kie
+    kie.load_library()
+    return torch
+
+
+def _run(torch, A, x, variant):
+    from memory_bandwidth_bound_amd import kie
+    At = torch.from_numpy(A).cuda()
+    xt = torch.from_numpy(x).cuda()
+    y, ms = kie.gemv_probe(At, xt, variant=variant)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64), ms
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("shape", [(512, 2560, 3), (300, 1024, 2), (2560, 8192, 1), (257, 512, 2)])
+def test_gemv_probe_matches_f64(torch_cuda, variant, shape):
+    M, K, C = shape
+    say(f"gemv probe variant={variant} M={M} K={K} copies={C}")
+    rng = np.random.default_rng(M * K + C)
+    A = (rng.standard_normal((C, M, K), dtype=np.float32) * 0.02).astype(np.float16)
+    x = rng.standard_normal(K, dtype=np.float32).astype(np.float16)
+    y, _ = _run(torch_cuda, A, x, variant)
+    for c in range(C):
+        ref = oracle.gemv_f64(A[c], x)
+        assert np.all(np.abs(y[c] - ref) <= gemv_bound(A[c], x)), f"copy {c}"
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_gemv_probe_integer_exact_and_unit_vector(torch_cuda, variant):
+    say(f"gemv probe integer/unit variant={variant}")
+    rng = np.random.default_rng(7)
+    M, K = 640, 2560
+    A = rng.integers(-8, 9, size=(1, M, K)).astype(np.float16)
+    x = rng.integers(-8, 9, size=K).astype(np.float16)
+    y, _ = _run(torch_cuda, A, x, variant)
+    assert np.array_equal(y[0], oracle.gemv_f64(A[0], x))
+    A = rng.standard_normal((1, M, K)).astype(np.float16)
+    for j in (0, 511, 2559):
+        e = np.zeros(K, dtype=np.float16)
+        e[j] = 1
+        y, _ = _run(torch_cuda, A, e, variant)
+        assert np.array_equal(y[0], A[0][:, j].astype(np.float64))
+
+
+@pytest.mark.parametrize("si", [0, 1, 2, 3])
+def test_gemv_probe_full_shapes_sampled(torch_cuda, si):
+    """The probe shapes at full size, in the benchmark's launch configuration
+    (rotating copies); sampled rows checked against the float64 GEMV."""
+    cfg = synth.get_config("gemv")
+    M, K = cfg.shapes[si]
+    A, x = synth.make_probe(si, M, K)
+    copies = 3
+    say(f"gemv probe full shape {M}x{K} copies={copies}")
+    Ac = np.stack([A] * copies)
+    y, ms = _run(torch_cuda, Ac, x, 0)
+    rows = np.random.default_rng(si).choice(M, size=min(M, 64), replace=False)
+    ref = oracle.gemv_f64(A[rows], x)
+    bnd = gemv_bound(A[rows], x)
+    for c in range(copies):
+        assert np.all(np.abs(y[c][rows] - ref) <= bnd)
+    assert ms > 0
+
+
+def test_barrier_probe(torch_cuda):
+    from memory_bandwidth_bound_amd import kie
+    say("barrier probe 20000 rounds")
+    us, err = kie.barrier_probe(20000)
+    say(f"barrier: {us:.3f} us per grid barrier (256 workgroups), errors={err}")
+    assert err == 0
+    assert 0 < us < 100
+
+
+def test_launch_probe(torch_cuda):
+    from memory_bandwidth_bound_amd import kie
+    us = kie.launch_probe(2000)
+    say(f"launch probe: {us:.2f} us per empty kernel launch")
+    assert us > 0
