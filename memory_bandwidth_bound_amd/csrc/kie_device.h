@@ -182,7 +182,7 @@ __device__ __forceinline__ bool ring_wait_ready(KIE_LDS RingCtl* ctl, uint32_t u
 // `gen` is the value the counter must reach (caller adds NC per sync).
 __device__ __forceinline__ bool consumer_sync(KIE_LDS RingCtl* ctl, uint32_t gen, uint32_t limit) {
     wait_lgkm0();
-    lds_add_u32(&ctl->sync, 1u);
+    if (lane_id() == 0) lds_add_u32(&ctl->sync, 1u);   // one arrival per wave
     uint32_t spins = 0;
     while (true) {
         uint32_t v = lds_ld_u32(&ctl->sync);

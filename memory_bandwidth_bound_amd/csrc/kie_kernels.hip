@@ -216,6 +216,14 @@ struct Consumer {
         return sync();
     }
 
+    // The next stream unit this wave will consume after phase-local unit i of
+    // a phase of n units starting at U0: the next unit of its residue class in
+    // this phase, else its first unit of the following phase. Publishing
+    // anything larger would let the streamer overwrite a slot not yet read.
+    __device__ __forceinline__ uint32_t next_unit(uint32_t U0, int i, int n) {
+        return (i + kConsumers < n) ? U0 + (uint32_t)(i + kConsumers) : U0 + (uint32_t)(n + cw);
+    }
+
     // --- the streamed GEMV ------------------------------------------------
     // Units U..U+n-1 of the stream hold this workgroup's rows. Segment-major:
     // nseg segments of nrows rows of K fp16 each (nseg > 1 only for the MoE
@@ -236,7 +244,7 @@ struct Consumer {
                 int cc = rem - row * upr;
                 uint4 xv = lds_ld16(xin + seg * K + cc * 512 + lane * 8);
                 float acc = dot8(w, xv, 0.f);
-                lds_st_u32(&ctl->cons[cw], u + kConsumers);
+                lds_st_u32(&ctl->cons[cw], next_unit(U0, i, n));
                 acc = wave_sum_to_lane63(acc);
                 if (lane == 63) part[row * (nseg * upr) + seg * upr + cc] = acc;
             }
@@ -248,7 +256,7 @@ struct Consumer {
                 uint4 w = lds_ld16(ring + (u & RC::kMask) * kUnitBytes + lane * 16);
                 uint4 xv = lds_ld16(xin + (lane & 31) * 8);
                 float acc = dot8(w, xv, 0.f);
-                lds_st_u32(&ctl->cons[cw], u + kConsumers);
+                lds_st_u32(&ctl->cons[cw], next_unit(U0, i, n));
                 acc = half32_sum_from_rows(row16_sum(acc));
                 int row = 2 * i + (lane >> 5);
                 if ((lane & 31) == 31 && row < nrows) part[row] = acc;
@@ -731,7 +739,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_ring_kernel(GemvArgs a) {
             int row = i / upr, cc = i - row * upr;
             uint4 xv = *(const uint4*)(a.x + cc * 512 + lane * 8);   // x stays in L1/L2
             float acc = dot8(w, xv, 0.f);
-            lds_st_u32(&ctl->cons[cw], u + kConsumers);
+            // the next unit this wave consumes (see Consumer::next_unit)
+            lds_st_u32(&ctl->cons[cw], (i + kConsumers < n) ? u + kConsumers : U + (uint32_t)(n + cw));
             acc = wave_sum_to_lane63(acc);
             if (lane == 63) part[row * upr + cc] = acc;
         }
