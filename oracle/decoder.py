@@ -265,6 +265,16 @@ class Decoder:
         self.pending = first
         return first, logits
 
+    def prefill_batched(self, prompt: Sequence[int]):
+        """Same result as ``prefill`` (up to rounding order), computed with one
+        causal forward over the whole prompt; returns (first token, last logits)."""
+        self.reset()
+        logits = self.forward_full(list(prompt), store_kv=True)[-1]
+        self.pos = len(prompt)
+        first = greedy_argmax(logits)
+        self.pending = first
+        return first, logits
+
     def decode(self, n: int, force: Optional[Sequence[int]] = None,
                keep_logits: bool = False, expert_overrides=None):
         """n passes; returns (ids, logits rows or None, experts per pass)."""
@@ -283,11 +293,13 @@ class Decoder:
         return np.asarray(ids, dtype=np.int32), (np.stack(rows) if keep_logits else None), exps
 
     # ---- non-incremental reference ----------------------------------------
-    def forward_full(self, tokens: Sequence[int]) -> np.ndarray:
+    def forward_full(self, tokens: Sequence[int], store_kv: bool = False) -> np.ndarray:
         """Logits at every position of ``tokens`` by a full causal recompute.
 
-        No KV cache: all positions are projected at once and attention applies
-        an explicit causal mask. Used to check the incremental path.
+        All positions are projected at once and attention applies an explicit
+        causal mask; the incremental path is checked against it. With
+        ``store_kv`` the rotated keys and the values of positions 0..T-1 are
+        also written to the cache (a batched prefill).
         """
         cfg, dt = self.cfg, self.dtype
         T = len(tokens)
@@ -303,6 +315,9 @@ class Decoder:
             Vf = (Hn @ self.w(f"l{l}.Wv").T).reshape(T, Hkv, hd)
             Q = apply_rope(Q, cos[:, None, :], sin[:, None, :])
             Kf = apply_rope(Kf, cos[:, None, :], sin[:, None, :])
+            if store_kv:
+                self.K[l, :T] = Kf
+                self.V[l, :T] = Vf
             O = np.empty((T, H, hd), dtype=dt)
             for j in range(H):
                 g = j // group

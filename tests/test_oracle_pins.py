@@ -332,6 +332,24 @@ def test_decoder_incremental_equals_full_causal():
     np.testing.assert_allclose(inc, full, rtol=1e-11, atol=1e-12)
 
 
+def test_batched_prefill_equals_incremental_prefill():
+    cfg = _tiny(n_layers=2, vocab=40, decode_steps=4)
+    W = make_weights(cfg)
+    P = [int(t) for t in np.random.default_rng(15).integers(0, cfg.vocab, cfg.prompt_len)]
+    a = oracle.Decoder(cfg, W, dtype=np.float64)
+    b = oracle.Decoder(cfg, W, dtype=np.float64)
+    fa, la = a.prefill(P)
+    fb, lb = b.prefill_batched(P)
+    assert fa == fb and a.pos == b.pos == len(P)
+    np.testing.assert_allclose(la, lb, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(a.K, b.K, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(a.V, b.V, rtol=1e-11, atol=1e-13)
+    ia, ra, _ = a.decode(3, keep_logits=True)
+    ib, rb, _ = b.decode(3, keep_logits=True)
+    np.testing.assert_array_equal(ia, ib)
+    np.testing.assert_allclose(ra, rb, rtol=1e-10, atol=1e-12)
+
+
 def test_decoder_causal_mask_ignores_future_cache():
     cfg = _tiny(decode_steps=10)
     W = make_weights(cfg)
