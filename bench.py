@@ -1,0 +1,266 @@
+"""Batch-1 decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2b|2b_32k|moe|tiny|gemv]
+
+A step is one generation request: ONE kie_decode launch of the workload's
+decode length (1024 greedy tokens for the default ~2.1B decoder) from the
+same post-prompt state. W untimed steps, then exactly K timed steps bracketed
+by torch.cuda.synchronize(); one JSON line is printed. Inputs are seeded and
+synthetic and stay resident in HBM; the workload stands in for the pages' 2B
+model (25 layers, fp16, batch 1).
+
+The JSON line carries:
+  value      whole-job tokens/s (one GPU);
+  mbu        (active weight + KV bytes per token) x tok/s / 8 TB/s;
+  roofline   algorithmic bytes of one launch / the launch's mean device time
+             (HIP events recorded by the library on its stream), against the
+             8 TB/s HBM peak; traffic from committed rocprofv3 counter
+             summaries when they match the current kernel sources, else null;
+  cpu_baseline  the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from memory_bandwidth_bound_amd import roofline  # noqa: E402
+
+PEAK_GBS = roofline.HBM_PEAK_BYTES_PER_S / 1e9
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "memory_bandwidth_bound_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(name: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def describe(cfg) -> str:
+    s = (f"{cfg.name} decoder: {cfg.n_layers} layers, d_model {cfg.d_model}, {cfg.n_heads} query / "
+         f"{cfg.n_kv_heads} KV heads x {cfg.head_dim}, SwiGLU {cfg.ffn_dim}")
+    if cfg.n_experts:
+        s += f" x {cfg.n_experts} experts (top-{cfg.top_k})"
+    s += f", vocab {cfg.vocab}, fp16 weights N(0,{cfg.weight_sigma}); batch 1, "
+    if cfg.kv_prefill:
+        s += f"KV cache pre-filled with {cfg.kv_prefill} seeded positions, "
+    else:
+        s += f"{cfg.prompt_len}-token prompt, "
+    s += f"{cfg.decode_steps} greedy decode steps per request"
+    return s
+
+
+# ----------------------------------------------------------------------------
+def cpu_baseline_decode(cfg, W, prompt, target_s: float):
+    """The oracle as it stands, timed on this host on a bounded sample: greedy
+    decode passes right after the prompt (or the pre-filled cache)."""
+    import oracle
+    dec = oracle.Decoder(cfg, W)
+    if cfg.kv_prefill:
+        K, V = synth.make_kv_prefill(cfg)
+        dec.set_kv(K, V, synth.make_pending_token(cfg))
+        del K, V
+    else:
+        dec.prefill_batched(prompt)
+    t0 = time.perf_counter()
+    dec.decode(1)
+    t1 = time.perf_counter() - t0
+    n = int(max(2, min(64, round(target_s / max(t1, 1e-3)))))
+    t0 = time.perf_counter()
+    dec.decode(n)
+    dt = time.perf_counter() - t0
+    start = (cfg.kv_prefill or cfg.prompt_len) + 1
+    return {"value": n / dt, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{n} greedy decode passes of the {cfg.name} decoder at positions "
+                      f"{start}..{start + n - 1} (numpy fp32 on fp16 weights), after one untimed pass; "
+                      f"host os.cpu_count()={os.cpu_count()}"}
+
+
+def bench_decode(cfg, args):
+    import torch
+    from memory_bandwidth_bound_amd import kie
+    t_setup = time.perf_counter()
+    W = synth.make_weights(cfg)
+    prompt = synth.make_prompt(cfg)
+    m = kie.Model(cfg, W, device="cuda:0")
+    if cfg.kv_prefill:
+        K, V = synth.make_kv_prefill(cfg)
+        pend = synth.make_pending_token(cfg)
+        m.set_kv(K, V, pend)
+        del K, V
+        pos0, first = cfg.kv_prefill, pend
+    else:
+        first, _, _ = m.prefill(prompt)
+        pos0 = cfg.prompt_len
+    n = cfg.decode_steps
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s; decode {n} tokens per step from position {pos0}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        m.rewind(pos0, first)
+        m.decode(n)
+    torch.cuda.synchronize()
+    kms = []
+    ids_first = None
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m.rewind(pos0, first)
+        ids, _, _ = m.decode(n)
+        kms.append(m.last_kernel_ms)
+        if ids_first is None:
+            ids_first = ids
+        elif not np.array_equal(ids, ids_first):
+            raise RuntimeError("repeated decode requests produced different tokens")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tok_s = args.steps * n / wall
+    algo = roofline.decode_bytes(cfg, pos0, n)
+    k_ms = float(np.mean(kms))
+    per_tok = algo / n
+    achieved = algo / (k_ms * 1e-3) / 1e9
+    traffic = counters_traffic(f"decode_{cfg.name}")
+    line = {
+        "metric": "batch-1 decode tokens/sec on 1 MI355X + MBU (% of 8 TB/s HBM)",
+        "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "global_batch": 1, "seq_len": pos0 + n,
+                   "decode_tokens_per_step": n, "parallelism": "single GPU, one persistent launch per request"},
+        "mbu": round(per_tok * tok_s / roofline.HBM_PEAK_BYTES_PER_S, 4),
+        "bytes_per_token": per_tok,
+        "kernel_ms_mean": round(k_ms, 3),
+        "kernel_tok_per_s": round(n / (k_ms * 1e-3), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic},
+        "launches_per_request": 1,
+    }
+    m.close()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(cfg, W, prompt, args.cpu_seconds)
+    return line
+
+
+def bench_gemv(args):
+    import torch
+    import oracle
+    from memory_bandwidth_bound_amd import kie
+    cfg = synth.get_config("gemv")
+    shapes = []
+    tot_bytes, tot_ms = 0.0, 0.0
+    for si, (M, K) in enumerate(cfg.shapes):
+        A, x = synth.make_probe(si, M, K)
+        mat = 2 * M * K
+        copies = max(1, -(-(1 << 30) // mat))       # >= 1 GiB per launch (4x the 256 MB MALL)
+        At = torch.from_numpy(A).cuda()
+        Ac = At.unsqueeze(0).repeat(copies, 1, 1).contiguous()
+        xt = torch.from_numpy(x).cuda()
+        for _ in range(args.warmup):
+            kie.gemv_probe(Ac, xt, variant=0)
+        ms = []
+        for _ in range(args.steps):
+            _, t = kie.gemv_probe(Ac, xt, variant=0)
+            ms.append(t)
+        _, t_direct = kie.gemv_probe(Ac, xt, variant=1)
+        b = copies * roofline.gemv_bytes(M, K)
+        gbs = b / (np.mean(ms) * 1e-3) / 1e9
+        shapes.append({"shape": [M, K], "copies": copies, "GB_s": round(gbs, 1),
+                       "direct_GB_s": round(b / (t_direct * 1e-3) / 1e9, 1)})
+        tot_bytes += b
+        tot_ms += float(np.mean(ms))
+        del Ac, At
+        torch.cuda.empty_cache()
+    agg = tot_bytes / (tot_ms * 1e-3) / 1e9
+    line = {
+        "metric": "GEMV achieved HBM bandwidth (fp16 matrix x vector, fp32 accumulate)",
+        "value": round(agg, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(tot_ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": "GEMV probe: fp16 row-major 2560x2560, 2560x8192, 8192x2560, 2560x32768 "
+                               "x fp16 vector, rotating copies >= 1 GiB per launch", "shapes": shapes},
+        "roofline": {"bound": "hbm", "achieved": round(agg, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(agg / PEAK_GBS, 4), "traffic": counters_traffic("gemv_probe")},
+    }
+    if not args.no_cpu_baseline:
+        M, K = cfg.shapes[1]
+        A, x = synth.make_probe(1, M, K)
+        reps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            oracle.gemv_f64(A, x)
+            reps += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(reps * roofline.gemv_bytes(M, K) / dt / 1e9, 3), "unit": "GB/s",
+                                "cores": blas_threads(), "kind": "oracle",
+                                "sample": f"{reps} float64 GEMVs of the {M}x{K} fp16 matrix (oracle gemv_f64)"}
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="2b", help="2b (default), 2b_32k, moe, tiny or gemv")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+    import torch
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    if args.config == "gemv":
+        line = bench_gemv(args)
+    else:
+        line = bench_decode(synth.get_config(args.config), args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

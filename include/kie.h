@@ -56,9 +56,12 @@ enum {
  *  the top_k experts by router probability are mixed with those
  *  probabilities (ties to the lower expert index, no renormalisation).
  * Supported (KIE_ERR_CONFIG otherwise): head_dim in {64, 128}; n_heads a
- * multiple of n_kv_heads with at most 8 query heads per KV head; d_model,
- * ffn_dim and n_heads*head_dim multiples of 256 and each either a multiple of
- * 512 or a divisor of 512; max_seq <= 65536; vocab >= 2.
+ * multiple of n_kv_heads with at most 8 query heads per KV head and at most
+ * 256 KV heads; d_model, ffn_dim and n_heads*head_dim each 256 or a multiple
+ * of 512 (MoE: d_model and ffn_dim multiples of 512, top_k <= 16, at most
+ * 1024 experts); the longest matrix-vector input (d_model, n_heads*head_dim,
+ * ffn_dim, or top_k*ffn_dim for MoE) at most 8192; 2 <= vocab <= 65536;
+ * max_seq <= 65536.
  */
 typedef struct kie_config {
     int32_t n_layers;
@@ -83,19 +86,34 @@ typedef struct kie_config {
  *  logits:    if non-NULL, [n][vocab] fp32 logits of every pass.
  *  experts:   if non-NULL (MoE only), [n][n_layers][top_k] selected expert
  *             ids of every pass, in descending router probability.
- * Debug outputs add device-to-host copies; they are for tests, not timing.
+ *  trace:     if non-NULL, [KIE_TRACE_PHASES][256][4] int64 phase timeline of
+ *             the call's first launch: for each of its first
+ *             KIE_TRACE_PHASES phases (see kie_phases_per_pass) and each
+ *             workgroup, the device's constant 100 MHz clock when the
+ *             workgroup's communication wave began the phase, had gathered
+ *             its input, saw the compute waves finish, and had published its
+ *             output (entries past the call's phases are left untouched).
+ * Debug outputs add device-to-host copies; they are for tests and profiling,
+ * not timing.
  */
+#define KIE_TRACE_PHASES 2048
 typedef struct kie_debug {
     const int32_t* force_ids;
     float* logits;
     int32_t* experts;
+    int64_t* trace;
 } kie_debug;
+
+/* Phases of one forward pass: n_layers * (6 dense | 7 MoE) + 2, in the order
+ * per layer QKV, ATTN, COMB, WO, then GU, DOWN (dense) or ROUTER, EGU,
+ * EDOWN (MoE); then LM, SAMPLE. 0 if the configuration is invalid. */
+int32_t kie_phases_per_pass(const kie_config* cfg);
 
 typedef struct kie_model kie_model;   /* opaque, owned by the library */
 
 /* Device bytes the caller must allocate for kie_load's workspace (weights in
- * the streaming layout, KV cache, activations, barrier words). 0 if the
- * configuration is invalid. Pure host computation. */
+ * the streaming layout, KV cache, the words workgroups exchange, status and
+ * debug buffers). 0 if the configuration is invalid. Pure host computation. */
 size_t kie_workspace_bytes(const kie_config* cfg);
 
 /* Number of fp16 tensors kie_load expects for this configuration. */
@@ -121,10 +139,12 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
              void* dev_workspace, size_t ws_bytes, void* hip_stream, kie_model** out);
 
 /*
- * Prefill: run one forward pass per prompt token at positions 0..n-1 (the
- * cache is reset first) and return the greedy first generated token, which
- * becomes the pending token. One kernel launch. Not part of the decode metric.
- * dbg may be NULL; dbg->logits, if set, receives [n][vocab].
+ * Prefill: run one forward pass per prompt token at positions 0..n-1 (cache
+ * entries at those positions are overwritten) and return the greedy first
+ * generated token, which becomes the pending token. The passes run in one
+ * kernel launch (launches of at most 64 passes when debug logits are
+ * requested); the LM head runs on the last pass only. Not part of the decode
+ * metric. dbg may be NULL; dbg->logits, if set, receives [n][vocab].
  */
 int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_token,
                 const kie_debug* dbg);
@@ -174,30 +194,37 @@ const char* kie_status_str(int status);
  * GEMV bandwidth probe: y[r][i] = sum_k A_r[i][k] x[k] for r < copies, where
  * A_r = A + r*M*K (fp16, row-major, device), x fp16 [K] (device), y fp32
  * [copies][M] (device), products accumulated in fp32 with v_dot2.
- * variant 0: one launch of the persistent 256-workgroup streaming GEMV the
- *            decode kernel uses (LDS-ring weight streamer + compute waves),
- *            each workgroup streaming its rows of every copy in turn;
- *            requires ceil(M/256) * K/512 <= 1024.
+ * variant 0: the persistent 256-workgroup GEMV streaming weights the way
+ *            the decode kernel does (LDS DMA into a per-wave ring of
+ *            batches kept in flight, 8 waves per workgroup, whole rows per
+ *            wave, x staged in LDS); K above 8192 runs as column blocks of
+ *            8192, one launch each, accumulated into y.
  * variant 1: a plain many-wave GEMV (4 rows per wave, all loads in flight).
- * K must be a multiple of 512, at most 65536. *ms_out (host, may be NULL)
- * receives the device time of the launch. Used to measure achieved HBM
- * bandwidth per shape (the pages' statement that batch-1 decode is a
- * bandwidth-bound matrix-vector product: paper-digest.app digest,
- * "Core Mechanics").
+ * K must be a multiple of 512, at most 65536, and copies*M*K*2 >= 4096.
+ * *ms_out (host, may be NULL) receives the device time of the launches.
+ * Used to measure achieved HBM bandwidth per shape (the pages' statement that
+ * batch-1 decode is a bandwidth-bound matrix-vector product:
+ * paper-digest.app digest, "Core Mechanics").
  */
 int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K, int32_t copies,
                    int32_t variant, void* hip_stream, float* ms_out);
 
 /*
- * Grid-barrier probe: one persistent launch that runs `rounds` grid-wide
- * barriers across all workgroups, each barrier also all-gathering an 8-byte
- * value per workgroup. scratch is device memory of at least
- * kie_barrier_probe_bytes() bytes. *us_per_barrier receives the mean time of
- * one barrier; *errors the number of rounds whose gathered values were wrong
- * (must be 0).
+ * Inter-workgroup exchange probe: one persistent launch of 256 one-wave
+ * workgroups running `rounds` exchange rounds.
+ * variant 0: every workgroup stores one value, then a fenced grid barrier
+ *            (agent-scope release, flag, poll, acquire), then reads all
+ *            256 values.
+ * variant 1: every workgroup publishes 5 flagged words (phase id + payload in
+ *            one 64-bit store) and gathers all 1280 words, waiting only until
+ *            every word carries the round's id - the residual exchange of the
+ *            decode kernel.
+ * scratch is device memory of at least kie_barrier_probe_bytes() bytes.
+ * *us_per_round receives the mean time of one round; *errors the number of
+ * values read wrong (must be 0), plus 1000000 per workgroup that gave up.
  */
 size_t kie_barrier_probe_bytes(void);
-int kie_barrier_probe(void* scratch, int32_t rounds, void* hip_stream, float* us_per_barrier,
+int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                       int32_t* errors);
 
 /* Launch-overhead probe: `launches` back-to-back launches of an empty kernel;

@@ -42,30 +42,33 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libkie.so; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link libkie.so; returns its path.
+
+    defines: extra -D flags (kernel tuning knobs such as KIE_NB=6); out and
+    build_dir place the library and objects elsewhere (for such variants)."""
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         raise RuntimeError("hipcc not found")
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    jobs = [
-        [GXX, *CXX_FLAGS, *inc, "-c", os.path.join(CSRC, "kie_host.cpp"), "-o", os.path.join(BUILD, "kie_host.o")],
-        [HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "kie_kernels.hip"), "-o",
-         os.path.join(BUILD, "kie_kernels.o")],
-        [HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "kie_api.hip"), "-o", os.path.join(BUILD, "kie_api.o")],
-    ]
-    with ThreadPoolExecutor(3) as ex:
+    units = ["kie_decode", "kie_probes", "kie_api"]
+    dflags = ["-D" + d for d in defines]
+    jobs = [[GXX, *CXX_FLAGS, *dflags, *inc, "-c", os.path.join(CSRC, "kie_host.cpp"), "-o",
+             os.path.join(build_dir, "kie_host.o")]]
+    for u in units:
+        jobs.append([HIPCC, *HIP_FLAGS, *dflags, *inc, "-c", os.path.join(CSRC, u + ".hip"), "-o",
+                     os.path.join(build_dir, u + ".o")])
+    with ThreadPoolExecutor(len(jobs)) as ex:
         outs = list(ex.map(_run, jobs))
-    tmp = LIB + ".tmp"
-    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-                      os.path.join(BUILD, "kie_host.o"), os.path.join(BUILD, "kie_kernels.o"),
-                      os.path.join(BUILD, "kie_api.o")]))
-    os.replace(tmp, LIB)
+    tmp = out + ".tmp"
+    objs = [os.path.join(build_dir, n + ".o") for n in ["kie_host", *units]]
+    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
+    os.replace(tmp, out)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

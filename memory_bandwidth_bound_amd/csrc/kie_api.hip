@@ -22,6 +22,7 @@ struct kie_model {
     hipStream_t stream;
     int pos;
     int pending;   // -1: none
+    uint32_t id_next;   // phase id of the next launch's first phase (ids never repeat)
     hipEvent_t ev0, ev1;
     float last_ms;
     std::string err;
@@ -80,6 +81,13 @@ size_t kie_workspace_bytes(const kie_config* cfg) {
     return t;
 }
 
+int32_t kie_phases_per_pass(const kie_config* cfg) {
+    if (!cfg) return 0;
+    std::string err;
+    if (validate_config(*cfg, &err) != KIE_OK) return 0;
+    return phases_per_step(dims_of(*cfg));
+}
+
 int32_t kie_tensor_count(const kie_config* cfg) {
     if (!cfg) return 0;
     return tensor_count(*cfg);
@@ -95,11 +103,6 @@ static int check_device(kie_model* m) {
     if (p.multiProcessorCount < kGrid)
         return fail(m, KIE_ERR_DEVICE, "device has fewer compute units than the 256-workgroup persistent grid");
     if (!p.cooperativeLaunch) return fail(m, KIE_ERR_DEVICE, "cooperative launch not supported");
-    static bool attr_done = false;
-    if (!attr_done) {
-        HIP_TRY(m, decode_kernel_setup());
-        attr_done = true;
-    }
     return KIE_OK;
 }
 
@@ -109,14 +112,16 @@ static int upload(kie_model* m, size_t off, const void* src, size_t bytes) {
     return KIE_OK;
 }
 
+// Zero the KV cache (optional) and the exchange words; phase ids restart at 1.
 static int clear_state(kie_model* m, bool kv) {
     const Layout& L = m->lay;
     if (kv) {
         HIP_TRY(m, hipMemsetAsync(m->ws + L.off_k, 0, L.kv_bytes, m->stream));
         HIP_TRY(m, hipMemsetAsync(m->ws + L.off_v, 0, L.kv_bytes, m->stream));
     }
-    HIP_TRY(m, hipMemsetAsync(m->ws + L.off_x, 0, L.off_dbg_logits - L.off_x, m->stream));
+    HIP_TRY(m, hipMemsetAsync(m->ws + L.off_ex_x, 0, L.ex_bytes, m->stream));
     HIP_TRY(m, hipStreamSynchronize(m->stream));
+    m->id_next = 1;
     return KIE_OK;
 }
 
@@ -138,6 +143,7 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     m->stream = (hipStream_t)hip_stream;
     m->pos = 0;
     m->pending = -1;
+    m->id_next = 1;
     m->last_ms = 0.f;
     m->ev0 = m->ev1 = nullptr;
     if (ws_bytes < m->lay.total) {
@@ -187,6 +193,8 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
         plan[kGrid + 1 + w] = L.lm_off[w];
     }
     if ((rc = upload(m, L.off_plan, plan.data(), plan.size() * 4)) != KIE_OK) return bail(rc);
+    static_assert(kIdleBytes <= 16384, "idle region");
+    if (hipMemsetAsync(m->ws + L.off_idle, 0, 16384, m->stream) != hipSuccess) return bail(KIE_ERR_HIP);
     if ((rc = clear_state(m, true)) != KIE_OK) return bail(rc);
     hipError_t e = hipEventCreate(&m->ev0);
     if (e == hipSuccess) e = hipEventCreate(&m->ev1);
@@ -202,7 +210,7 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
 // of pass i where force[i] >= 0. One launch unless debug rows are requested,
 // then launches of at most kDebugRows passes.
 static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_ids, float* dbg_logits,
-                      int32_t* dbg_experts, bool skip_lm) {
+                      int32_t* dbg_experts, int64_t* trace, bool skip_lm) {
     const Layout& L = m->lay;
     const Dims& D = L.D;
     const bool debug = dbg_logits || dbg_experts;
@@ -210,9 +218,12 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
     int tok = m->pending;
     for (int s0 = 0; s0 < n; s0 += chunk) {
         int nc = (n - s0 < chunk) ? n - s0 : chunk;
-        // reset the barrier words, status, attention counters for this launch
-        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_attn_cnt, 0, (size_t)D.Hkv * 64, m->stream));
-        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_bar, 0, (size_t)kGrid * 4, m->stream));
+        const uint32_t nphase = (uint32_t)nc * (uint32_t)phases_per_step(D);
+        if (m->id_next > 0xffffffffu - nphase) {
+            // phase ids would wrap: forget every published word and restart
+            int rc = clear_state(m, false);
+            if (rc != KIE_OK) return rc;
+        }
         HIP_TRY(m, hipMemsetAsync(m->ws + L.off_status, 0, 256, m->stream));
         if (force)
             HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_force, force + s0, (size_t)nc * 4, hipMemcpyHostToDevice,
@@ -222,8 +233,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.D = D;
         a.eps = m->cfg.rms_eps;
         a.items_per_head = L.attn_items_per_head;
-        a.spin_lds = 1u << 24;
-        a.spin_grid = 1u << 21;
+        a.spin = 1u << 22;
         a.layers = m->ws + L.off_layers;
         a.layer_bytes = L.layer_bytes;
         a.lm = m->ws + L.off_lm;
@@ -233,28 +243,30 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.rope = (const float*)(m->ws + L.off_rope);
         a.kc = (uint16_t*)(m->ws + L.off_k);
         a.vc = (uint16_t*)(m->ws + L.off_v);
-        a.x = (float*)(m->ws + L.off_x);
-        a.q = (float*)(m->ws + L.off_q);
-        a.o16 = (uint16_t*)(m->ws + L.off_o);
-        a.h16 = (uint16_t*)(m->ws + L.off_h);
-        a.router = (float*)(m->ws + L.off_router);
-        a.attn_part = (float*)(m->ws + L.off_attn_part);
-        a.attn_cnt = (uint32_t*)(m->ws + L.off_attn_cnt);
-        a.argmax = (float*)(m->ws + L.off_argmax);
-        a.bar = (uint32_t*)(m->ws + L.off_bar);
+        a.ex.x = (uint64_t*)(m->ws + L.off_ex_x);
+        a.ex.qkv = (uint64_t*)(m->ws + L.off_ex_qkv);
+        a.ex.part = (uint64_t*)(m->ws + L.off_ex_part);
+        a.ex.o = (uint64_t*)(m->ws + L.off_ex_o);
+        a.ex.h = (uint64_t*)(m->ws + L.off_ex_h);
+        a.ex.r = (uint64_t*)(m->ws + L.off_ex_r);
+        a.ex.am = (uint64_t*)(m->ws + L.off_ex_am);
         a.status = (uint32_t*)(m->ws + L.off_status);
         a.out_ids = (int32_t*)(m->ws + L.off_out);
         a.force_ids = (const int32_t*)(m->ws + L.off_force);
         a.dbg_logits = (float*)(m->ws + L.off_dbg_logits);
         a.dbg_experts = (int32_t*)(m->ws + L.off_dbg_experts);
         a.plan = (const int32_t*)(m->ws + L.off_plan);
+        a.idle = m->ws + L.off_idle;
+        a.trace = (int64_t*)(m->ws + L.off_trace);
         a.pos0 = m->pos + s0;
         a.pending = tok;
         a.n_steps = nc;
         a.flags = (force ? F_FORCE : 0) | (dbg_logits ? F_DBG_LOGITS : 0) | (dbg_experts ? F_DBG_EXPERTS : 0) |
-                  ((skip_lm && !debug) ? F_SKIP_LM : 0);
-        a.epoch0 = 0;
+                  ((skip_lm && !debug) ? F_SKIP_LM : 0) | ((trace && s0 == 0) ? F_TRACE : 0);
+        a.id0 = m->id_next;
+        m->id_next += nphase;
         static_assert(sizeof(DecodeArgs) <= 4096, "argument block");
+        static_assert(KIE_TRACE_PHASES == kTracePhases, "trace length");
         HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
         HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
         HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, kGrid, m->stream));
@@ -265,7 +277,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         HIP_TRY(m, hipMemcpy(&status, m->ws + L.off_status, 4, hipMemcpyDeviceToHost));
         if (status != 0) {
             m->pending = -1;
-            return fail(m, KIE_ERR_TIMEOUT, "a grid barrier or ring wait hit its spin limit");
+            return fail(m, KIE_ERR_TIMEOUT, "a device-side wait for another workgroup hit its spin limit");
         }
         HIP_TRY(m, hipMemcpy(out_ids + s0, m->ws + L.off_out, (size_t)nc * 4, hipMemcpyDeviceToHost));
         if (dbg_logits)
@@ -274,6 +286,10 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         if (dbg_experts)
             HIP_TRY(m, hipMemcpy(dbg_experts + (size_t)s0 * D.L * D.topk, m->ws + L.off_dbg_experts,
                                  (size_t)nc * D.L * D.topk * 4, hipMemcpyDeviceToHost));
+        if (trace && s0 == 0) {
+            size_t np = (size_t)nphase < (size_t)kTracePhases ? (size_t)nphase : (size_t)kTracePhases;
+            HIP_TRY(m, hipMemcpy(trace, m->ws + L.off_trace, np * kGrid * 4 * 8, hipMemcpyDeviceToHost));
+        }
         int last = nc - 1;
         tok = (force && force[s0 + last] >= 0) ? force[s0 + last] : out_ids[s0 + last];
     }
@@ -296,7 +312,7 @@ int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_t
     m->pos = 0;
     m->pending = tokens[0];
     int rc = run_passes(m, n, force.data(), ids.data(), dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr,
-                        true);
+                        dbg ? dbg->trace : nullptr, true);
     if (rc != KIE_OK) return rc;
     *first_token = ids[n - 1];
     return KIE_OK;
@@ -312,7 +328,8 @@ int kie_decode(kie_model* m, int32_t n, int32_t* out_ids, const kie_debug* dbg) 
     if (force)
         for (int i = 0; i < n; ++i)
             if (force[i] >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "forced token out of range");
-    return run_passes(m, n, force, out_ids, dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr, false);
+    return run_passes(m, n, force, out_ids, dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr,
+                      dbg ? dbg->trace : nullptr, false);
 }
 
 int kie_set_kv(kie_model* m, const void* k, const void* v, int32_t n_pos, int32_t pending) {
@@ -387,18 +404,10 @@ int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K,
     if (!A || !x || !y) return fail(nullptr, KIE_ERR_ARG, "null pointer");
     if (M < 1 || copies < 1 || K < 512 || K % 512 || K > 65536)
         return fail(nullptr, KIE_ERR_ARG, "need M >= 1, copies >= 1, K a multiple of 512 up to 65536");
-    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (ring) or 1 (direct)");
-    if (variant == 0 && (long)ceil_div(M, kGrid) * (K / 512) > kPartFloats)
-        return fail(nullptr, KIE_ERR_ARG, "rows per workgroup x K/512 must be at most 1024");
+    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (stream) or 1 (direct)");
+    if ((long)M * copies * K < kIdleBytes / 2)
+        return fail(nullptr, KIE_ERR_ARG, "the matrices must hold at least one batch (kNB KiB)");
     hipStream_t s = (hipStream_t)hip_stream;
-    if (variant == 0) {
-        static bool attr_done = false;
-        if (!attr_done) {
-            hipError_t e = decode_kernel_setup();
-            if (e != hipSuccess) return hip_fail(nullptr, e, "decode_kernel_setup");
-            attr_done = true;
-        }
-    }
     hipEvent_t e0, e1;
     HIP_TRY(nullptr, hipEventCreate(&e0));
     HIP_TRY(nullptr, hipEventCreate(&e1));
@@ -406,13 +415,28 @@ int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K,
     a.A = (const uint8_t*)A;
     a.x = (const uint16_t*)x;
     a.y = y;
+    a.idle = (const uint8_t*)A;   // any readable 4 KiB: the loads it serves are never used
+    a.lda = K;
     a.M = M;
     a.K = K;
     a.copies = copies;
-    a.spin_lds = 1u << 24;
+    a.accumulate = 0;
     HIP_TRY(nullptr, hipEventRecord(e0, s));
-    hipError_t le = variant == 0 ? launch_gemv_ring(a, kGrid, s) : launch_gemv_direct(a, s);
-    if (le != hipSuccess) return hip_fail(nullptr, le, "gemv probe launch");
+    if (variant == 0) {
+        // the streaming kernel keeps x in LDS: column blocks of at most kMaxInput
+        for (int k0 = 0; k0 < K; k0 += kMaxInput) {
+            GemvArgs b = a;
+            b.A = a.A + (size_t)k0 * 2;
+            b.x = a.x + k0;
+            b.K = (K - k0 < kMaxInput) ? K - k0 : kMaxInput;
+            b.accumulate = k0 > 0;
+            hipError_t le = launch_gemv_stream(b, kGrid, s);
+            if (le != hipSuccess) return hip_fail(nullptr, le, "gemv probe launch");
+        }
+    } else {
+        hipError_t le = launch_gemv_direct(a, s);
+        if (le != hipSuccess) return hip_fail(nullptr, le, "gemv probe launch");
+    }
     HIP_TRY(nullptr, hipEventRecord(e1, s));
     HIP_TRY(nullptr, hipEventSynchronize(e1));
     float ms = 0.f;
@@ -423,22 +447,23 @@ int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K,
     return KIE_OK;
 }
 
-size_t kie_barrier_probe_bytes(void) { return 16384; }
+size_t kie_barrier_probe_bytes(void) { return 65536; }
 
-int kie_barrier_probe(void* scratch, int32_t rounds, void* hip_stream, float* us_per_barrier, int32_t* errors) {
-    if (!scratch || !us_per_barrier || !errors || rounds < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
+                      int32_t* errors) {
+    if (!scratch || !us_per_round || !errors || rounds < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (fenced) or 1 (flagged)");
     hipStream_t s = (hipStream_t)hip_stream;
     uint8_t* b = (uint8_t*)scratch;
-    uint32_t* bar = (uint32_t*)b;                 // 1 KiB
-    uint32_t* status = (uint32_t*)(b + 4096);
-    int32_t* err = (int32_t*)(b + 4096 + 256);
-    float* vals = (float*)(b + 8192);             // 2 x 256 x 2 floats = 4 KiB
+    uint64_t* words = (uint64_t*)b;               // 2 x 5 x 256 words = 20 KiB
+    uint32_t* status = (uint32_t*)(b + 32768);
+    int32_t* err = (int32_t*)(b + 32768 + 256);
     HIP_TRY(nullptr, hipMemsetAsync(scratch, 0, kie_barrier_probe_bytes(), s));
     hipEvent_t e0, e1;
     HIP_TRY(nullptr, hipEventCreate(&e0));
     HIP_TRY(nullptr, hipEventCreate(&e1));
     HIP_TRY(nullptr, hipEventRecord(e0, s));
-    hipError_t le = launch_barrier_probe(bar, status, vals, err, rounds, kGrid, s);
+    hipError_t le = launch_barrier_probe(variant, words, status, err, rounds, kGrid, s);
     if (le != hipSuccess) return hip_fail(nullptr, le, "barrier probe launch");
     HIP_TRY(nullptr, hipEventRecord(e1, s));
     HIP_TRY(nullptr, hipEventSynchronize(e1));
@@ -447,7 +472,7 @@ int kie_barrier_probe(void* scratch, int32_t rounds, void* hip_stream, float* us
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     HIP_TRY(nullptr, hipMemcpy(errors, err, 4, hipMemcpyDeviceToHost));
-    *us_per_barrier = ms * 1000.f / (float)rounds;
+    *us_per_round = ms * 1000.f / (float)rounds;
     return KIE_OK;
 }
 

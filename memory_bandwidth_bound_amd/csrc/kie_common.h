@@ -23,12 +23,15 @@
 namespace kie {
 
 constexpr int kGrid = 256;                 // persistent workgroups: one per MI355X compute unit
-constexpr int kUnitBytes = 1024;           // one global_load_lds_dwordx4 of a wave
+constexpr int kUnitBytes = 1024;           // one 16-byte-per-lane load of a wave
 constexpr int kUnitHalves = 512;           // fp16 elements per unit
 constexpr int kMaxGroup = 8;               // query heads per KV head supported
-constexpr int kAttnChunkMax = 1024;        // positions per attention work item
-constexpr int kAttnChunkMin = 32;
+constexpr int kAttnChunkMin = 32;          // fewest positions per attention work item
 constexpr int kMaxSeq = 65536;
+constexpr int kMaxRowsWg = 256;            // rows of one phase per workgroup
+constexpr int kMaxOwnRows = 32;            // residual rows per workgroup
+constexpr int kMaxInput = 8192;            // longest GEMV input (fp16 elements)
+constexpr int kTracePhases = 2048;         // phases covered by the phase timeline
 
 // Phase kinds of the per-layer pipeline.
 enum Phase : int {
@@ -78,14 +81,18 @@ struct PhaseShape {
 KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
     PhaseShape s;
     switch (ph) {
-    case PH_QKV: s.M = (D.H + 2 * D.Hkv) * D.hd; s.K = D.d; s.gran = 2; break;
-    case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = 1; break;
-    case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 2; break;
-    case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = 1; break;
+    // Granularities: QKV rows come in groups of 4 (two rotary pairs, so the
+    // new key and value rows are written as whole 32-bit pairs), gate/up rows
+    // in groups of 4 (two (gate, up) pairs -> one fp16 pair of h), residual
+    // rows (Wo, down) in pairs (one fp16 pair of x per exchanged word).
+    case PH_QKV: s.M = (D.H + 2 * D.Hkv) * D.hd; s.K = D.d; s.gran = 4; break;
+    case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = 2; break;
+    case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 4; break;
+    case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;
     case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = 1; break;
     case PH_LM: s.M = D.V; s.K = D.d; s.gran = 1; break;
-    case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 2; break;
-    case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 1; break;   // K per selected expert
+    case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 4; break;
+    case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;   // K per selected expert
     default: s.M = 0; s.K = 0; s.gran = 1; break;
     }
     return s;

@@ -1,0 +1,1138 @@
+// kie_decode.hip - the persistent batch-1 decode kernel for gfx950.
+//
+// One launch runs n whole forward passes: one resident grid for the whole
+// decode loop, with weight prefetch, inter-CU synchronisation and on-device
+// greedy sampling inside it (the monokernel design of the news.creeta.com
+// article, "Inside the monokernel"). The grid is one 512-thread workgroup per
+// compute unit (256 on MI355X); each workgroup owns a fixed share of every
+// weight matrix (rows, laid out contiguously by the host) and of the residual.
+//
+// Waves of a workgroup:
+//   wave 0 (communication): gathers each phase's input from the other
+//     workgroups through flagged words, normalises it into LDS, runs the
+//     phase epilogue (RoPE, KV-cache append, SwiGLU, residual add, argmax) and
+//     publishes the outputs as flagged words;
+//   waves 1..7 (compute): stream this workgroup's weights from HBM into
+//     registers with non-temporal 16-byte loads, two 12-unit batches in
+//     flight per wave, and take v_dot2 products against the LDS input; they
+//     also run the attention of the workgroups that hold an attention item.
+//     A batch is refilled as soon as it is consumed, with the next units in
+//     phase order, so weight streaming runs on across phase boundaries while
+//     the communication wave waits for the next input.
+//
+// Phase sequence of one pass (each phase has a unique 32-bit id that tags
+// every word it publishes):
+//   per layer:  QKV | ATTN | COMB | WO | GU | DOWN               (dense FFN)
+//               QKV | ATTN | COMB | WO | ROUTER | EGU | EDOWN     (top-k MoE)
+//   then        LM | SAMPLE
+// There is no grid-wide barrier: a phase waits only for the words it reads.
+// A workgroup reads a phase's input only when it has work in that phase; then
+// every overwrite of a buffer it reads depends, through the words the
+// overwriting workgroup had to read first, on this workgroup having finished
+// its read, so one buffer per exchanged vector suffices.
+#include <hip/hip_runtime.h>
+
+#include "kie_common.h"
+#include "kie_device.h"
+#include "kie_kernels.h"
+
+namespace kie {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum Kind : int {
+    K_QKV = 0, K_ATTN = 1, K_COMB = 2, K_WO = 3, K_GU = 4, K_DOWN = 5,
+    K_ROUTER = 6, K_EGU = 7, K_EDOWN = 8, K_LM = 9, K_SAMPLE = 10, K_COUNT = 11
+};
+
+__device__ __forceinline__ int ppl_of(const Dims& D) { return D.E ? 7 : 6; }
+__device__ __forceinline__ int pps_of(const Dims& D) { return D.L * ppl_of(D) + 2; }
+
+__device__ __forceinline__ bool is_gemv(int kind) {
+    return kind == K_QKV || kind == K_WO || kind == K_GU || kind == K_DOWN || kind == K_ROUTER ||
+           kind == K_EGU || kind == K_EDOWN || kind == K_LM;
+}
+
+// Walks the phase sequence: q = global phase index within the launch; layer
+// == D.L for the per-pass LM / SAMPLE phases (k = 0 / 1).
+struct PIter {
+    int q, step, layer, k;
+};
+
+__device__ __forceinline__ int kind_of(const Dims& D, const PIter& it) {
+    if (it.layer == D.L) return it.k == 0 ? K_LM : K_SAMPLE;
+    if (it.k < 4) return it.k;
+    return D.E ? K_ROUTER + it.k - 4 : K_GU + it.k - 4;
+}
+
+__device__ __forceinline__ void advance(const Dims& D, PIter& it) {
+    ++it.q;
+    ++it.k;
+    if (it.layer < D.L) {
+        if (it.k == ppl_of(D)) {
+            it.k = 0;
+            ++it.layer;
+        }
+    } else if (it.k == 2) {
+        it.k = 0;
+        it.layer = 0;
+        ++it.step;
+    }
+}
+
+// Attention of c positions is cut into nper chunks of CH positions per KV head.
+__device__ __forceinline__ int attn_split(int c, int items, int* CH) {
+    int nper = ceil_div(c, kAttnChunkMin);
+    if (nper > items) nper = items;
+    *CH = ceil_div(c, nper);
+    return ceil_div(c, *CH);
+}
+
+__device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
+    return (a.flags & F_SKIP_LM) && step != a.n_steps - 1;
+}
+
+// Do this workgroup's waves meet at the two barriers of a phase? Every wave
+// evaluates the same test, so the barrier sequences match.
+__device__ __forceinline__ bool phase_bars(const DecodeArgs& a, int kind, int step, int wg) {
+    if (kind == K_ATTN) {
+        int CH;
+        return wg < a.D.Hkv * attn_split(a.pos0 + step + 1, a.items_per_head, &CH);
+    }
+    if (kind == K_LM) return !lm_skipped(a, step);
+    return is_gemv(kind);
+}
+
+// This workgroup's share of each phase.
+struct WgPlan {
+    int q0, qn, wo0, won, gu0, gun, r0, rn, egu0, egun, lm0, lmn;
+    int nq, nwo, ngu, nd, nr, negu, ned, nlm;
+};
+
+__device__ __forceinline__ void make_plan(const Dims& D, int wg, WgPlan& P) {
+    const int G = kGrid;
+    RowSplit r;
+    PhaseShape s = phase_shape(D, PH_QKV);
+    r = split_rows(s.M, s.gran, G, wg);
+    P.q0 = r.row0; P.qn = r.nrows;
+    s = phase_shape(D, PH_WO);
+    r = split_rows(s.M, s.gran, G, wg);   // residual ownership (Wo, down)
+    P.wo0 = r.row0; P.won = r.nrows;
+    r = split_rows(D.V, phase_shape(D, PH_LM).gran, G, wg);
+    P.lm0 = r.row0; P.lmn = r.nrows;
+    P.nq = phase_units(D, PH_QKV, G, wg);
+    P.nwo = phase_units(D, PH_WO, G, wg);
+    P.nlm = phase_units(D, PH_LM, G, wg);
+    P.gu0 = P.gun = P.r0 = P.rn = P.egu0 = P.egun = 0;
+    P.ngu = P.nd = P.nr = P.negu = P.ned = 0;
+    if (D.E) {
+        r = split_rows(D.E, phase_shape(D, PH_ROUTER).gran, G, wg);
+        P.r0 = r.row0; P.rn = r.nrows;
+        s = phase_shape(D, PH_EGU);
+        r = split_rows(s.M, s.gran, G, wg);
+        P.egu0 = r.row0; P.egun = r.nrows;
+        P.nr = phase_units(D, PH_ROUTER, G, wg);
+        P.negu = phase_units(D, PH_EGU, G, wg);
+        P.ned = phase_units(D, PH_EDOWN, G, wg);
+    } else {
+        s = phase_shape(D, PH_GU);
+        r = split_rows(s.M, s.gran, G, wg);
+        P.gu0 = r.row0; P.gun = r.nrows;
+        P.ngu = phase_units(D, PH_GU, G, wg);
+        P.nd = phase_units(D, PH_DOWN, G, wg);
+    }
+}
+
+// Per-phase geometry of this workgroup, kept in LDS for the compute waves.
+struct Geo {
+    int n;      // units
+    int nrows;  // rows
+    int K;      // row length per segment (fp16)
+    int nseg;   // segments per row (MoE down: top_k)
+    int off;    // units from the start of the layer block (LM: of the LM block)
+    int row0;   // first row (MoE gate/up: virtual row)
+};
+
+// LDS shared by the waves of one workgroup.
+struct Smem {
+    // per compute wave: kNS batches of kNB weight units, written by LDS DMA
+    alignas(16) uint8_t ring[kCompute * kNS * kBatchBytes];
+    union {
+        struct {                                // GEMV phases
+            alignas(16) uint16_t xin[kMaxIn];   // fp16 input of the current phase
+            float part[kMaxRowsWg * kCompute];  // per (row, compute wave) partial dot products
+        };
+        float att_o[kCompute * kMaxGroup * 128];   // attention: per compute wave, unnormalised o
+    };
+    float att_q[kMaxGroup * 128];               // queries of the attention group, pre-scaled (also scratch)
+    alignas(8) uint16_t att_k[128];             // the new position's key and value
+    alignas(8) uint16_t att_v[128];
+    float att_ml[kCompute * kMaxGroup * 2];     // per compute wave: (max, sum)
+    float own_x[kMaxOwnRows];                   // this workgroup's residual rows (fp32)
+    uint32_t sel[16];                           // MoE: experts selected for the current layer
+    float pi[16];                               //      and their router probabilities
+    Geo geo[K_COUNT];
+    uint32_t abort;                             // set when the communication wave gave up
+};
+
+__device__ __forceinline__ void set_geo(KIE_LDS Geo* g, int n, int nrows, int K, int nseg, int off, int row0) {
+    g->n = n;
+    g->nrows = nrows;
+    g->K = K;
+    g->nseg = nseg;
+    g->off = off;
+    g->row0 = row0;
+}
+
+__device__ __forceinline__ void write_geo(const DecodeArgs& a, const WgPlan& W, int wg, KIE_LDS Geo* geo) {
+    const Dims& D = a.D;
+    for (int k = 0; k < K_COUNT; ++k) set_geo(geo + k, 0, 0, kUnitHalves, 1, 0, 0);
+    const int piece = a.plan[wg];
+    set_geo(geo + K_QKV, W.nq, W.qn, D.d, 1, piece, W.q0);
+    set_geo(geo + K_WO, W.nwo, W.won, D.H * D.hd, 1, piece + W.nq, W.wo0);
+    if (D.E) {
+        set_geo(geo + K_ROUTER, W.nr, W.rn, D.d, 1, piece + W.nq + W.nwo, W.r0);
+        set_geo(geo + K_EGU, W.negu, W.egun, D.d, 1, 0, W.egu0);
+        set_geo(geo + K_EDOWN, W.ned, W.won, D.F, D.topk, 0, W.wo0);
+    } else {
+        set_geo(geo + K_GU, W.ngu, W.gun, D.d, 1, piece + W.nq + W.nwo, W.gu0);
+        set_geo(geo + K_DOWN, W.nd, W.won, D.F, 1, piece + W.nq + W.nwo + W.ngu, W.wo0);
+    }
+    set_geo(geo + K_LM, W.nlm, W.lmn, D.d, 1, a.plan[kGrid + 1 + wg], W.lm0);
+}
+
+// ------------------------------------------------------------------------
+// Communication wave.
+// ------------------------------------------------------------------------
+template <int HD>
+struct Comm {
+    const DecodeArgs& a;
+    KIE_LDS Smem* S;
+    WgPlan W;
+    int wg, lane, tok;
+    bool dead;
+
+    __device__ __forceinline__ Comm(const DecodeArgs& args, KIE_LDS Smem* s, const WgPlan& plan)
+        : a(args), S(s), W(plan) {
+        wg = blockIdx.x;
+        lane = lane_id();
+        tok = a.pending;
+        dead = false;
+    }
+
+    __device__ __forceinline__ uint32_t id_of(int q) { return a.id0 + (uint32_t)q; }
+
+    // why: 1 = this wave's wait timed out, 2 = another workgroup reported one
+    __device__ __forceinline__ void fail(int why) {
+        if (!dead && lane == 0) {
+            if (why == 1) dev_store32(a.status, (uint32_t)kStatusTimeout);
+            S->abort = 1u;
+        }
+        dead = true;
+    }
+
+    template <class F>
+    __device__ __forceinline__ bool gather(const uint64_t* src, int n, uint32_t id, F f) {
+        if (dead) return false;
+        const int r = fw_gather(src, n, id, a.spin, a.status, f);
+        if (r) fail(r);
+        return r == 0;
+    }
+
+    // xin = fp16(v * rsqrt(mean(v^2) + eps)) for the d-vector v, given as
+    // flagged fp16 pairs or (first layer) as the token's embedding row.
+    __device__ __forceinline__ void input_norm(const uint64_t* xw, uint32_t id, const uint16_t* emb_row) {
+        const int d = a.D.d;
+        KIE_LDS uint32_t* xi = (KIE_LDS uint32_t*)S->xin;
+        float ss = 0.f;
+        if (emb_row) {
+            const KIE_GLOBAL uint32_t* e = (const KIE_GLOBAL uint32_t*)gptr(emb_row);
+            for (int i = lane; i < d / 2; i += 64) {
+                const uint32_t v = e[i];
+                const float x0 = h2f_bits((uint16_t)v), x1 = h2f_bits((uint16_t)(v >> 16));
+                ss += x0 * x0 + x1 * x1;
+                xi[i] = v;
+            }
+        } else {
+            const bool ok = gather(xw, d / 2, id, [&](int i, uint32_t v) {
+                const float x0 = h2f_bits((uint16_t)v), x1 = h2f_bits((uint16_t)(v >> 16));
+                ss += x0 * x0 + x1 * x1;
+                xi[i] = v;
+            });
+            if (!ok) return;
+        }
+        ss = wave_sum(ss);
+        const float s = 1.0f / sqrtf(ss / (float)d + a.eps);
+        for (int i = lane; i < d / 2; i += 64) {
+            const uint32_t v = xi[i];
+            xi[i] = pack_h2(h2f_bits((uint16_t)v) * s, h2f_bits((uint16_t)(v >> 16)) * s);
+        }
+    }
+
+    __device__ __forceinline__ void input_pairs(const uint64_t* src, int npairs, uint32_t id) {
+        KIE_LDS uint32_t* xi = (KIE_LDS uint32_t*)S->xin;
+        gather(src, npairs, id, [&](int i, uint32_t v) { xi[i] = v; });
+    }
+
+    __device__ __forceinline__ void zero_part(int nrows) {
+        for (int i = lane; i < nrows * kCompute; i += 64) S->part[i] = 0.f;
+    }
+    __device__ __forceinline__ float rowsum(int r) {
+        const KIE_LDS float* p = S->part + r * kCompute;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCompute; ++w) s += p[w];
+        return s;
+    }
+
+    // Add the projection to the owned residual rows and publish them.
+    __device__ __forceinline__ void residual_add_publish(uint32_t id) {
+        for (int j = 2 * lane; j < W.won; j += 128) {
+            const float x0 = S->own_x[j] + rowsum(j);
+            const float x1 = S->own_x[j + 1] + rowsum(j + 1);
+            S->own_x[j] = x0;
+            S->own_x[j + 1] = x1;
+            fw_store(a.ex.x + (W.wo0 + j) / 2, pack_h2(x0, x1), id);
+        }
+    }
+
+    // Softmax over the router logits, then the top k (ties to the lower
+    // expert index) with their probabilities, into LDS.
+    __device__ __forceinline__ void route(int q, const PIter& it) {
+        const Dims& D = a.D;
+        const int E = D.E;
+        KIE_LDS float* lg = S->att_q;   // scratch (E <= 1024): no attention is running
+        if (!gather(a.ex.r, E, id_of(q - 1), [&](int i, uint32_t v) { lg[i] = __builtin_bit_cast(float, v); }))
+            return;
+        float mx = -3.0e38f;
+        for (int e = lane; e < E; e += 64) mx = fmaxf(mx, lg[e]);
+        mx = wave_max(mx);
+        float sum = 0.f;
+        for (int e = lane; e < E; e += 64) sum += __expf(lg[e] - mx);
+        sum = wave_sum(sum);
+        float pv = 3.0e38f;
+        int pix = -1;
+        for (int k = 0; k < D.topk; ++k) {
+            float bv = -3.0e38f;
+            int bi = 0x7fffffff;
+            for (int e = lane; e < E; e += 64) {
+                const float v = lg[e];
+                const bool below = (v < pv) || (v == pv && e > pix);
+                if (below && (v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
+            }
+            wave_argmax(bv, bi);
+            if (bi >= E) bi = E - 1;   // only with NaN logits: keep the expert loads in bounds
+            pv = bv;
+            pix = bi;
+            if (lane == 0) {
+                S->sel[k] = (uint32_t)bi;
+                S->pi[k] = __expf(bv - mx) / sum;
+                if ((a.flags & F_DBG_EXPERTS) && wg == 0)
+                    gptr(a.dbg_experts)[((size_t)(it.step % 64) * D.L + it.layer) * D.topk + k] = bi;
+            }
+        }
+    }
+
+    // ---- before the compute waves run: gather and prepare the input -------
+    __device__ __forceinline__ void pre(int kind, const PIter& it) {
+        const Dims& D = a.D;
+        if (dead) return;
+        const int q = it.q;
+        switch (kind) {
+        case K_QKV:
+            zero_part(W.qn);
+            if (it.layer == 0) {
+                const uint16_t* e = a.emb + (size_t)tok * D.d;
+                for (int j = lane; j < W.won; j += 64) S->own_x[j] = h2f_bits(gptr(e)[W.wo0 + j]);
+                if (W.nq) input_norm(nullptr, 0, e);
+            } else if (W.nq) {
+                input_norm(a.ex.x, id_of(q - 1), nullptr);   // the previous layer's last phase
+            }
+            break;
+        case K_ATTN: {
+            const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = wg % D.Hkv;
+            const float qs = kLog2e / sqrtf((float)HD);
+            gather(a.ex.qkv + (size_t)g * GW, GW, id_of(q - 1), [&](int i, uint32_t v) {
+                if (i < Gq * HD) {
+                    S->att_q[i] = __builtin_bit_cast(float, v) * qs;
+                } else if (i < Gq * HD + HD / 2) {
+                    const int k = i - Gq * HD;
+                    S->att_k[k] = (uint16_t)v;
+                    S->att_k[k + HD / 2] = (uint16_t)(v >> 16);
+                } else {
+                    const int k = i - Gq * HD - HD / 2;
+                    S->att_v[2 * k] = (uint16_t)v;
+                    S->att_v[2 * k + 1] = (uint16_t)(v >> 16);
+                }
+            });
+            break;
+        }
+        case K_WO:
+            zero_part(W.won);
+            if (W.nwo) input_pairs(a.ex.o, D.H * HD / 2, id_of(q - 1));
+            break;
+        case K_GU:
+            zero_part(W.gun);
+            if (W.ngu) input_norm(a.ex.x, id_of(q - 1), nullptr);
+            break;
+        case K_DOWN:
+            zero_part(W.won);
+            if (W.nd) input_pairs(a.ex.h, D.F / 2, id_of(q - 1));
+            break;
+        case K_ROUTER:
+            zero_part(W.rn);
+            if (W.nr || W.negu || W.ned) input_norm(a.ex.x, id_of(q - 1), nullptr);
+            break;
+        case K_EGU:
+            zero_part(W.egun);
+            if (W.negu || W.ned) route(q, it);   // xin still holds the router's normalised input
+            break;
+        case K_EDOWN:
+            zero_part(W.won);
+            if (W.ned) input_pairs(a.ex.h, D.topk * D.F / 2, id_of(q - 1));
+            break;
+        case K_LM:
+            zero_part(W.lmn);
+            if (W.nlm) input_norm(a.ex.x, id_of(q - 1), nullptr);
+            break;
+        default: break;
+        }
+    }
+
+    // ---- after the compute waves: epilogue and publication ----------------
+    __device__ __forceinline__ void post(int kind, const PIter& it, int pos) {
+        const Dims& D = a.D;
+        if (dead) return;
+        const uint32_t id = id_of(it.q);
+        const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD;
+        switch (kind) {
+        case K_QKV: {
+            const int qd = D.H * HD, kd = D.Hkv * HD;
+            const KIE_GLOBAL float* rope = gptr(a.rope) + (size_t)pos * HD;   // [hd/2][cos, sin]
+            // one lane per group of 4 rows: two rotary pairs, or 4 values
+            for (int j = lane; j < W.qn / 4; j += 64) {
+                const int vr = W.q0 + 4 * j;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = rowsum(4 * j + e);
+                if (vr < qd + kd) {
+                    // rows (4j, 4j+1) = elements (i, i+hd/2), rows (4j+2, 4j+3) = (i+1, i+1+hd/2)
+                    const int i = (vr % HD) >> 1;
+                    float r[4];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float c = rope[2 * (i + e)], s = rope[2 * (i + e) + 1];
+                        const float x0 = y[2 * e], x1 = y[2 * e + 1];
+                        r[2 * e] = x0 * c - x1 * s;
+                        r[2 * e + 1] = x1 * c + x0 * s;
+                    }
+                    if (vr < qd) {
+                        const int head = vr / HD;
+                        uint64_t* b = a.ex.qkv + (size_t)(head / Gq) * GW + (head % Gq) * HD;
+                        fw_store(b + i, __builtin_bit_cast(uint32_t, r[0]), id);
+                        fw_store(b + i + HD / 2, __builtin_bit_cast(uint32_t, r[1]), id);
+                        fw_store(b + i + 1, __builtin_bit_cast(uint32_t, r[2]), id);
+                        fw_store(b + i + 1 + HD / 2, __builtin_bit_cast(uint32_t, r[3]), id);
+                    } else {
+                        const int g = (vr - qd) / HD;
+                        uint64_t* b = a.ex.qkv + (size_t)g * GW + Gq * HD;
+                        fw_store(b + i, pack_h2(r[0], r[1]), id);
+                        fw_store(b + i + 1, pack_h2(r[2], r[3]), id);
+                        uint16_t* kp = a.kc + (((size_t)it.layer * D.Hkv + g) * D.max_seq + pos) * HD;
+                        dev_store32(kp + i, pack_h2(r[0], r[2]));
+                        dev_store32(kp + i + HD / 2, pack_h2(r[1], r[3]));
+                    }
+                } else {
+                    const int vi = vr - qd - kd, g = vi / HD, dd = vi % HD;
+                    uint64_t* b = a.ex.qkv + (size_t)g * GW + Gq * HD + HD / 2;
+                    fw_store(b + dd / 2, pack_h2(y[0], y[1]), id);
+                    fw_store(b + dd / 2 + 1, pack_h2(y[2], y[3]), id);
+                    uint16_t* vp = a.vc + (((size_t)it.layer * D.Hkv + g) * D.max_seq + pos) * HD;
+                    dev_store64(vp + dd, (uint64_t)pack_h2(y[0], y[1]) | ((uint64_t)pack_h2(y[2], y[3]) << 32));
+                }
+            }
+            break;
+        }
+        case K_ATTN: {
+            // merge the compute waves' states; publish o, or this chunk's partial
+            int CH;
+            const int nper = attn_split(pos + 1, a.items_per_head, &CH);
+            const int g = wg % D.Hkv, chunk = wg / D.Hkv;
+            for (int idx = 2 * lane; idx < Gq * HD; idx += 128) {
+                const int j = idx / HD, dd = idx % HD;
+                float M = -3.0e38f;
+#pragma unroll
+                for (int w = 0; w < kCompute; ++w) M = fmaxf(M, S->att_ml[(w * kMaxGroup + j) * 2]);
+                float L = 0.f, O0 = 0.f, O1 = 0.f;
+#pragma unroll
+                for (int w = 0; w < kCompute; ++w) {
+                    const float f = __builtin_amdgcn_exp2f(S->att_ml[(w * kMaxGroup + j) * 2] - M);
+                    L += f * S->att_ml[(w * kMaxGroup + j) * 2 + 1];
+                    O0 += f * S->att_o[(w * kMaxGroup + j) * HD + dd];
+                    O1 += f * S->att_o[(w * kMaxGroup + j) * HD + dd + 1];
+                }
+                const int head = g * Gq + j;
+                if (nper == 1) {
+                    // the whole row is here: publish o under the combine phase's id
+                    fw_store(a.ex.o + (head * HD + dd) / 2, pack_h2(O0 / L, O1 / L), id + 1);
+                } else {
+                    uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + chunk) * (HD + 2);
+                    fw_store(pp + 2 + dd, __builtin_bit_cast(uint32_t, O0), id);
+                    fw_store(pp + 3 + dd, __builtin_bit_cast(uint32_t, O1), id);
+                    if (dd == 0) {
+                        fw_store(pp, __builtin_bit_cast(uint32_t, M), id);
+                        fw_store(pp + 1, __builtin_bit_cast(uint32_t, L), id);
+                    }
+                }
+            }
+            break;
+        }
+        case K_WO:
+        case K_DOWN:
+        case K_EDOWN:
+            residual_add_publish(id);
+            break;
+        case K_GU:
+            // rows (4j .. 4j+3) = (g_m, u_m, g_m+1, u_m+1) with m = (gu0 + 4j) / 2
+            for (int j = lane; j < W.gun / 4; j += 64) {
+                float h[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float gv = rowsum(4 * j + 2 * e), uv = rowsum(4 * j + 2 * e + 1);
+                    h[e] = gv / (1.0f + __expf(-gv)) * uv;
+                }
+                fw_store(a.ex.h + (W.gu0 / 4 + j), pack_h2(h[0], h[1]), id);
+            }
+            break;
+        case K_ROUTER:
+            for (int j = lane; j < W.rn; j += 64)
+                fw_store(a.ex.r + W.r0 + j, __builtin_bit_cast(uint32_t, rowsum(j)), id);
+            break;
+        case K_EGU:
+            for (int j = lane; j < W.egun / 4; j += 64) {
+                const int vr = W.egu0 + 4 * j;
+                const int k = vr / (2 * D.F), m = (vr % (2 * D.F)) >> 1;
+                float h[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float gv = rowsum(4 * j + 2 * e), uv = rowsum(4 * j + 2 * e + 1);
+                    h[e] = S->pi[k] * (gv / (1.0f + __expf(-gv))) * uv;
+                }
+                fw_store(a.ex.h + (k * D.F + m) / 2, pack_h2(h[0], h[1]), id);
+            }
+            break;
+        case K_LM: {
+            float bv = -3.0e38f;
+            int bi = 0x7fffffff;
+            const bool dbg = (a.flags & F_DBG_LOGITS) != 0;
+            for (int j = lane; j < W.lmn; j += 64) {
+                const float v = rowsum(j);
+                const int r = W.lm0 + j;
+                if (dbg) gptr(a.dbg_logits)[(size_t)(it.step % 64) * D.V + r] = v;
+                if (v > bv || (v == bv && r < bi)) { bv = v; bi = r; }
+            }
+            wave_argmax(bv, bi);
+            if (lane == 0) {
+                fw_store(a.ex.am + 2 * wg, __builtin_bit_cast(uint32_t, bv), id);
+                fw_store(a.ex.am + 2 * wg + 1, (uint32_t)bi, id);
+            }
+            break;
+        }
+        default: break;
+        }
+    }
+
+    // ---- phases the compute waves take no part in --------------------------
+    __device__ __forceinline__ void solo(int kind, const PIter& it, int pos) {
+        if (dead) return;
+        if (kind == K_COMB) {
+            combine(it.q, pos);
+        } else if (kind == K_SAMPLE) {
+            if (lm_skipped(a, it.step)) {
+                tok = gptr(a.force_ids)[it.step];
+                return;
+            }
+            if (!(W.nq || W.won || wg == 0)) return;   // this workgroup never reads the token
+            KIE_LDS uint32_t* t = (KIE_LDS uint32_t*)S->att_q;   // scratch: 2 x 256 words
+            if (!gather(a.ex.am, 2 * kGrid, id_of(it.q - 1), [&](int i, uint32_t v) { t[i] = v; })) return;
+            float bv = -3.0e38f;
+            int bi = 0x7fffffff;
+            for (int w = lane; w < kGrid; w += 64) {
+                const float v = __builtin_bit_cast(float, t[2 * w]);
+                const int i = (int)t[2 * w + 1];
+                if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+            }
+            wave_argmax(bv, bi);
+            int next = (bi >= 0 && bi < a.D.V) ? bi : 0;   // out of range only with NaN logits
+            if (wg == 0 && lane == 0) gptr(a.out_ids)[it.step] = next;
+            if (a.flags & F_FORCE) {
+                const int f = gptr(a.force_ids)[it.step];
+                if (f >= 0) next = f;
+            }
+            tok = next;
+        }
+    }
+
+    // Split attention: the workgroup of chunk c of KV group g combines the
+    // nper partial states of its slice of the group's output pairs. Every
+    // (pair, chunk) state is read in one trip (lanes over pairs x chunks),
+    // staged in LDS, then one lane per pair merges its chunks.
+    __device__ __forceinline__ void combine(int q, int pos) {
+        const Dims& D = a.D;
+        int CH;
+        const int nper = attn_split(pos + 1, a.items_per_head, &CH);
+        if (nper == 1 || wg >= D.Hkv * nper) return;
+        const int Gq = D.H / D.Hkv, g = wg % D.Hkv, chunk = wg / D.Hkv;
+        const int P = Gq * HD / 2;
+        const int p0 = chunk * P / nper, p1 = (chunk + 1) * P / nper, np = p1 - p0;
+        const int T = np * nper;   // (pair, chunk) states, at most P + nper <= 768
+        const uint32_t ida = id_of(q - 1);
+        KIE_LDS float* st = S->att_o;   // scratch: [T][4] (m, l, o0, o1)
+        constexpr int R = 8;            // states per lane per trip
+        for (int t0 = 0; t0 < T; t0 += R * 64) {   // one trip unless T > 512
+            uint64_t w[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int t = t0 + r * 64 + lane;
+                if (t < T) {
+                    const int pr = p0 + t / nper, ch = t % nper;
+                    const int idx = 2 * pr, head = g * Gq + idx / HD, dd = idx % HD;
+                    const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + ch) * (HD + 2);
+                    w[r][0] = fw_load(pp);
+                    w[r][1] = fw_load(pp + 1);
+                    w[r][2] = fw_load(pp + 2 + dd);
+                    w[r][3] = fw_load(pp + 3 + dd);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[r][e] = (uint64_t)ida << 32;
+                }
+            }
+            uint32_t spins = 0;
+            while (true) {
+                bool ok = true;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ok = fw_ok(w[r][e], ida) && ok;
+                if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+                if (++spins > a.spin) {
+                    fail(1);
+                    return;
+                }
+                if ((spins & 63) == 0 && dev_load32(a.status) != 0) {
+                    fail(2);
+                    return;
+                }
+                __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int t = t0 + r * 64 + lane;
+                    if (t < T) {
+                        const int pr = p0 + t / nper, ch = t % nper;
+                        const int idx = 2 * pr, head = g * Gq + idx / HD, dd = idx % HD;
+                        const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + ch) * (HD + 2);
+                        if (!fw_ok(w[r][0], ida)) w[r][0] = fw_load(pp);
+                        if (!fw_ok(w[r][1], ida)) w[r][1] = fw_load(pp + 1);
+                        if (!fw_ok(w[r][2], ida)) w[r][2] = fw_load(pp + 2 + dd);
+                        if (!fw_ok(w[r][3], ida)) w[r][3] = fw_load(pp + 3 + dd);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int t = t0 + r * 64 + lane;
+                if (t < T)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st[t * 4 + e] = __builtin_bit_cast(float, fw_val(w[r][e]));
+            }
+        }
+        for (int j = lane; j < np; j += 64) {
+            float m = -3.0e38f, l = 0.f, o0 = 0.f, o1 = 0.f;
+            for (int ch = 0; ch < nper; ++ch) {
+                const KIE_LDS float* e = st + (j * nper + ch) * 4;
+                const float M = fmaxf(m, e[0]);
+                const float fo = __builtin_amdgcn_exp2f(m - M), fn = __builtin_amdgcn_exp2f(e[0] - M);
+                l = l * fo + e[1] * fn;
+                o0 = o0 * fo + e[2] * fn;
+                o1 = o1 * fo + e[3] * fn;
+                m = M;
+            }
+            const int idx = 2 * (p0 + j), head = g * Gq + idx / HD, dd = idx % HD;
+            fw_store(a.ex.o + (head * HD + dd) / 2, pack_h2(o0 / l, o1 / l), id_of(q));
+        }
+    }
+
+    // phase timeline: event e of phase q at the constant 100 MHz clock
+    __device__ __forceinline__ void stamp(int q, int e) {
+        if ((a.flags & F_TRACE) && q < kTracePhases && lane == 0)
+            gptr(a.trace)[((size_t)q * kGrid + wg) * 4 + e] = (int64_t)__builtin_amdgcn_s_memrealtime();
+    }
+
+    __device__ __forceinline__ void run() {
+        const Dims& D = a.D;
+        const int Q = a.n_steps * pps_of(D);
+        PIter it{0, 0, 0, 0};
+        for (; it.q < Q; advance(D, it)) {
+            const int kind = kind_of(D, it);
+            const int pos = a.pos0 + it.step;
+            stamp(it.q, 0);
+            if (phase_bars(a, kind, it.step, wg)) {
+                pre(kind, it);
+                stamp(it.q, 1);
+                wg_barrier();
+                wg_barrier();
+                stamp(it.q, 2);
+                post(kind, it, pos);
+            } else {
+                solo(kind, it, pos);
+            }
+            stamp(it.q, 3);
+        }
+        wait_vm0();
+    }
+};
+
+// ------------------------------------------------------------------------
+// Compute waves.
+// ------------------------------------------------------------------------
+// Each compute wave owns an LDS ring of kNS batches of kNB weight units,
+// filled by LDS DMA in phase order and consumed oldest first. Every fill
+// issues exactly kNB loads (a short batch tops up from the idle region, an
+// idle batch loads only from it), so when the oldest batch is consumed the
+// kNS-1 younger batches' loads are the only ones issued after it and
+// vmcnt((kNS-1)*kNB) is the exact wait. A batch is refilled right after it
+// is consumed, so up to kNS*kNB units stay in flight across phase
+// boundaries while the communication wave waits for the next input.
+struct Slot {
+    int q, kind, layer, step, u0, n;   // n == 0: idle batch; q: the phase to reach before consuming it
+};
+
+// Geometry of one GEMV phase as seen by one compute wave (uniform values).
+struct WaveGeo {
+    int q, kind, layer;
+    int n, nrows, K, nseg, off, row0;
+    int lo, hi;   // this wave's unit range
+    int upr;      // units per row segment (0: 256-wide rows, two per unit)
+};
+
+template <int HD>
+struct Compute {
+    const DecodeArgs& a;
+    KIE_LDS Smem* S;
+    int w, lane, wg, Q;
+    uint32_t ring0;    // LDS byte address of this wave's ring
+    PIter ic;          // issue cursor phase
+    WaveGeo ig;        // its geometry
+    int iu;            // next unit to issue in it
+    int routed;        // last MoE gate/up phase whose routing is in LDS
+    bool stop;         // the communication wave gave up: stream nothing more
+    PIter cc;          // next phase to enter (or the entered one when `entered`)
+    bool entered;
+    WaveGeo cg;        // geometry of the phase being consumed
+    int crow, cseg, ccol;   // position of the next unit to consume in it
+    float acc;         // running partial dot product of the current row
+
+    __device__ __forceinline__ Compute(const DecodeArgs& args, KIE_LDS Smem* s, int wi) : a(args), S(s), w(wi) {
+        lane = lane_id();
+        wg = blockIdx.x;
+        Q = a.n_steps * pps_of(a.D);
+        ring0 = lds_addr_of(S->ring) + (uint32_t)(w * kNS * kBatchBytes);
+        routed = -1;
+        stop = false;
+        cc = PIter{0, 0, 0, 0};
+        entered = false;
+        cg.q = -1;
+        crow = cseg = ccol = 0;
+        acc = 0.f;
+        ic = PIter{0, 0, 0, 0};
+        seek(false);
+    }
+
+    __device__ __forceinline__ void load_geo(WaveGeo& g, int q, int kind, int layer, int step) const {
+        const KIE_LDS int* p = (const KIE_LDS int*)&S->geo[kind];
+        g.q = q;
+        g.kind = kind;
+        g.layer = layer;
+        g.n = (kind == K_LM && lm_skipped(a, step)) ? 0 : __builtin_amdgcn_readfirstlane(p[0]);
+        g.nrows = __builtin_amdgcn_readfirstlane(p[1]);
+        g.K = __builtin_amdgcn_readfirstlane(p[2]);
+        g.nseg = __builtin_amdgcn_readfirstlane(p[3]);
+        g.off = __builtin_amdgcn_readfirstlane(p[4]);
+        g.row0 = __builtin_amdgcn_readfirstlane(p[5]);
+        g.lo = g.n * w / kCompute;
+        g.hi = g.n * (w + 1) / kCompute;
+        g.upr = g.K / kUnitHalves;
+    }
+
+    // move the issue cursor (from ic, or past it when `next`) to the first
+    // GEMV phase that has units for this wave
+    __device__ __forceinline__ void seek(bool next) {
+        if (next) advance(a.D, ic);
+        for (; ic.q < Q; advance(a.D, ic)) {
+            const int kind = kind_of(a.D, ic);
+            if (!is_gemv(kind)) continue;
+            load_geo(ig, ic.q, kind, ic.layer, ic.step);
+            if (ig.hi > ig.lo) {
+                iu = ig.lo;
+                return;
+            }
+        }
+    }
+
+    // kNB loads into the batch at LDS address dst: units iu .. iu+n-1 of the
+    // cursor phase, then units of the idle region
+    __device__ __forceinline__ void load_units(uint32_t dst, int n) {
+        const Dims& D = a.D;
+        const uint8_t* idle = a.idle + lane * 16;
+        const int kind = ig.kind;
+        if (kind == K_EGU || kind == K_EDOWN) {
+            const uint8_t* lb = a.experts + (size_t)ig.layer * D.E * a.expert_bytes + lane * 16;
+            const int upr = ig.upr;
+#pragma unroll
+            for (int s = 0; s < kNB; ++s) {
+                const uint8_t* src = idle + (size_t)s * kUnitBytes;
+                if (s < n) {
+                    const int u = iu + s;
+                    size_t off;
+                    if (kind == K_EGU) {
+                        const int vr = ig.row0 + u / upr, c = u % upr;
+                        const int k = vr / (2 * D.F), rr = vr % (2 * D.F);
+                        const int e = __builtin_amdgcn_readfirstlane(S->sel[k]);
+                        off = (size_t)e * a.expert_bytes + ((size_t)rr * D.d + c * kUnitHalves) * 2;
+                    } else {
+                        const int row = u / (D.topk * upr), rem = u % (D.topk * upr);
+                        const int k = rem / upr, c = rem % upr;
+                        const int e = __builtin_amdgcn_readfirstlane(S->sel[k]);
+                        off = (size_t)e * a.expert_bytes + (size_t)2 * D.F * D.d * 2 +
+                              ((size_t)(ig.row0 + row) * D.F + c * kUnitHalves) * 2;
+                    }
+                    src = lb + off;
+                }
+                dma_unit(src, dst + s * kUnitBytes);
+            }
+        } else {
+            const uint8_t* base = (kind == K_LM) ? a.lm : a.layers + (size_t)ig.layer * a.layer_bytes;
+            const uint8_t* src = base + (size_t)(ig.off + iu) * kUnitBytes + lane * 16;
+#pragma unroll
+            for (int s = 0; s < kNB; ++s)
+                dma_unit((s < n ? src : idle) + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+        }
+    }
+
+    __device__ __forceinline__ void load_idle(uint32_t dst) {
+        const uint8_t* idle = a.idle + lane * 16;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) dma_unit(idle + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+    }
+
+    // Refill the batch at dst: the next units in phase order, or an idle batch
+    // tagged with the phase whose first barrier must pass before issue can go
+    // on (the MoE gate/up phase of a blocked layer) or with Q (nothing left).
+    __device__ __forceinline__ Slot fill(uint32_t dst) {
+        if (!stop && ic.q < Q) {
+            const int gate = ig.kind == K_EGU ? ic.q : (ig.kind == K_EDOWN ? ic.q - 1 : -1);
+            if (gate <= routed) {
+                const int n = (ig.hi - iu < kNB) ? ig.hi - iu : kNB;
+                load_units(dst, n);
+                const Slot sl{ic.q, ig.kind, ic.layer, ic.step, iu, n};
+                iu += n;
+                if (iu >= ig.hi) seek(true);
+                return sl;
+            }
+            load_idle(dst);
+            return Slot{gate, 0, 0, 0, 0, 0};
+        }
+        load_idle(dst);
+        return Slot{Q, 0, 0, 0, 0, 0};
+    }
+
+    __device__ __forceinline__ void enter() {
+        const int kind = kind_of(a.D, cc);
+        if (!phase_bars(a, kind, cc.step, wg)) return;
+        wg_barrier();   // the input (and the routing, for MoE gate/up) is in LDS
+        stop = S->abort != 0u;
+        if (kind == K_EGU) routed = cc.q;
+    }
+
+    __device__ __forceinline__ void finish() {
+        const int kind = kind_of(a.D, cc);
+        if (!phase_bars(a, kind, cc.step, wg)) return;
+        if (kind == K_ATTN && !stop) {
+            const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
+            // register arrays sized for the group (1, 2, 4, 5 or 8 heads)
+            if (G == 1) attention<1>(l, pos);
+            else if (G == 2) attention<2>(l, pos);
+            else if (G <= 4) attention<4>(l, pos);
+            else if (G == 5) attention<5>(l, pos);
+            else attention<8>(l, pos);
+        }
+        wg_barrier();   // partial sums / attention states are in LDS
+    }
+
+    // Afterwards phase qx is entered and not finished (qx == Q: all finished).
+    __device__ __forceinline__ void goto_phase(int qx) {
+        while (true) {
+            if (entered) {
+                if (cc.q == qx) return;
+                finish();
+                advance(a.D, cc);
+                entered = false;
+            }
+            if (cc.q >= Q) return;
+            enter();
+            entered = true;
+        }
+    }
+
+    // consume the batch at LDS address src: all LDS reads of the batch are
+    // issued before the first product
+    __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
+        if (cg.q != sl.q) {
+            load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
+            if (cg.upr) {
+                const int per_row = cg.nseg * cg.upr;
+                crow = cg.lo / per_row;
+                const int rem = cg.lo - crow * per_row;
+                cseg = rem / cg.upr;
+                ccol = rem - cseg * cg.upr;
+            }
+        }
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
+        uint4 wv[kNB], xv[kNB];
+        if (cg.upr) {
+            int seg = cseg, c = ccol;
+#pragma unroll
+            for (int s = 0; s < kNB; ++s) {
+                if (s < sl.n) {
+                    wv[s] = lds_ld16(wb + s * kUnitBytes);
+                    xv[s] = lds_ld16(S->xin + seg * cg.K + c * kUnitHalves + lane * 8);
+                    if (++c == cg.upr) {
+                        c = 0;
+                        if (++seg == cg.nseg) seg = 0;
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < kNB; ++s) {
+                if (s < sl.n) {
+                    acc = dot8(wv[s], xv[s], acc);
+                    const bool row_end = (cseg == cg.nseg - 1 && ccol == cg.upr - 1) || sl.u0 + s == cg.hi - 1;
+                    if (row_end) {
+                        const float r = wave_sum_to_lane63(acc);
+                        if (lane == 63) S->part[crow * kCompute + w] = r;
+                        acc = 0.f;
+                    }
+                    if (++ccol == cg.upr) {
+                        ccol = 0;
+                        if (++cseg == cg.nseg) {
+                            cseg = 0;
+                            ++crow;
+                        }
+                    }
+                }
+            }
+        } else {
+            // 256-wide rows: one unit holds two rows (lanes 0-31 and 32-63)
+            const uint4 x = lds_ld16(S->xin + (lane & 31) * 8);
+#pragma unroll
+            for (int s = 0; s < kNB; ++s)
+                if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
+#pragma unroll
+            for (int s = 0; s < kNB; ++s) {
+                if (s < sl.n) {
+                    const float r = half32_sum_from_rows(row16_sum(dot8(wv[s], x, 0.f)));
+                    const int row = 2 * (sl.u0 + s) + (lane >> 5);
+                    if ((lane & 31) == 31 && row < cg.nrows) S->part[row * kCompute + w] = r;
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void run() {
+        Slot sq[kNS];   // batches in issue order; sq[i] sits at ring slot (head + i) % kNS
+        int head = 0;
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) sq[i] = fill(ring0 + i * kBatchBytes);
+#ifdef KIE_CTRACE
+        uint64_t tacc[4] = {0, 0, 0, 0};
+#define KIE_T(i) { const uint64_t t_ = __builtin_readcyclecounter(); tacc[i] += t_ - tlast; tlast = t_; }
+        uint64_t tlast = __builtin_readcyclecounter();
+#else
+#define KIE_T(i)
+#endif
+        while (cc.q < Q) {
+            const uint32_t at = ring0 + head * kBatchBytes;
+            goto_phase(sq[0].q);   // sq[0].q == Q once nothing is left: finishes every phase
+            KIE_T(0)
+            wait_vm<(kNS - 1) * kNB>();
+            KIE_T(1)
+            if (sq[0].n > 0 && !stop) consume(at, sq[0]);
+            wait_lgkm0();          // this batch's LDS reads are done before it is overwritten
+            KIE_T(2)
+            const Slot t = fill(at);
+            KIE_T(3)
+#pragma unroll
+            for (int i = 0; i + 1 < kNS; ++i) sq[i] = sq[i + 1];
+            sq[kNS - 1] = t;
+            head = (head + 1 == kNS) ? 0 : head + 1;
+        }
+        wait_vm0();
+#ifdef KIE_CTRACE
+        if ((a.flags & F_TRACE) && lane == 0)
+            for (int i = 0; i < 4; ++i)
+                gptr(a.trace)[((size_t)(kTracePhases - 8 + w) * kGrid + wg) * 4 + i] = (int64_t)tacc[i];
+#endif
+#undef KIE_T
+    }
+
+    // Attention of this workgroup's chunk: each compute wave takes every 7th
+    // block of positions, keeps an online-softmax state per query head of the
+    // group (GB >= heads per group), and leaves it in LDS for the
+    // communication wave to merge. Lanes: HD/4 per position, 4 dims each;
+    // U position blocks per round of loads.
+    template <int GB>
+    __device__ __forceinline__ void attention(int layer, int pos) {
+        const Dims& D = a.D;
+        constexpr int LPP = HD / 4;       // lanes per position
+        constexpr int PPI = 64 / LPP;     // positions per wave instruction
+        constexpr int U = 4;              // instructions per round
+        int CH;
+        attn_split(pos + 1, a.items_per_head, &CH);
+        const int Gq = D.H / D.Hkv;
+        const int g = wg % D.Hkv, chunk = wg / D.Hkv;
+        const int c = pos + 1;
+        const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
+        const int gi = lane / LPP, dl = (lane % LPP) * 4;
+        float qv[GB][4];
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qv[j][e] = (j < Gq) ? S->att_q[j * HD + dl + e] : 0.f;
+        float m[GB], ls[GB], o[GB][4];
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+            m[j] = -3.0e38f;
+            ls[j] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[j][e] = 0.f;
+        }
+        const uint16_t* Kb = a.kc + ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
+        const uint16_t* Vb = a.vc + ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
+        const uint64_t knew = *(const KIE_LDS uint64_t*)(S->att_k + dl);
+        const uint64_t vnew = *(const KIE_LDS uint64_t*)(S->att_v + dl);
+        static_assert(U == 4, "the cache loads below come in fours");
+        for (int b = p0 + w * PPI * U; b < p1; b += kCompute * PPI * U) {
+            uint64_t kw[U], vw[U];
+            const uint16_t* kp[U];
+            const uint16_t* vp[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int pp = b + u * PPI + gi;
+                const int src = (pp < pos && pp < p1) ? pp : 0;   // in-bounds address for every lane
+                kp[u] = Kb + (size_t)src * HD + dl;
+                vp[u] = Vb + (size_t)src * HD + dl;
+            }
+            dev_load64x4_sync(kp[0], kp[1], kp[2], kp[3], kw[0], kw[1], kw[2], kw[3]);
+            dev_load64x4_sync(vp[0], vp[1], vp[2], vp[3], vw[0], vw[1], vw[2], vw[3]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int pp = b + u * PPI + gi;
+                if (!(pp < pos && pp < p1)) {
+                    kw[u] = knew;   // the new position (or padding, masked below)
+                    vw[u] = vnew;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int pp = b + u * PPI + gi;
+                const bool valid = pp < p1;
+                float kf[4], vf[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kf[e] = h2f_bits((uint16_t)(kw[u] >> (16 * e)));
+                    vf[e] = h2f_bits((uint16_t)(vw[u] >> (16 * e)));
+                }
+#pragma unroll
+                for (int j = 0; j < GB; ++j) {
+                    if (j < Gq) {
+                        float s = qv[j][0] * kf[0] + qv[j][1] * kf[1] + qv[j][2] * kf[2] + qv[j][3] * kf[3];
+                        s = row16_sum(s);
+                        if (LPP == 32)   // swap 16-lane halves of each 32-lane group
+                            s += __builtin_bit_cast(float,
+                                                    __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, s), 0x401F));
+                        if (valid) {
+                            const float mn = fmaxf(m[j], s);
+                            const float cr = __builtin_amdgcn_exp2f(m[j] - mn);
+                            const float pr = __builtin_amdgcn_exp2f(s - mn);
+                            ls[j] = ls[j] * cr + pr;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) o[j][e] = o[j][e] * cr + pr * vf[e];
+                            m[j] = mn;
+                        }
+                    }
+                }
+            }
+        }
+        // merge the position groups of this wave
+#pragma unroll
+        for (int off = LPP; off < 64; off <<= 1) {
+#pragma unroll
+            for (int j = 0; j < GB; ++j) {
+                if (j < Gq) {
+                    const float m2 = shfl_xor_f(m[j], off), l2 = shfl_xor_f(ls[j], off);
+                    const float mn = fmaxf(m[j], m2);
+                    const float f1 = __builtin_amdgcn_exp2f(m[j] - mn), f2 = __builtin_amdgcn_exp2f(m2 - mn);
+                    ls[j] = ls[j] * f1 + l2 * f2;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[j][e] = o[j][e] * f1 + shfl_xor_f(o[j][e], off) * f2;
+                    m[j] = mn;
+                }
+            }
+        }
+        if (lane < LPP) {
+#pragma unroll
+            for (int j = 0; j < GB; ++j) {
+                if (j < Gq) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S->att_o[(w * kMaxGroup + j) * HD + dl + e] = o[j][e];
+                    if (lane == 0) {
+                        S->att_ml[(w * kMaxGroup + j) * 2] = m[j];
+                        S->att_ml[(w * kMaxGroup + j) * 2 + 1] = ls[j];
+                    }
+                }
+            }
+        }
+    }
+};
+
+template <int HD>
+__global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
+    __shared__ Smem smem_;
+    KIE_LDS Smem* S = (KIE_LDS Smem*)&smem_;
+    const DecodeArgs& a = *ap;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    WgPlan W;
+    if (wave == 0) {
+        make_plan(a.D, blockIdx.x, W);
+        if (threadIdx.x == 0) {
+            S->abort = 0u;
+            write_geo(a, W, blockIdx.x, S->geo);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        Comm<HD> cm(a, S, W);
+        cm.run();
+    } else {
+        Compute<HD> cp(a, S, wave - 1);
+        cp.run();
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int grid, hipStream_t s) {
+    void* args[] = {&dev_args};
+    const void* fn = hd == 64 ? (const void*)decode_kernel<64> : (const void*)decode_kernel<128>;
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+}  // namespace kie

@@ -1,20 +1,18 @@
 // kie_device.h - gfx950 device primitives of the persistent decode kernel.
 //
-//  * LDS helpers that bypass the compiler's LDS-DMA tracking (inline asm), so a
-//    wave that issues global_load_lds can poll LDS without draining vmcnt.
-//  * The weight streamer ("producer" waves): non-temporal 16-byte-per-lane
-//    global_load_lds_dwordx4 into a ring of 1 KiB LDS slots, a fixed number of
-//    loads kept in flight, readiness published per slot in issue order.
-//    This is the monokernel article's non-temporal streaming of weights into
-//    LDS and registers ("Inside the monokernel"), done with CDNA4's direct
-//    global->LDS loads.
-//  * Wave-wide DPP reductions (row_ror / row_bcast, gfx9 family).
-//  * v_dot2 fp16 x fp16 -> fp32 inner products (the pages' VDOT path for
-//    batch-1 GEMV, same section).
-//  * The grid barrier: each workgroup's leader publishes an epoch in its own
-//    word of a flat array and polls the whole array (an all-gather barrier,
-//    the shape of the 256-CU / 2,048-byte publish test in "Inside the
-//    monokernel"), with agent-scope release/acquire and a bounded spin.
+//  * v_dot2 fp16 x fp16 -> fp32 inner products and wave-wide DPP reductions:
+//    batch-1 projections are matrix-vector products done on the vector ALU,
+//    not on matrix cores (news.creeta.com monokernel article, "Inside the
+//    monokernel": VDOT/SDOT instead of matrix cores at batch 1).
+//  * Non-temporal 16-byte weight loads into registers (same section: weights
+//    are streamed non-temporally rather than through the caches).
+//  * Flagged words for data exchange between workgroups: a 64-bit word holds
+//    a 32-bit payload and the 32-bit id of the phase that wrote it; it is
+//    stored and loaded as one device-scope (sc1) access, so a reader that sees
+//    the expected id also sees the payload, with no cache flush or grid
+//    barrier. This plays the part of the pages' publish buffer ("Inside the
+//    monokernel": a 2,048-byte publish buffer across 256 CUs).
+//  * The classic fenced grid barrier, kept for the barrier probe.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,28 +24,72 @@ namespace kie {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte non-temporal global load.
-__device__ __forceinline__ uint4 ld_nt16(const void* p) {
-    u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 // Pointers into LDS carry address space 3 explicitly so that every access
 // through them is a ds_* instruction (a generic pointer would become flat_*).
 #define KIE_LDS __attribute__((address_space(3)))
+// Pointers read from the argument block are generic; casting them to the
+// global address space makes every access a global_* instruction (a flat_*
+// access would also count against lgkmcnt, which the LDS waits rely on).
+#define KIE_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ KIE_GLOBAL T* gptr(T* p) {
+    return (KIE_GLOBAL T*)p;
+}
 
 constexpr int kStatusTimeout = 1;
 
-__device__ __forceinline__ uint32_t lds_off(const KIE_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// LDS load/store the compiler does not see as LDS accesses (so it inserts no
-// vmcnt wait for in-flight LDS-DMA). The load waits for its own result and
-// returns it as a wave-uniform value (every lane reads the same word).
-__device__ __forceinline__ uint32_t lds_ld_u32(const KIE_LDS uint32_t* p) {
-    uint32_t v;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_off(p)) : "memory");
-    return __builtin_amdgcn_readfirstlane(v);
+// ------------------------------------------------------------- loads -------
+// 16-byte non-temporal global load.
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+    u32x4_t v = __builtin_nontemporal_load((const KIE_GLOBAL u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
-// 16-byte LDS load/store (ds_read_b128 / ds_write_b128).
+
+// One streaming unit (1 KiB: 16 bytes per lane, lane l's bytes at
+// gsrc_lane = base + 16 l) straight from global memory into LDS at byte
+// address lds_addr + 16 l, non-temporally and without passing through
+// registers. The load is written in assembly, so the compiler neither tracks
+// it nor inserts waits for it: the caller waits with wait_vm<N>() (vmcnt
+// counts these loads in issue order) before reading the LDS bytes, and
+// makes sure its own earlier LDS reads of the target have returned before
+// issuing the next load into it.
+__device__ __forceinline__ void dma_unit(const void* gsrc_lane, uint32_t lds_addr) {
+    uint32_t saved;   // m0 is reserved by the compiler: put its value back
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gsrc_lane), "s"(lds_addr)
+        : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const KIE_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+// Also a compiler barrier for memory accesses, so LDS reads of DMA'd data
+// are not moved above it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that waits for this wave's LDS traffic only: weight loads
+// still in flight stay in flight across it.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ----------------------------------------------------------------- LDS ------
 __device__ __forceinline__ uint4 lds_ld16(const KIE_LDS void* p) {
     u32x4_t v = *(const KIE_LDS u32x4_t*)p;
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -56,25 +98,8 @@ __device__ __forceinline__ void lds_st16(KIE_LDS void* p, uint4 v) {
     u32x4_t w = {v.x, v.y, v.z, v.w};
     *(KIE_LDS u32x4_t*)p = w;
 }
-__device__ __forceinline__ void lds_st_u32(KIE_LDS uint32_t* p, uint32_t v) {
-    asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
-}
-__device__ __forceinline__ void lds_add_u32(KIE_LDS uint32_t* p, uint32_t v) {
-    asm volatile("ds_add_u32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// ------------------------------------------------------------------ DPP ---
+// ------------------------------------------------------------------ DPP -----
 template <int CTRL, int RM = 0xF>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float,
@@ -100,23 +125,33 @@ __device__ __forceinline__ float row8_sum(float v) {
 __device__ __forceinline__ float half32_sum_from_rows(float v) { return v + dpp_f<0x142, 0xA>(v); }
 // After half32_sum_from_rows: lanes 48..63 hold the sum of all 64 lanes.
 __device__ __forceinline__ float full_sum_from_halves(float v) { return v + dpp_f<0x143, 0xC>(v); }
-
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
     return full_sum_from_halves(half32_sum_from_rows(row16_sum(v)));
 }
-__device__ __forceinline__ float readlane_f(float v, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
 __device__ __forceinline__ float shfl_xor_f(float v, int m) {
-    int src = (lane_id() ^ m) << 2;
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, __builtin_bit_cast(int, v)));
 }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) {
     return __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
 }
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off; off >>= 1) v = fmaxf(v, shfl_xor_f(v, off));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off; off >>= 1) v += shfl_xor_f(v, off);
+    return v;
+}
+// (value, index) maximum over the wave, ties to the lower index.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    for (int off = 32; off; off >>= 1) {
+        float ov = shfl_xor_f(v, off);
+        int oi = shfl_xor_i(i, off);
+        if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+    }
+}
 
-// ---------------------------------------------------------------- dot2 ----
+// ---------------------------------------------------------------- dot2 ------
 __device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w.x), __builtin_bit_cast(h2_t, x.x), acc, false);
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w.y), __builtin_bit_cast(h2_t, x.y), acc, false);
@@ -125,97 +160,118 @@ __device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
     return acc;
 }
 
-__device__ __forceinline__ uint16_t f2h_bits(float f) {
-    return __builtin_bit_cast(uint16_t, (_Float16)f);
+__device__ __forceinline__ uint16_t f2h_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h2f_bits(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    return (uint32_t)f2h_bits(a) | ((uint32_t)f2h_bits(b) << 16);
 }
-__device__ __forceinline__ float h2f_bits(uint16_t h) {
-    return (float)__builtin_bit_cast(_Float16, h);
+
+// ------------------------------------------------------- flagged words -----
+// Word = (phase id << 32) | payload; one device-scope 64-bit store / load.
+__device__ __forceinline__ void fw_store(uint64_t* p, uint32_t payload, uint32_t id) {
+    __hip_atomic_store(gptr(p), ((uint64_t)id << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fw_load(const uint64_t* p) {
+    return __hip_atomic_load(gptr(const_cast<uint64_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool fw_ok(uint64_t w, uint32_t id) { return (uint32_t)(w >> 32) == id; }
+__device__ __forceinline__ uint32_t fw_val(uint64_t w) { return (uint32_t)w; }
+
+// Device-scope plain data (the KV cache): 8-byte loads and stores that are
+// coherent across the XCDs' L2 caches without a flush.
+__device__ __forceinline__ void dev_store64(void* p, uint64_t v) {
+    __hip_atomic_store(gptr((uint64_t*)p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void dev_store32(void* p, uint32_t v) {
+    __hip_atomic_store(gptr((uint32_t*)p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t dev_load64(const void* p) {
+    return __hip_atomic_load(gptr((uint64_t*)const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t dev_load32(const void* p) {
+    return __hip_atomic_load(gptr((uint32_t*)const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------------ LDS ring ----
-// Control block shared by the waves of one workgroup (lives in LDS).
-struct RingCtl {
-    uint32_t ready[2];        // per producer wave: its units landed in LDS
-    uint32_t cons[8];         // per consumer wave: lower bound of its next unit
-    uint32_t sync;            // consumer-wave LDS barrier counter
-    uint32_t abort;           // nonzero: every wave leaves its loops
-    uint32_t flag;            // leader -> other consumer waves broadcast
-    uint32_t route;           // MoE: number of routing decisions published
-    uint32_t token;           // broadcast of the sampled token
-    uint32_t sel[16];         // MoE: selected experts of the current layer
-    float pi[16];             // MoE: their router probabilities
-    float scratch[64];        // small cross-wave reductions
-};
+// Four device-scope 8-byte loads per lane whose data has arrived when the
+// statement returns (the wait is part of it). Code that also keeps LDS DMA in
+// flight uses this so that the compiler never sees a load of its own in
+// flight there (it would otherwise insert waits that also drain the DMA).
+__device__ __forceinline__ void dev_load64x4_sync(const void* p0, const void* p1, const void* p2, const void* p3,
+                                                  uint64_t& v0, uint64_t& v1, uint64_t& v2, uint64_t& v3) {
+    asm volatile(
+        "global_load_dwordx2 %0, %4, off sc1\n\t"
+        "global_load_dwordx2 %1, %5, off sc1\n\t"
+        "global_load_dwordx2 %2, %6, off sc1\n\t"
+        "global_load_dwordx2 %3, %7, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+        : "memory");
+}
 
-template <int NP, int NC, int NSLOT>
-struct RingCfg {
-    static constexpr int kNP = NP;
-    static constexpr int kNC = NC;
-    static constexpr int kSlots = NSLOT;
-    static constexpr uint32_t kMask = NSLOT - 1;
-    static_assert((NSLOT & (NSLOT - 1)) == 0, "slot count must be a power of two");
-    static_assert(NP == 2, "readiness is tracked per unit parity");
-};
-
-// Consumer side: wait until stream unit u is in LDS. Producer 0 has landed
-// units 0, 2, .., 2*ready[0]-2 and producer 1 units 1, 3, .., 2*ready[1]-1, so
-// every unit below min(2*ready[0], 2*ready[1]+1) is in LDS; `avail` caches
-// that bound. Returns false on abort.
-__device__ __forceinline__ bool ring_wait_ready(KIE_LDS RingCtl* ctl, uint32_t u, uint32_t& avail, uint32_t limit) {
-    if ((int)(u - avail) < 0) return true;
+// Wait until words [0, n) of src all carry `id`, then call f(i, payload) for
+// every word (lane l handles i = l, l + 64, ...). One wave calls this. The
+// words are read in blocks of 64 * kGatherRegs with every load of a block
+// issued at once, so when the data is already published one trip through the
+// memory pipeline per block suffices; words not yet published are re-read
+// until they are.
+// Returns 0, or 1 when spin_limit polls went by, or 2 when *status became
+// non-zero (another workgroup gave up).
+constexpr int kGatherRegs = 32;   // words per lane per block
+template <class F>
+__device__ __forceinline__ int fw_gather(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
+                                         const uint32_t* status, F f) {
+    const int lane = lane_id();
     uint32_t spins = 0;
-    while (true) {
-        uint32_t r0 = 2u * lds_ld_u32(&ctl->ready[0]);
-        uint32_t r1 = 2u * lds_ld_u32(&ctl->ready[1]) + 1u;
-        avail = ((int)(r0 - r1) < 0) ? r0 : r1;
-        if ((int)(u - avail) < 0) return true;
-        if (lds_ld_u32(&ctl->abort)) return false;
-        if (++spins > limit) {
-            lds_st_u32(&ctl->abort, 1);
-            return false;
+    for (int base = 0; base < n; base += 64 * kGatherRegs) {
+        uint64_t w[kGatherRegs];
+#pragma unroll
+        for (int c = 0; c < kGatherRegs; ++c) {
+            const int i = base + c * 64 + lane;
+            w[c] = (i < n) ? fw_load(src + i) : ((uint64_t)id << 32);
         }
-        __builtin_amdgcn_s_sleep(0);
+        while (true) {
+            bool ok = true;
+#pragma unroll
+            for (int c = 0; c < kGatherRegs; ++c) ok = fw_ok(w[c], id) && ok;
+            if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+            if (++spins > spin_limit) return 1;
+            if ((spins & 63) == 0 && dev_load32(status) != 0) return 2;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int c = 0; c < kGatherRegs; ++c) {
+                const int i = base + c * 64 + lane;
+                if (i < n && !fw_ok(w[c], id)) w[c] = fw_load(src + i);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kGatherRegs; ++c) {
+            const int i = base + c * 64 + lane;
+            if (i < n) f(i, fw_val(w[c]));
+        }
     }
+    return 0;
 }
 
-// Consumer-wave LDS barrier (producers do not take part). Returns false on abort.
-// `gen` is the value the counter must reach (caller adds NC per sync).
-__device__ __forceinline__ bool consumer_sync(KIE_LDS RingCtl* ctl, uint32_t gen, uint32_t limit) {
-    wait_lgkm0();
-    if (lane_id() == 0) lds_add_u32(&ctl->sync, 1u);   // one arrival per wave
-    uint32_t spins = 0;
-    while (true) {
-        uint32_t v = lds_ld_u32(&ctl->sync);
-        if ((int)(v - gen) >= 0) return true;
-        if (lds_ld_u32(&ctl->abort)) return false;
-        if (++spins > limit) {
-            lds_st_u32(&ctl->abort, 1);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(0);
-    }
-}
-
-// Grid barrier executed by ONE wave per workgroup (the leader wave).
-// Publishes `epoch` in bar[wg] after an agent-scope release, then polls every
-// workgroup's word until all reached `epoch`, then acquires. Returns false on
-// timeout or when another workgroup reported a failure in *status.
-__device__ __forceinline__ bool grid_barrier_leader(uint32_t* bar, uint32_t* status, int nwg, int wg,
+// ------------------------------------------------------- fenced barrier -----
+// Grid barrier executed by ONE wave per workgroup: agent-scope release, publish
+// `epoch` in bar[wg], poll every workgroup's word, agent-scope acquire.
+// Returns false on timeout or when *status reports a failure.
+__device__ __forceinline__ bool grid_barrier_fenced(uint32_t* bar, uint32_t* status, int nwg, int wg,
                                                     uint32_t epoch, uint32_t limit) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (lane_id() == 0) __hip_atomic_store(&bar[wg], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane_id() == 0) dev_store32(&bar[wg], epoch);
     uint32_t spins = 0;
     while (true) {
         bool ok = true;
         for (int i = lane_id(); i < nwg; i += 64) {
-            uint32_t v = __hip_atomic_load(&bar[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t v = dev_load32(&bar[i]);
             ok = ok && ((int)(v - epoch) >= 0);
         }
         if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-        if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+        if (dev_load32(status) != 0) return false;
         if (++spins > limit) {
-            if (lane_id() == 0)
-                __hip_atomic_store(status, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane_id() == 0) dev_store32(status, (uint32_t)kStatusTimeout);
             return false;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -223,92 +279,5 @@ __device__ __forceinline__ bool grid_barrier_leader(uint32_t* bar, uint32_t* sta
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return true;
 }
-
-// ----------------------------------------------------------- producer -----
-// The producer waves walk the workgroup's weight stream unit by unit; wave p
-// issues the units of parity p. A unit may be loaded into slot u % NSLOT only
-// when every consumer wave has moved past unit u - NSLOT.
-template <class RC, int DEPTH>
-struct Producer {
-    KIE_LDS RingCtl* ctl;
-    KIE_LDS uint8_t* ring;   // LDS ring base
-    uint32_t p;              // producer index (unit parity)
-    uint32_t u;              // next stream unit index (both parities)
-    uint32_t issued;         // units issued by this wave
-    uint32_t published;      // ready value last published
-    uint32_t free_lim;       // units below this may be issued
-    uint32_t limit;
-    uint32_t aux;            // cache-policy bits of the load (non-temporal)
-
-    __device__ __forceinline__ void init(KIE_LDS RingCtl* c, KIE_LDS uint8_t* r, uint32_t pi, uint32_t spin_limit) {
-        ctl = c;
-        ring = r;
-        p = pi;
-        u = 0;
-        issued = 0;
-        published = 0;
-        free_lim = RC::kSlots;
-        limit = spin_limit;
-    }
-
-    __device__ __forceinline__ uint32_t min_cons() {
-        uint32_t m = lds_ld_u32(&ctl->cons[0]);
-#pragma unroll
-        for (int c = 1; c < RC::kNC; ++c) {
-            uint32_t v = lds_ld_u32(&ctl->cons[c]);
-            if ((int)(v - m) < 0) m = v;
-        }
-        return m;
-    }
-
-    __device__ __forceinline__ void publish_all() {
-        wait_vm0();
-        if (issued != published) {
-            published = issued;
-            lds_st_u32(p ? &ctl->ready[1] : &ctl->ready[0], issued);
-        }
-    }
-
-    // Wait until unit u may be loaded. Returns false on abort.
-    __device__ __forceinline__ bool wait_slot() {
-        if ((int)(u - free_lim) < 0) return true;
-        free_lim = min_cons() + RC::kSlots;
-        if ((int)(u - free_lim) < 0) return true;
-        publish_all();   // consumers may be waiting for units already in flight
-        uint32_t spins = 0;
-        while (true) {
-            __builtin_amdgcn_s_sleep(1);
-            free_lim = min_cons() + RC::kSlots;
-            if ((int)(u - free_lim) < 0) return true;
-            if (lds_ld_u32(&ctl->abort)) return false;
-            if (++spins > limit) {
-                lds_st_u32(&ctl->abort, 1);
-                return false;
-            }
-        }
-    }
-
-    // Stream n units starting at global address src (1 KiB each). Returns false on abort.
-    __device__ __forceinline__ bool stream(const uint8_t* src, uint32_t n) {
-        uint32_t end = u + n;
-        // first unit of my parity
-        uint32_t j = (u & 1u) == p ? 0u : 1u;
-        u += j;
-        for (; (int)(u - end) < 0; u += 2, j += 2) {
-            if (!wait_slot()) return false;
-            const uint8_t* g = src + (size_t)j * kUnitBytes + lane_id() * 16;
-            KIE_LDS uint8_t* dst = ring + (u & RC::kMask) * kUnitBytes;
-            __builtin_amdgcn_global_load_lds((const void*)g, (KIE_LDS void*)dst, 16, 0, 2 /* nt */);
-            ++issued;
-            if (issued - published > (uint32_t)DEPTH) {
-                wait_vm<DEPTH>();
-                published = issued - DEPTH;
-                lds_st_u32(p ? &ctl->ready[1] : &ctl->ready[0], published);
-            }
-        }
-        u = end;
-        return true;
-    }
-};
 
 }  // namespace kie

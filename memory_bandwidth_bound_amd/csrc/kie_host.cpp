@@ -70,24 +70,23 @@ int validate_config(const kie_config& c, std::string* err) {
         if (c.n_experts > 1024) return fail("at most 1024 experts");
         if (c.d_model % 512 || c.ffn_dim % 512) return fail("MoE needs d_model and ffn_dim multiples of 512");
     }
+    if (c.vocab > kMaxRowsWg * kGrid) return fail("vocab must be at most 65536");
     Dims D = dims_of(c);
-    int items = kGrid / c.n_kv_heads;
-    if ((long)items * kAttnChunkMax < c.max_seq) return fail("max_seq too long for the attention split");
-    // LDS budget: input vector and per-phase partial sums
+    // LDS budget: input vector, per-phase partial sums, owned residual rows
     int max_in = c.d_model;
     if (c.n_heads * c.head_dim > max_in) max_in = c.n_heads * c.head_dim;
     int kdown = c.n_experts ? c.top_k * c.ffn_dim : c.ffn_dim;
     if (kdown > max_in) max_in = kdown;
-    if (max_in > 8192) return fail("largest GEMV input must be at most 8192 elements");
+    if (max_in > kMaxInput) return fail("largest GEMV input must be at most 8192 elements");
     for (int ph = 0; ph < PH_COUNT; ++ph) {
         if (c.n_experts == 0 && (ph == PH_ROUTER || ph == PH_EGU || ph == PH_EDOWN)) continue;
         if (c.n_experts != 0 && (ph == PH_GU || ph == PH_DOWN)) continue;
-        for (int w = 0; w < kGrid; ++w) {
-            PhaseShape s = phase_shape(D, ph);
-            RowSplit r = split_rows(s.M, s.gran, kGrid, w);
-            int parts = (ph == PH_EDOWN ? c.top_k : 1) * r.nrows * (s.K >= 512 ? s.K / 512 : 1);
-            if (parts > 1024) return fail("a workgroup's share of a phase exceeds 1024 partial sums");
-        }
+        PhaseShape s = phase_shape(D, ph);
+        if (s.M % s.gran) return fail("phase rows not a multiple of their split granularity");
+        RowSplit r = split_rows(s.M, s.gran, kGrid, 0);   // workgroup 0 has the largest share
+        if (r.nrows > kMaxRowsWg) return fail("a workgroup's share of a phase exceeds 256 rows");
+        if ((ph == PH_WO || ph == PH_DOWN || ph == PH_EDOWN) && r.nrows > kMaxOwnRows)
+            return fail("a workgroup's share of the residual exceeds 32 rows");
     }
     if (err) err->clear();
     return KIE_OK;
@@ -132,16 +131,15 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.kv_bytes = (size_t)D.L * D.Hkv * D.max_seq * D.hd * 2;
     Y.off_k = take(Y.kv_bytes);
     Y.off_v = take(Y.kv_bytes);
-    Y.off_x = take((size_t)D.d * 4);
-    Y.off_q = take((size_t)D.H * D.hd * 4);
-    Y.off_o = take((size_t)D.H * D.hd * 2);
+    Y.off_ex_x = take((size_t)D.d / 2 * 8);
+    Y.off_ex_qkv = take((size_t)(D.H + D.Hkv) * D.hd * 8);
+    Y.off_ex_part = take((size_t)D.H * Y.attn_items_per_head * (D.hd + 2) * 8);
+    Y.off_ex_o = take((size_t)D.H * D.hd / 2 * 8);
     size_t hlen = D.E ? (size_t)D.topk * D.F : (size_t)D.F;
-    Y.off_h = take(hlen * 2);
-    Y.off_router = take((size_t)(D.E ? D.E : 1) * 4);
-    Y.off_attn_part = take((size_t)D.H * Y.attn_items_per_head * (D.hd + 2) * 4);
-    Y.off_attn_cnt = take((size_t)D.Hkv * 64);
-    Y.off_argmax = take((size_t)kGrid * 8);
-    Y.off_bar = take((size_t)kGrid * 4);
+    Y.off_ex_h = take(hlen / 2 * 8);
+    Y.off_ex_r = take((size_t)(D.E ? D.E : 1) * 8);
+    Y.off_ex_am = take((size_t)kGrid * 2 * 8);
+    Y.ex_bytes = off - Y.off_ex_x;
     Y.off_status = take(64 * 4);
     Y.off_out = take((size_t)D.max_seq * 4);
     Y.off_force = take((size_t)D.max_seq * 4);
@@ -149,6 +147,8 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_dbg_experts = take((size_t)kDebugRows * D.L * (D.topk ? D.topk : 1) * 4);
     Y.off_plan = take((size_t)2 * (kGrid + 1) * 4);
     Y.off_args = take(4096);
+    Y.off_idle = take(16384);
+    Y.off_trace = take((size_t)kTracePhases * kGrid * 4 * 8);
     Y.total = off;
 }
 

@@ -27,15 +27,15 @@ struct Layout {
     size_t off_rope;              // float2 [max_seq][hd/2] (cos, sin)
     size_t off_k, off_v;          // fp16 [L][Hkv][max_seq][hd]
     size_t kv_bytes;              // one of K or V
-    size_t off_x;                 // fp32 [d] residual
-    size_t off_q;                 // fp32 [H*hd]
-    size_t off_o;                 // fp16 [H*hd]
-    size_t off_h;                 // fp16 [max(F, topk*F)]
-    size_t off_router;            // fp32 [E]
-    size_t off_attn_part;         // fp32 [H][items per kv head][hd + 2]
-    size_t off_attn_cnt;          // u32 [Hkv] (padded)
-    size_t off_argmax;            // {f32, i32} [kGrid]
-    size_t off_bar;               // u32 [kGrid] barrier slots
+    // flagged-word exchange buffers (64-bit words), zeroed at load
+    size_t off_ex_x;              // [d/2]
+    size_t off_ex_qkv;            // [Hkv][(H/Hkv + 1) * hd]
+    size_t off_ex_part;           // [H][items per kv head][hd + 2]
+    size_t off_ex_o;              // [H*hd/2]
+    size_t off_ex_h;              // [max(F, topk*F)/2]
+    size_t off_ex_r;              // [max(E, 1)]
+    size_t off_ex_am;             // [kGrid][2]
+    size_t ex_bytes;              // whole exchange region, from off_ex_x
     size_t off_status;            // u32 [64]
     size_t off_out;               // i32 [max_seq]
     size_t off_force;             // i32 [max_seq]
@@ -43,6 +43,8 @@ struct Layout {
     size_t off_dbg_experts;       // i32 [kDebugRows][L][topk]
     size_t off_plan;              // i32 piece_off[kGrid+1], lm_off[kGrid+1]
     size_t off_args;              // kernel argument block (4 KiB)
+    size_t off_idle;              // 16 KiB read by weight batches that have nothing to stream
+    size_t off_trace;             // i64 [kTracePhases][kGrid][4] phase timeline
     size_t total;
     int piece_off[kGrid + 1];     // units: start of workgroup w's piece in a layer block
     int lm_off[kGrid + 1];        // units: start of workgroup w's LM slab

@@ -1,5 +1,5 @@
-// kie_kernels.h - kernel argument blocks and launch helpers shared by the
-// kernels (kie_kernels.hip) and the C ABI (kie_api.hip).
+// kie_kernels.h - kernel argument blocks and launchers shared by the kernels
+// (kie_decode.hip, kie_probes.hip) and the C ABI (kie_api.hip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -8,31 +8,52 @@
 
 namespace kie {
 
-// Waves of the persistent workgroup: 2 weight-streaming waves + 6 compute waves.
-constexpr int kProducers = 2;
-constexpr int kConsumers = 6;
-constexpr int kThreads = 64 * (kProducers + kConsumers);
-constexpr int kSlots = 128;                    // 1 KiB LDS ring slots
-constexpr int kDepth = 40;                     // loads in flight per streaming wave
-constexpr int kRegionA = 28 * 1024;            // input vector + partials | attention scratch
-constexpr int kXinBytes = 16 * 1024;           // fp16 GEMV input, up to 8192 elements
-constexpr int kPartFloats = 1024;              // per-phase partial sums
-constexpr int kCtlBytes = 512;
-constexpr int kLdsBytes = kSlots * 1024 + kRegionA + kCtlBytes;
+// Waves of a persistent workgroup: wave 0 exchanges data with the other
+// workgroups and runs the epilogues; waves 1..7 stream weights into LDS and
+// compute the dot products.
+constexpr int kWaves = 8;
+constexpr int kCompute = kWaves - 1;
+constexpr int kThreads = 64 * kWaves;
+// Ring geometry (compile-time tuning knobs).
+#ifndef KIE_NB
+#define KIE_NB 8
+#endif
+#ifndef KIE_NS
+#define KIE_NS 2
+#endif
+constexpr int kNB = KIE_NB;               // 1 KiB units per batch
+constexpr int kNS = KIE_NS;               // batches in flight per compute wave (an LDS ring)
+constexpr int kBatchBytes = kNB * kUnitBytes;
+constexpr int kIdleBytes = kBatchBytes;   // zero region loaded by batches with nothing to stream
+constexpr int kMaxIn = kMaxInput;
 
 enum : int {
     F_FORCE = 1,        // force_ids drives the next input where >= 0
     F_DBG_LOGITS = 2,   // write every pass's logits to dbg_logits
     F_DBG_EXPERTS = 4,  // write every pass's expert ids to dbg_experts
-    F_SKIP_LM = 8       // skip the LM head on every pass but the last (prefill)
+    F_SKIP_LM = 8,      // skip the LM head on every pass but the last (prefill)
+    F_TRACE = 16        // record the phase timeline in trace
+};
+
+// Flagged-word exchange buffers (64-bit words: phase id << 32 | payload).
+struct Exchange {
+    uint64_t* x;     // [d/2]    residual after Wo / down, fp16 pairs
+    uint64_t* qkv;   // [Hkv][(G+1)*hd] per KV group (G query heads): the group's
+                     //          rotated queries (fp32), then the new key as
+                     //          rotary pairs (k[i], k[i+hd/2]) and the new value
+                     //          as pairs (v[2i], v[2i+1]), fp16
+    uint64_t* part;  // [H][items][hd+2] split attention partials (m, l, o), fp32
+    uint64_t* o;     // [H*hd/2] attention output, fp16 pairs
+    uint64_t* h;     // [max(F, topk*F)/2] SwiGLU output, fp16 pairs
+    uint64_t* r;     // [E] router logits, fp32
+    uint64_t* am;    // [grid][2] per-workgroup argmax value, index
 };
 
 struct DecodeArgs {
     Dims D;
     float eps;
     int items_per_head;
-    uint32_t spin_lds;       // spin limit of LDS waits
-    uint32_t spin_grid;      // spin limit of grid-barrier polls
+    uint32_t spin;           // polls before a device-side wait gives up
     const uint8_t* layers;   // L streaming blocks
     uint64_t layer_bytes;
     const uint8_t* lm;       // LM head block
@@ -42,44 +63,47 @@ struct DecodeArgs {
     const float* rope;       // [max_seq][hd/2][2]
     uint16_t* kc;            // [L][Hkv][max_seq][hd]
     uint16_t* vc;
-    float* x;
-    float* q;
-    uint16_t* o16;
-    uint16_t* h16;
-    float* router;
-    float* attn_part;
-    uint32_t* attn_cnt;
-    float* argmax;           // [grid][2] (value, index bits)
-    uint32_t* bar;
+    Exchange ex;
     uint32_t* status;
     int32_t* out_ids;
     const int32_t* force_ids;
     float* dbg_logits;
     int32_t* dbg_experts;
     const int32_t* plan;     // piece_off[kGrid+1], lm_off[kGrid+1]
+    const uint8_t* idle;     // kIdleBytes of zeros: target of loads that keep a batch slot busy
+    int64_t* trace;          // [kTracePhases][kGrid][4] phase timeline (F_TRACE)
     int32_t pos0;
     int32_t pending;
     int32_t n_steps;
     int32_t flags;
-    uint32_t epoch0;         // barrier epoch before the first barrier of this launch
+    uint32_t id0;            // phase id of this launch's first phase (ids never repeat)
 };
 
 struct GemvArgs {
-    const uint8_t* A;
-    const uint16_t* x;
-    float* y;
-    int32_t M, K, copies;
-    uint32_t spin_lds;
+    const uint8_t* A;      // copies*M rows of K fp16, row stride lda elements
+    const uint16_t* x;     // [K] fp16
+    float* y;              // [copies*M]
+    const uint8_t* idle;   // kIdleBytes of readable memory (streaming variant)
+    int64_t lda;
+    int32_t M, K, copies, accumulate;
 };
 
-// Launchers (defined in kie_kernels.hip). Return the hipError_t of the launch.
-// dev_args: the argument block already copied to device memory.
+// Phases per decode step (used by the host to advance phase ids).
+inline int phases_per_layer(const Dims& D) { return D.E ? 7 : 6; }
+inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2; }
+
+// Launchers. dev_args: the argument block already copied to device memory.
 hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int grid, hipStream_t s);
-hipError_t launch_gemv_ring(const GemvArgs& a, int grid, hipStream_t s);
+// Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
+// per workgroup, whole rows per wave). Needs K <= kMaxInput.
+hipError_t launch_gemv_stream(const GemvArgs& a, int grid, hipStream_t s);
+// Plain GEMV: one wave per 4 rows, all loads of a row block in flight.
 hipError_t launch_gemv_direct(const GemvArgs& a, hipStream_t s);
-hipError_t launch_barrier_probe(uint32_t* bar, uint32_t* status, float* vals, int32_t* errors, int rounds,
+// Inter-workgroup exchange probe. variant 0: fenced grid barrier; variant 1:
+// every workgroup publishes 5 flagged words per round and gathers all of them
+// (the residual exchange of the decode kernel). words: >= 2 * grid * 8 words.
+hipError_t launch_barrier_probe(int variant, uint64_t* words, uint32_t* status, int32_t* errors, int rounds,
                                 int grid, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);
-hipError_t decode_kernel_setup();
 
 }  // namespace kie

@@ -1,0 +1,205 @@
+// kie_probes.hip - measurement kernels behind the kie_*_probe entry points:
+// the weight-streaming GEMV on its own, a plain GEMV for comparison, the
+// inter-workgroup exchange (fenced grid barrier vs. flagged words), and an
+// empty kernel for the launch cost. None of them is on the decode path.
+#include <hip/hip_runtime.h>
+
+#include "kie_common.h"
+#include "kie_device.h"
+#include "kie_kernels.h"
+
+namespace kie {
+
+// Persistent GEMV with the decode kernel's weight streaming: every wave
+// streams whole rows (row r by global wave r mod 2048) through its own LDS
+// ring of kNS batches of kNB units filled by LDS DMA, consumes the oldest
+// batch after vmcnt((kNS-1)*kNB) and refills it at once. x (K <= 8192) is
+// staged in LDS; A has row stride lda; y = A x, or y += A x when accumulate.
+__global__ void __launch_bounds__(512, 1) gemv_stream_kernel(GemvArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[8 * kNS * kBatchBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxInput];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+    const int nwaves = gridDim.x * 8;
+    const int gw = blockIdx.x * 8 + w;
+    for (int i = threadIdx.x; i < a.K / 8; i += blockDim.x)
+        lds_st16((KIE_LDS void*)(xs + 8 * i), *(const uint4*)(a.x + 8 * i));
+    __syncthreads();
+    const long rows_total = (long)a.M * a.copies;
+    const int upr = a.K / kUnitHalves;
+    const long my_rows = rows_total > gw ? (rows_total - gw + nwaves - 1) / nwaves : 0;
+    const long n = my_rows * upr;   // units of this wave
+    const uint32_t ring0 = lds_addr_of((KIE_LDS void*)ring) + (uint32_t)(w * kNS * kBatchBytes);
+    const uint8_t* idle = a.idle + lane * 16;
+    long iu = 0;
+    auto unit_src = [&](long t) {
+        const long row = gw + (t / upr) * (long)nwaves;
+        return a.A + ((size_t)row * a.lda + (size_t)(t % upr) * kUnitHalves) * 2 + lane * 16;
+    };
+    auto fill = [&](uint32_t dst, long* u0, int* cnt) {
+        const long m = n - iu;
+        const int c = m < kNB ? (int)m : kNB;
+        *u0 = iu;
+        *cnt = c;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s)
+            dma_unit(s < c ? unit_src(iu + s) : idle + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+        iu += c;
+    };
+    long su[kNS];
+    int sn[kNS];
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) fill(ring0 + i * kBatchBytes, &su[i], &sn[i]);
+    int head = 0;
+    float acc = 0.f;
+    while (sn[0] > 0) {
+        const uint32_t at = ring0 + head * kBatchBytes;
+        wait_vm<(kNS - 1) * kNB>();
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)at + lane * 16;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) {
+            if (s < sn[0]) {
+                const long t = su[0] + s;
+                const int c = (int)(t % upr);
+                acc = dot8(lds_ld16(wb + s * kUnitBytes), lds_ld16((const KIE_LDS void*)(xs + c * kUnitHalves + lane * 8)),
+                           acc);
+                if (c == upr - 1) {
+                    const float r = wave_sum_to_lane63(acc);
+                    if (lane == 63) {
+                        // stores and no-return atomics only: a load here would make the
+                        // compiler wait for every LDS DMA in flight
+                        float* yp = a.y + gw + (t / upr) * (long)nwaves;
+                        if (a.accumulate)
+                            __hip_atomic_fetch_add(gptr(yp), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else
+                            *gptr(yp) = r;
+                    }
+                    acc = 0.f;
+                }
+            }
+        }
+        wait_lgkm0();
+        long u0;
+        int cnt;
+        fill(at, &u0, &cnt);
+#pragma unroll
+        for (int i = 0; i + 1 < kNS; ++i) {
+            su[i] = su[i + 1];
+            sn[i] = sn[i + 1];
+        }
+        su[kNS - 1] = u0;
+        sn[kNS - 1] = cnt;
+        head = (head + 1 == kNS) ? 0 : head + 1;
+    }
+    wait_vm0();
+}
+
+// A plain many-wave GEMV for comparison: each wave owns 4 rows and keeps all
+// loads of a 4-row x 4-unit block in flight at once.
+__global__ void __launch_bounds__(256) gemv_direct_kernel(GemvArgs a) {
+    const int lane = lane_id();
+    const long wave = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const long rows_total = (long)a.M * a.copies;
+    const long r0 = wave * 4;
+    if (r0 >= rows_total) return;
+    const int upr = a.K / kUnitHalves;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int cc0 = 0; cc0 < upr; cc0 += 4) {
+        uint4 wv[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const long row = r0 + r;
+                const int cc = cc0 + q;
+                if (row < rows_total && cc < upr)
+                    wv[r][q] = ld_nt16(a.A + ((size_t)row * a.lda + (size_t)cc * kUnitHalves + lane * 8) * 2);
+                else
+                    wv[r][q] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int cc = cc0 + q;
+            if (cc < upr) {
+                const uint4 xv = *(const uint4*)(a.x + cc * kUnitHalves + lane * 8);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = dot8(wv[r][q], xv, acc[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float s = wave_sum_to_lane63(acc[r]);
+        const long row = r0 + r;
+        if (lane == 63 && row < rows_total) a.y[row] = a.accumulate ? a.y[row] + s : s;
+    }
+}
+
+// ------------------------------------------------------------ exchange probe
+// variant 0: per round, publish one value with a plain store, fenced grid
+// barrier, read every workgroup's value.
+// variant 1: per round, publish 5 flagged words and gather all 5 x grid words
+// (buffers alternate by round parity, so a workgroup that runs a round ahead
+// cannot overwrite words another one is still reading).
+__global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint64_t* words, uint32_t* status,
+                                                              int32_t* errors, int rounds) {
+    const int wg = blockIdx.x, nwg = gridDim.x, lane = lane_id();
+    int err = 0;
+    for (int r = 1; r <= rounds; ++r) {
+        if (variant == 0) {
+            uint32_t* bar = (uint32_t*)words;
+            uint32_t* vals = (uint32_t*)(words + nwg) + (size_t)(r & 1) * nwg;
+            if (lane == 0) vals[wg] = (uint32_t)(wg * 4096 + r);
+            if (!grid_barrier_fenced(bar, status, nwg, wg, (uint32_t)r, 1u << 22)) {
+                if (lane == 0) atomicAdd(errors, 1000000);
+                return;
+            }
+            for (int i = lane; i < nwg; i += 64)
+                if (vals[i] != (uint32_t)(i * 4096 + r)) ++err;
+        } else {
+            uint64_t* buf = words + (size_t)(r & 1) * 5 * nwg;
+            if (lane < 5) fw_store(buf + 5 * wg + lane, (uint32_t)((wg * 8 + lane) ^ r), (uint32_t)r);
+            const int e = fw_gather(buf, 5 * nwg, (uint32_t)r, 1u << 22, status, [&](int i, uint32_t v) {
+                if (v != (uint32_t)(((i / 5) * 8 + i % 5) ^ r)) ++err;
+            });
+            if (e) {
+                if (lane == 0) {
+                    if (e == 1)
+                        __hip_atomic_store(status, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    atomicAdd(errors, 1000000);
+                }
+                return;
+            }
+        }
+    }
+    for (int off = 32; off; off >>= 1) err += shfl_xor_i(err, off);
+    if (lane == 0 && err) atomicAdd(errors, err);
+}
+
+__global__ void empty_kernel() {}
+
+hipError_t launch_gemv_stream(const GemvArgs& a, int grid, hipStream_t s) {
+    GemvArgs copy = a;
+    void* args[] = {&copy};
+    return hipLaunchCooperativeKernel((const void*)gemv_stream_kernel, dim3(grid), dim3(512), args, 0, s);
+}
+
+hipError_t launch_gemv_direct(const GemvArgs& a, hipStream_t s) {
+    const long waves = ((long)a.M * a.copies + 3) / 4;
+    const long blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL(gemv_direct_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_barrier_probe(int variant, uint64_t* words, uint32_t* status, int32_t* errors, int rounds,
+                                int grid, hipStream_t s) {
+    void* args[] = {&variant, &words, &status, &errors, &rounds};
+    return hipLaunchCooperativeKernel((const void*)barrier_probe_kernel, dim3(grid), dim3(64), args, 0, s);
+}
+
+hipError_t launch_empty(hipStream_t s) {
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+    return hipGetLastError();
+}
+
+}  // namespace kie

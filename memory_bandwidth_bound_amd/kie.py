@@ -33,7 +33,7 @@ class KieConfig(ctypes.Structure):
 
 class KieDebug(ctypes.Structure):
     _fields_ = [("force_ids", POINTER(c_int32)), ("logits", POINTER(c_float)),
-                ("experts", POINTER(c_int32))]
+                ("experts", POINTER(c_int32)), ("trace", POINTER(ctypes.c_int64))]
 
 
 class KieError(RuntimeError):
@@ -52,10 +52,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m memory_bandwidth_bound_amd.build`")
+    # torch ships its own HIP runtime: load it first so that the library binds
+    # to that same runtime instead of a second copy from /opt/rocm
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     sig = {
         "kie_workspace_bytes": (c_size_t, [POINTER(KieConfig)]),
         "kie_tensor_count": (c_int32, [POINTER(KieConfig)]),
+        "kie_phases_per_pass": (c_int32, [POINTER(KieConfig)]),
         "kie_load": (c_int32, [POINTER(KieConfig), POINTER(c_void_p), c_int32, c_void_p, c_size_t,
                                c_void_p, POINTER(c_void_p)]),
         "kie_prefill": (c_int32, [c_void_p, POINTER(c_int32), c_int32, POINTER(c_int32), POINTER(KieDebug)]),
@@ -72,7 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_gemv_probe": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                      c_void_p, POINTER(c_float)]),
         "kie_barrier_probe_bytes": (c_size_t, []),
-        "kie_barrier_probe": (c_int32, [c_void_p, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
+        "kie_barrier_probe": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
         "kie_launch_probe": (c_int32, [c_int32, c_void_p, POINTER(c_float)]),
     }
     for name, (res, args) in sig.items():
@@ -183,6 +187,23 @@ class Model:
         _check(rc, self._h)
         return out, keep.get("logits"), keep.get("experts")
 
+    def trace_decode(self, n: int):
+        """Decode n tokens recording the phase timeline of the launch.
+
+        Returns (ids [n], trace int64 [phases][256][4]) where phases =
+        min(n * phases_per_pass, 2048) and the 4 events per workgroup are the
+        device clock (100 MHz ticks) at phase begin, input gathered, compute
+        waves done, output published."""
+        out = np.zeros(n, dtype=np.int32)
+        pp = int(self._lib.kie_phases_per_pass(ctypes.byref(self._kc)))
+        tr = np.zeros((2048, 256, 4), dtype=np.int64)
+        dbg = KieDebug()
+        dbg.trace = tr.ctypes.data_as(POINTER(ctypes.c_int64))
+        with self._torch.cuda.device(self.device):
+            rc = self._lib.kie_decode(self._h, n, _i32p(out), ctypes.byref(dbg))
+        _check(rc, self._h)
+        return out, tr[:min(n * pp, 2048)]
+
     def set_kv(self, K: np.ndarray, V: np.ndarray, pending: int):
         K = np.ascontiguousarray(K, dtype=np.float16)
         V = np.ascontiguousarray(V, dtype=np.float16)
@@ -247,15 +268,16 @@ def gemv_probe(A, x, variant: int = 0, stream=None):
     return y, float(ms.value)
 
 
-def barrier_probe(rounds: int, device: str = "cuda:0"):
-    """Mean microseconds per grid barrier across the 256-workgroup grid, and
-    the number of rounds whose all-gathered values were wrong."""
+def barrier_probe(rounds: int, variant: int = 1, device: str = "cuda:0"):
+    """Mean microseconds per exchange round across the 256-workgroup grid
+    (variant 0: fenced grid barrier; 1: flagged-word all-gather of 5 words per
+    workgroup), and the count of wrong values (0 when correct)."""
     import torch
     lib = load_library()
     scratch = torch.zeros(int(lib.kie_barrier_probe_bytes()), dtype=torch.uint8, device=device)
     us, err = c_float(), c_int32()
     with torch.cuda.device(scratch.device):
-        rc = lib.kie_barrier_probe(c_void_p(scratch.data_ptr()), rounds,
+        rc = lib.kie_barrier_probe(c_void_p(scratch.data_ptr()), variant, rounds,
                                    _stream_handle(torch, scratch.device, None), ctypes.byref(us),
                                    ctypes.byref(err))
     _check(rc)

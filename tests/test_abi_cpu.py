@@ -100,9 +100,18 @@ def test_probe_argument_errors(lib):
     # K not a multiple of 512
     assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 300, 1, 0, None,
                               ctypes.byref(ms)) == -1
-    # too many rows per workgroup for the ring variant
-    assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 1 << 20, 8192, 1, 0,
+    # K too long
+    assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 65536 + 512, 1, 0,
+                              None, ctypes.byref(ms)) == -1
+    # matrices smaller than the 4 KiB the streaming variant reads for idle batches
+    assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 1, 512, 1, 0,
+                              None, ctypes.byref(ms)) == -1
+    # unknown variant
+    assert lib.kie_gemv_probe(ctypes.c_void_p(1), ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 512, 1, 2,
                               None, ctypes.byref(ms)) == -1
     assert lib.kie_gemv_probe(None, ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 512, 1, 0, None, None) == -1
-    assert lib.kie_barrier_probe(None, 10, None, ctypes.byref(ms), None) == -1
+    err = ctypes.c_int32()
+    assert lib.kie_barrier_probe(None, 1, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
+    assert lib.kie_barrier_probe(ctypes.c_void_p(1), 2, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
+    assert lib.kie_barrier_probe(ctypes.c_void_p(1), 1, 0, None, ctypes.byref(ms), ctypes.byref(err)) == -1
     assert lib.kie_launch_probe(0, None, ctypes.byref(ms)) == -1

@@ -1,4 +1,4 @@
-"""GEMV bandwidth probe, grid-barrier probe and launch probe on the GPU.
+"""GEMV bandwidth probe, inter-workgroup exchange probe and launch probe on the GPU.
 
 Parity: the probe GEMV against the oracle's float64 GEMV within the fp32
 accumulation bound, bit-exact on integer-valued inputs, and x = e_j returns
@@ -82,11 +82,12 @@ def test_gemv_probe_full_shapes_sampled(torch_cuda, si):
     assert ms > 0
 
 
-def test_barrier_probe(torch_cuda):
+@pytest.mark.parametrize("variant", [0, 1])
+def test_barrier_probe(torch_cuda, variant):
     from memory_bandwidth_bound_amd import kie
-    say("barrier probe 20000 rounds")
-    us, err = kie.barrier_probe(20000)
-    say(f"barrier: {us:.3f} us per grid barrier (256 workgroups), errors={err}")
+    say(f"exchange probe variant={variant} 20000 rounds")
+    us, err = kie.barrier_probe(20000, variant=variant)
+    say(f"exchange variant {variant}: {us:.3f} us per round (256 workgroups), errors={err}")
     assert err == 0
     assert 0 < us < 100
 
