@@ -729,7 +729,7 @@ struct Compute {
     PIter cc;          // next phase to enter (or the entered one when `entered`)
     bool entered;
     WaveGeo cg;        // geometry of the phase being consumed
-    int crow, cseg, ccol;   // position of the next unit to consume in it
+    int crow, cseg;    // row and unit-in-row of the next unit to consume in it
     float acc;         // running partial dot product of the current row
 
     __device__ __forceinline__ Compute(const DecodeArgs& args, KIE_LDS Smem* s, int wi) : a(args), S(s), w(wi) {
@@ -742,7 +742,7 @@ struct Compute {
         cc = PIter{0, 0, 0, 0};
         entered = false;
         cg.q = -1;
-        crow = cseg = ccol = 0;
+        crow = cseg = 0;
         acc = 0.f;
         ic = PIter{0, 0, 0, 0};
         seek(false);
@@ -811,18 +811,27 @@ struct Compute {
                 dma_unit(src, dst + s * kUnitBytes);
             }
         } else {
+            // contiguous units: one m0 per four, the instruction offset steps both addresses
+            static_assert(kNB % 4 == 0, "dense batches are issued in fours");
             const uint8_t* base = (kind == K_LM) ? a.lm : a.layers + (size_t)ig.layer * a.layer_bytes;
             const uint8_t* src = base + (size_t)(ig.off + iu) * kUnitBytes + lane * 16;
 #pragma unroll
-            for (int s = 0; s < kNB; ++s)
-                dma_unit((s < n ? src : idle) + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+            for (int g = 0; g < kNB; g += 4) {
+                const uint8_t* sg = src + (size_t)g * kUnitBytes;
+                const uint8_t* ig4 = idle + (size_t)g * kUnitBytes;
+                dma_unit4(g + 0 < n ? sg : ig4, g + 1 < n ? sg : ig4, g + 2 < n ? sg : ig4, g + 3 < n ? sg : ig4,
+                          dst + g * kUnitBytes);
+            }
         }
     }
 
     __device__ __forceinline__ void load_idle(uint32_t dst) {
         const uint8_t* idle = a.idle + lane * 16;
 #pragma unroll
-        for (int s = 0; s < kNB; ++s) dma_unit(idle + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+        for (int g = 0; g < kNB; g += 4) {
+            const uint8_t* ig4 = idle + (size_t)g * kUnitBytes;
+            dma_unit4(ig4, ig4, ig4, ig4, dst + g * kUnitBytes);
+        }
     }
 
     // Refill the batch at dst: the next units in phase order, or an idle batch
@@ -885,49 +894,47 @@ struct Compute {
     }
 
     // consume the batch at LDS address src: all LDS reads of the batch are
-    // issued before the first product
+    // issued before the first product. The input offset of a unit is its
+    // position in its row times 512 (the segments of a MoE down row follow
+    // each other in the input), so the per-unit bookkeeping is one counter.
     __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
         if (cg.q != sl.q) {
             load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
             if (cg.upr) {
                 const int per_row = cg.nseg * cg.upr;
                 crow = cg.lo / per_row;
-                const int rem = cg.lo - crow * per_row;
-                cseg = rem / cg.upr;
-                ccol = rem - cseg * cg.upr;
+                cseg = cg.lo - crow * per_row;   // unit position within the row
             }
         }
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
         uint4 wv[kNB], xv[kNB];
         if (cg.upr) {
-            int seg = cseg, c = ccol;
+            const int per_row = cg.nseg * cg.upr;
+            int rp = cseg;
 #pragma unroll
             for (int s = 0; s < kNB; ++s) {
                 if (s < sl.n) {
                     wv[s] = lds_ld16(wb + s * kUnitBytes);
-                    xv[s] = lds_ld16(S->xin + seg * cg.K + c * kUnitHalves + lane * 8);
-                    if (++c == cg.upr) {
-                        c = 0;
-                        if (++seg == cg.nseg) seg = 0;
-                    }
+                    xv[s] = lds_ld16(S->xin + rp * kUnitHalves + lane * 8);
+                    rp = (rp + 1 == per_row) ? 0 : rp + 1;
                 }
             }
+            const int last = cg.hi - 1 - sl.u0;   // batch index of the range's last unit
 #pragma unroll
             for (int s = 0; s < kNB; ++s) {
                 if (s < sl.n) {
                     acc = dot8(wv[s], xv[s], acc);
-                    const bool row_end = (cseg == cg.nseg - 1 && ccol == cg.upr - 1) || sl.u0 + s == cg.hi - 1;
-                    if (row_end) {
+                    const bool row_done = cseg + 1 == per_row;
+                    if (row_done || s == last) {
                         const float r = wave_sum_to_lane63(acc);
                         if (lane == 63) S->part[crow * kCompute + w] = r;
                         acc = 0.f;
                     }
-                    if (++ccol == cg.upr) {
-                        ccol = 0;
-                        if (++cseg == cg.nseg) {
-                            cseg = 0;
-                            ++crow;
-                        }
+                    if (row_done) {
+                        cseg = 0;
+                        ++crow;
+                    } else {
+                        ++cseg;
                     }
                 }
             }

@@ -68,6 +68,26 @@ __device__ __forceinline__ void dma_unit(const void* gsrc_lane, uint32_t lds_add
         : "v"(gsrc_lane), "s"(lds_addr)
         : "memory");
 }
+// Four units with one m0: unit s goes from p_s + 1024 s (+ 16 lane) to LDS
+// lds_addr + 1024 s (+ 16 lane) - the instruction offset applies to both
+// addresses. Same rules as dma_unit.
+__device__ __forceinline__ void dma_unit4(const void* p0, const void* p1, const void* p2, const void* p3,
+                                          uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "global_load_lds_dwordx4 %2, off offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %3, off offset:2048 nt\n\t"
+        "global_load_lds_dwordx4 %4, off offset:3072 nt\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "s"(lds_addr)
+        : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr_of(const KIE_LDS void* p) { return (uint32_t)(uintptr_t)p; }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
