@@ -167,6 +167,7 @@ class Decoder:
         self.pos = 0
         self.pending: Optional[int] = None
         self.last_experts: List[np.ndarray] = []
+        self.last_router: List[np.ndarray] = []   # MoE: router logits per layer of the last pass
 
     # ---- weights ---------------------------------------------------------
     def _build_index(self) -> Dict[str, int]:
@@ -206,13 +207,33 @@ class Decoder:
         self.pos = n
         self.pending = int(pending_token)
 
+    def _moe_rows(self, l: int, Hn: np.ndarray) -> np.ndarray:
+        """The MoE FFN of every row of Hn: row t gets sum over its top-k experts
+        e of pi_te * FFN_e(h_t), with pi_t the softmax of its router logits.
+        Rows are grouped by expert so each expert's matrices are read once."""
+        cfg = self.cfg
+        probs = softmax(Hn @ self.w(f"l{l}.Wr").T)                    # [T, E]
+        sel = np.stack([topk_experts(p, cfg.top_k) for p in probs])   # [T, k]
+        Y = np.zeros_like(Hn)
+        for e in range(cfg.n_experts):
+            rows = np.nonzero((sel == e).any(axis=1))[0]
+            if rows.size == 0:
+                continue
+            Hs = Hn[rows]
+            G = Hs @ self.w(f"l{l}.e{e}.Wg").T
+            U = Hs @ self.w(f"l{l}.e{e}.Wu").T
+            Y[rows] += probs[rows, e:e + 1] * ((silu(G) * U) @ self.w(f"l{l}.e{e}.Wd").T)
+        return Y
+
     # ---- one pass ----------------------------------------------------------
     def _ffn(self, l: int, h: np.ndarray,
              override: Optional[np.ndarray]) -> Tuple[np.ndarray, Optional[np.ndarray]]:
         cfg = self.cfg
         if not cfg.n_experts:
             return swiglu_ffn(h, self.w(f"l{l}.Wg"), self.w(f"l{l}.Wu"), self.w(f"l{l}.Wd")), None
-        probs = softmax(self.w(f"l{l}.Wr") @ h)
+        logits = self.w(f"l{l}.Wr") @ h
+        self.last_router.append(logits)
+        probs = softmax(logits)
         sel = topk_experts(probs, cfg.top_k) if override is None else np.asarray(override)
         out = np.zeros(cfg.d_model, dtype=self.dtype)
         for e in sel:
@@ -233,6 +254,7 @@ class Decoder:
         cos, sin = rope_angles([p], hd, cfg.rope_theta)
         x = self.w("E")[token].copy()
         experts = []
+        self.last_router = []
         for l in range(cfg.n_layers):
             h = rmsnorm(x, self.w(f"l{l}.g_attn"), cfg.rms_eps)
             q = (self.w(f"l{l}.Wq") @ h).reshape(H, hd)
@@ -327,7 +349,7 @@ class Decoder:
             X = X + O.reshape(T, H * hd) @ self.w(f"l{l}.Wo").T
             Hn = rmsnorm(X, self.w(f"l{l}.g_ffn"), cfg.rms_eps)
             if cfg.n_experts:
-                Y = np.stack([self._ffn(l, Hn[t], None)[0] for t in range(T)])
+                Y = self._moe_rows(l, Hn)
             else:
                 G = Hn @ self.w(f"l{l}.Wg").T
                 U = Hn @ self.w(f"l{l}.Wu").T

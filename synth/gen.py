@@ -9,7 +9,7 @@ even).
 Stream ids: tensor i of the canonical order -> i; prompt -> 1000; pre-filled
 K/V of layer l -> (2000, l, 0|1); first pending token after a pre-filled
 cache -> 3000; GEMV probe shape s -> (4000 + s, 0) for the matrix and
-(4000 + s, 1) for the vector.
+(4000 + s, 1) for the vector; teacher-forcing token stream -> 5000.
 """
 from __future__ import annotations
 
@@ -26,6 +26,7 @@ PROMPT_STREAM = 1000
 KV_STREAM = 2000
 PENDING_STREAM = 3000
 PROBE_STREAM = 4000
+FORCE_STREAM = 5000
 
 
 def _workers() -> int:
@@ -68,6 +69,13 @@ def make_pending_token(cfg: DecoderConfig) -> int:
     """The first decode input after a pre-filled KV cache (uniform over the vocab)."""
     rng = np.random.default_rng([cfg.seed, PENDING_STREAM])
     return int(rng.integers(0, cfg.vocab))
+
+
+def make_forced_tokens(cfg: DecoderConfig, n: int) -> np.ndarray:
+    """n token ids, uniform over the vocabulary, int32: inputs for teacher-forced
+    decoding (pass i+1 is fed token i whatever pass i produced)."""
+    rng = np.random.default_rng([cfg.seed, FORCE_STREAM])
+    return rng.integers(0, cfg.vocab, size=n, dtype=np.int64).astype(np.int32)
 
 
 def make_kv_prefill(cfg: DecoderConfig, n_pos: int | None = None) -> Tuple[np.ndarray, np.ndarray]:

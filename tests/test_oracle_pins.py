@@ -322,8 +322,9 @@ def test_decoder_matches_scalar_brute_force(kw):
     np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
 
 
-def test_decoder_incremental_equals_full_causal():
-    cfg = _tiny(n_layers=3, vocab=50)
+@pytest.mark.parametrize("kw", [dict(), dict(n_experts=6, top_k=3, ffn_dim=6)])
+def test_decoder_incremental_equals_full_causal(kw):
+    cfg = _tiny(n_layers=3, vocab=50, **kw)
     W = make_weights(cfg)
     toks = [int(t) for t in np.random.default_rng(10).integers(0, cfg.vocab, 9)]
     dec = oracle.Decoder(cfg, W, dtype=np.float64)
