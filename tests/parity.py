@@ -28,3 +28,83 @@ def gemv_bound(A, x):
     |err_i| <= K * 2^-23 * sum_k |a_ik x_k| (fp16 x fp16 products are exact in fp32)."""
     K = A.shape[-1]
     return K * 2.0 ** -23 * (np.abs(A.astype(np.float64)) @ np.abs(x.astype(np.float64))) + 1e-30
+
+
+ROUTE_TOL = 2e-2   # z-scored router-logit margin below which either expert is a valid choice
+
+
+def routing_agrees(dev_sel, router_logits, k, tol=ROUTE_TOL, label=""):
+    """Check one pass's device routing against the oracle's router logits.
+
+    dev_sel [L][k]: experts the device chose; router_logits [L][E]: oracle.
+    Every layer's choice must be a valid top-k: k distinct in-range experts,
+    none of them below an unchosen one by more than tol (in units of the
+    layer's logit spread). Returns True when every layer chose exactly the
+    oracle's top-k set, False when some layer differs only inside a near tie.
+    """
+    same = True
+    for l, (sel, r) in enumerate(zip(dev_sel, router_logits)):
+        r = np.asarray(r, dtype=np.float64)
+        sel = np.asarray(sel, dtype=np.int64)
+        assert sel.min() >= 0 and sel.max() < len(r), f"{label} layer {l}: expert out of range {sel}"
+        assert len(set(sel.tolist())) == k, f"{label} layer {l}: repeated expert {sel}"
+        rest = np.setdiff1d(np.arange(len(r)), sel)
+        sd = r.std()
+        if rest.size:
+            worst = (r[rest].max() - r[sel].min()) / sd
+            assert worst <= tol, f"{label} layer {l}: experts {sel} are not a top-{k} (margin {worst:.3e})"
+        want = set(oracle.topk_experts(oracle.softmax(r), k).tolist())
+        if set(sel.tolist()) != want:
+            say(f"[{label}] layer {l}: near tie, device {sorted(sel.tolist())} vs oracle {sorted(want)}, "
+                f"margin {worst:.2e}")
+            same = False
+    return same
+
+
+def moe_request_parity(m, cfg, W, P, n, n_compare, label):
+    """MoE parity of one device model `m` (freshly loaded) against the oracle.
+
+    1. The prompt: every pass's routing must be a valid top-k of the oracle's
+       router logits; the last logits are compared when no pass hit a near tie.
+    2. From a seeded cache of len(P) positions that both sides store exactly,
+       n teacher-forced passes as ONE launch; the same passes split over debug
+       launches must give the same ids bit for bit, each id must be the argmax
+       of its own logits row, and the first n_compare passes are compared with
+       the oracle element by element until the first near tie in routing.
+    Returns the number of passes compared in step 2.
+    """
+    import synth
+    ref = oracle.Decoder(cfg, W)
+    say(f"{label}: oracle batched prefill of {len(P)} tokens")
+    first, last = ref.prefill_batched(P)
+    routes = ref.full_router
+    g_first, g_logits, g_exp = m.prefill(P, logits=True, experts=True)
+    same = [routing_agrees(g_exp[i], [r[i] for r in routes], cfg.top_k, label=f"{label} prompt {i}")
+            for i in range(len(P))]
+    if all(same):
+        check_rows(g_logits[-1:], last[None], label=f"{label} prefill")
+        if oracle.top2_gap(last) > TOL:
+            assert g_first == first
+    else:
+        say(f"{label}: near tie in the prompt's routing; its last logits are not compared")
+    del ref
+    K, V = synth.make_kv_prefill(cfg, n_pos=len(P))
+    F = synth.make_forced_tokens(cfg, n + 1)
+    dec = oracle.Decoder(cfg, W, cache_experts=True)
+    dec.set_kv(K, V, int(F[0]))
+    m.set_kv(K, V, int(F[0]))
+    say(f"{label}: one teacher-forced launch of {n} passes, then the same passes with debug output")
+    g_ids, _, _ = m.decode(n, force=F[1:])
+    m.rewind(len(P), int(F[0]))
+    c_ids, c_rows, c_exp = m.decode(n, force=F[1:], logits=True, experts=True)
+    assert np.array_equal(g_ids, c_ids)
+    assert np.array_equal(c_ids, np.argmax(c_rows, axis=1))
+    done = 0
+    for i in range(min(n, n_compare)):
+        row = dec.step(int(F[i]))
+        if not routing_agrees(c_exp[i], dec.last_router, cfg.top_k, label=f"{label} pass {i}"):
+            break
+        check_rows(c_rows[i:i + 1], row[None], label=f"{label} pass {i}")
+        done += 1
+    say(f"{label}: {done}/{min(n, n_compare)} passes compared")
+    return done

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from tests.parity import check_rows, say
+from tests.parity import check_rows, moe_request_parity, say
 
 pytestmark = pytest.mark.gpu
 
@@ -156,3 +156,30 @@ def test_capacity_and_state_errors(torch_cuda):
         m.prefill(np.array([cfg.vocab], dtype=np.int32))
     assert e.value.code == -1
     m.close()
+
+
+# ---- MoE -----------------------------------------------------------------------
+MOE_CASES = {
+    # 8 experts, top-2, head_dim 128
+    "moe_e8k2": synth.DecoderConfig(name="moe_e8k2", n_layers=2, d_model=512, n_heads=4, n_kv_heads=2,
+                                    head_dim=128, ffn_dim=512, vocab=3000, n_experts=8, top_k=2,
+                                    prompt_len=10, decode_steps=16),
+    # 64 experts, top-8 (the gathered down input is 8192 wide), head_dim 64
+    "moe_e64k8": synth.DecoderConfig(name="moe_e64k8", n_layers=3, d_model=1024, n_heads=8, n_kv_heads=2,
+                                     head_dim=64, ffn_dim=1024, vocab=5000, n_experts=64, top_k=8,
+                                     prompt_len=8, decode_steps=12),
+}
+
+
+@pytest.mark.parametrize("name", list(MOE_CASES))
+def test_moe_teacher_forced_parity(torch_cuda, name):
+    cfg = MOE_CASES[name]
+    say(f"case {name}: {cfg}")
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    m = _model(cfg, W)
+    try:
+        done = moe_request_parity(m, cfg, W, P, cfg.decode_steps, cfg.decode_steps, name)
+    finally:
+        m.close()
+    assert done >= 4
