@@ -269,7 +269,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         static_assert(KIE_TRACE_PHASES == kTracePhases, "trace length");
         HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
         HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
-        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, kGrid, m->stream));
+        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, skip_lm, kGrid, m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
         HIP_TRY(m, hipEventSynchronize(m->ev1));
         HIP_TRY(m, hipEventElapsedTime(&m->last_ms, m->ev0, m->ev1));

@@ -158,8 +158,9 @@ struct Smem {
     // per compute wave: kNS batches of kNB weight units, written by LDS DMA
     alignas(16) uint8_t ring[kCompute * kNS * kBatchBytes];
     union {
-        struct {                                // GEMV phases
-            alignas(16) uint16_t xin[kMaxIn];   // fp16 input of the current phase
+        struct {                                // GEMV phases: the input as two fp16 terms,
+            alignas(16) uint16_t xin[kMaxIn];   // hi = fp16(v)
+            alignas(16) uint16_t xlo[kMaxIn];   // lo = fp16(v - hi)
             float part[kMaxRowsWg * kCompute];  // per (row, compute wave) partial dot products
         };
         float att_o[kCompute * kMaxGroup * 128];   // attention: per compute wave, unnormalised o
@@ -239,11 +240,25 @@ struct Comm {
         return r == 0;
     }
 
-    // xin = fp16(v * rsqrt(mean(v^2) + eps)) for the d-vector v, given as
-    // flagged fp16 pairs or (first layer) as the token's embedding row.
+    // Stage v in LDS as two fp16 terms: xin = fp16(v), xlo = fp16(v - xin).
+    // A GEMV sums the products with both, so its input keeps about 22
+    // significant bits while every product is a v_dot2 of fp16 pairs.
+    __device__ __forceinline__ void put1(int i, float v) {
+        const _Float16 hi = (_Float16)v;
+        S->xin[i] = __builtin_bit_cast(uint16_t, hi);
+        S->xlo[i] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi));
+    }
+    __device__ __forceinline__ void put2(int i, float v0, float v1) {
+        const uint32_t hi = pack_h2(v0, v1);
+        const float r0 = v0 - h2f_bits((uint16_t)hi), r1 = v1 - h2f_bits((uint16_t)(hi >> 16));
+        ((KIE_LDS uint32_t*)S->xin)[i] = hi;
+        ((KIE_LDS uint32_t*)S->xlo)[i] = pack_h2(r0, r1);
+    }
+
+    // the d-vector v * rsqrt(mean(v^2) + eps), for v given as flagged fp32
+    // words or (first layer) as the token's embedding row
     __device__ __forceinline__ void input_norm(const uint64_t* xw, uint32_t id, const uint16_t* emb_row) {
         const int d = a.D.d;
-        KIE_LDS uint32_t* xi = (KIE_LDS uint32_t*)S->xin;
         float ss = 0.f;
         if (emb_row) {
             const KIE_GLOBAL uint32_t* e = (const KIE_GLOBAL uint32_t*)gptr(emb_row);
@@ -251,27 +266,31 @@ struct Comm {
                 const uint32_t v = e[i];
                 const float x0 = h2f_bits((uint16_t)v), x1 = h2f_bits((uint16_t)(v >> 16));
                 ss += x0 * x0 + x1 * x1;
-                xi[i] = v;
+                put2(i, x0, x1);
             }
         } else {
-            const bool ok = gather(xw, d / 2, id, [&](int i, uint32_t v) {
-                const float x0 = h2f_bits((uint16_t)v), x1 = h2f_bits((uint16_t)(v >> 16));
-                ss += x0 * x0 + x1 * x1;
-                xi[i] = v;
+            const bool ok = gather(xw, d, id, [&](int i, uint32_t v) {
+                const float x = __builtin_bit_cast(float, v);
+                ss += x * x;
+                put1(i, x);
             });
             if (!ok) return;
         }
         ss = wave_sum(ss);
         const float s = 1.0f / sqrtf(ss / (float)d + a.eps);
+        const KIE_LDS uint32_t* hi = (const KIE_LDS uint32_t*)S->xin;
+        const KIE_LDS uint32_t* lo = (const KIE_LDS uint32_t*)S->xlo;
         for (int i = lane; i < d / 2; i += 64) {
-            const uint32_t v = xi[i];
-            xi[i] = pack_h2(h2f_bits((uint16_t)v) * s, h2f_bits((uint16_t)(v >> 16)) * s);
+            const uint32_t h = hi[i], l = lo[i];
+            const float x0 = h2f_bits((uint16_t)h) + h2f_bits((uint16_t)l);
+            const float x1 = h2f_bits((uint16_t)(h >> 16)) + h2f_bits((uint16_t)(l >> 16));
+            put2(i, x0 * s, x1 * s);
         }
     }
 
-    __device__ __forceinline__ void input_pairs(const uint64_t* src, int npairs, uint32_t id) {
-        KIE_LDS uint32_t* xi = (KIE_LDS uint32_t*)S->xin;
-        gather(src, npairs, id, [&](int i, uint32_t v) { xi[i] = v; });
+    // n values given as flagged fp32 words, staged as they are
+    __device__ __forceinline__ void input_split(const uint64_t* src, int n, uint32_t id) {
+        gather(src, n, id, [&](int i, uint32_t v) { put1(i, __builtin_bit_cast(float, v)); });
     }
 
     __device__ __forceinline__ void zero_part(int nrows) {
@@ -292,7 +311,8 @@ struct Comm {
             const float x1 = S->own_x[j + 1] + rowsum(j + 1);
             S->own_x[j] = x0;
             S->own_x[j + 1] = x1;
-            fw_store(a.ex.x + (W.wo0 + j) / 2, pack_h2(x0, x1), id);
+            fw_store(a.ex.x + W.wo0 + j, __builtin_bit_cast(uint32_t, x0), id);
+            fw_store(a.ex.x + W.wo0 + j + 1, __builtin_bit_cast(uint32_t, x1), id);
         }
     }
 
@@ -369,7 +389,7 @@ struct Comm {
         }
         case K_WO:
             zero_part(W.won);
-            if (W.nwo) input_pairs(a.ex.o, D.H * HD / 2, id_of(q - 1));
+            if (W.nwo) input_split(a.ex.o, D.H * HD, id_of(q - 1));
             break;
         case K_GU:
             zero_part(W.gun);
@@ -377,7 +397,7 @@ struct Comm {
             break;
         case K_DOWN:
             zero_part(W.won);
-            if (W.nd) input_pairs(a.ex.h, D.F / 2, id_of(q - 1));
+            if (W.nd) input_split(a.ex.h, D.F, id_of(q - 1));
             break;
         case K_ROUTER:
             zero_part(W.rn);
@@ -389,7 +409,7 @@ struct Comm {
             break;
         case K_EDOWN:
             zero_part(W.won);
-            if (W.ned) input_pairs(a.ex.h, D.topk * D.F / 2, id_of(q - 1));
+            if (W.ned) input_split(a.ex.h, D.topk * D.F, id_of(q - 1));
             break;
         case K_LM:
             zero_part(W.lmn);
@@ -474,7 +494,8 @@ struct Comm {
                 const int head = g * Gq + j;
                 if (nper == 1) {
                     // the whole row is here: publish o under the combine phase's id
-                    fw_store(a.ex.o + (head * HD + dd) / 2, pack_h2(O0 / L, O1 / L), id + 1);
+                    fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, O0 / L), id + 1);
+                    fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, O1 / L), id + 1);
                 } else {
                     uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + chunk) * (HD + 2);
                     fw_store(pp + 2 + dd, __builtin_bit_cast(uint32_t, O0), id);
@@ -501,7 +522,9 @@ struct Comm {
                     const float gv = rowsum(4 * j + 2 * e), uv = rowsum(4 * j + 2 * e + 1);
                     h[e] = gv / (1.0f + __expf(-gv)) * uv;
                 }
-                fw_store(a.ex.h + (W.gu0 / 4 + j), pack_h2(h[0], h[1]), id);
+                const int m = W.gu0 / 2 + 2 * j;
+                fw_store(a.ex.h + m, __builtin_bit_cast(uint32_t, h[0]), id);
+                fw_store(a.ex.h + m + 1, __builtin_bit_cast(uint32_t, h[1]), id);
             }
             break;
         case K_ROUTER:
@@ -518,7 +541,8 @@ struct Comm {
                     const float gv = rowsum(4 * j + 2 * e), uv = rowsum(4 * j + 2 * e + 1);
                     h[e] = S->pi[k] * (gv / (1.0f + __expf(-gv))) * uv;
                 }
-                fw_store(a.ex.h + (k * D.F + m) / 2, pack_h2(h[0], h[1]), id);
+                fw_store(a.ex.h + k * D.F + m, __builtin_bit_cast(uint32_t, h[0]), id);
+                fw_store(a.ex.h + k * D.F + m + 1, __builtin_bit_cast(uint32_t, h[1]), id);
             }
             break;
         case K_LM: {
@@ -658,7 +682,8 @@ struct Comm {
                 m = M;
             }
             const int idx = 2 * (p0 + j), head = g * Gq + idx / HD, dd = idx % HD;
-            fw_store(a.ex.o + (head * HD + dd) / 2, pack_h2(o0 / l, o1 / l), id_of(q));
+            fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, o0 / l), id_of(q));
+            fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, o1 / l), id_of(q));
         }
     }
 
@@ -907,7 +932,7 @@ struct Compute {
             }
         }
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
-        uint4 wv[kNB], xv[kNB];
+        uint4 wv[kNB], xv[kNB], xl[kNB];
         if (cg.upr) {
             const int per_row = cg.nseg * cg.upr;
             int rp = cseg;
@@ -916,6 +941,7 @@ struct Compute {
                 if (s < sl.n) {
                     wv[s] = lds_ld16(wb + s * kUnitBytes);
                     xv[s] = lds_ld16(S->xin + rp * kUnitHalves + lane * 8);
+                    xl[s] = lds_ld16(S->xlo + rp * kUnitHalves + lane * 8);
                     rp = (rp + 1 == per_row) ? 0 : rp + 1;
                 }
             }
@@ -923,7 +949,7 @@ struct Compute {
 #pragma unroll
             for (int s = 0; s < kNB; ++s) {
                 if (s < sl.n) {
-                    acc = dot8(wv[s], xv[s], acc);
+                    acc = dot8(wv[s], xl[s], dot8(wv[s], xv[s], acc));
                     const bool row_done = cseg + 1 == per_row;
                     if (row_done || s == last) {
                         const float r = wave_sum_to_lane63(acc);
@@ -941,13 +967,14 @@ struct Compute {
         } else {
             // 256-wide rows: one unit holds two rows (lanes 0-31 and 32-63)
             const uint4 x = lds_ld16(S->xin + (lane & 31) * 8);
+            const uint4 xlo = lds_ld16(S->xlo + (lane & 31) * 8);
 #pragma unroll
             for (int s = 0; s < kNB; ++s)
                 if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
 #pragma unroll
             for (int s = 0; s < kNB; ++s) {
                 if (s < sl.n) {
-                    const float r = half32_sum_from_rows(row16_sum(dot8(wv[s], x, 0.f)));
+                    const float r = half32_sum_from_rows(row16_sum(dot8(wv[s], xlo, dot8(wv[s], x, 0.f))));
                     const int row = 2 * (sl.u0 + s) + (lane >> 5);
                     if ((lane & 31) == 31 && row < cg.nrows) S->part[row * kCompute + w] = r;
                 }
@@ -1113,10 +1140,7 @@ struct Compute {
 };
 
 template <int HD>
-__global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
-    __shared__ Smem smem_;
-    KIE_LDS Smem* S = (KIE_LDS Smem*)&smem_;
-    const DecodeArgs& a = *ap;
+__device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WgPlan W;
     if (wave == 0) {
@@ -1136,9 +1160,27 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* _
     }
 }
 
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int grid, hipStream_t s) {
+// Two symbols for the same code, so that profiles keep the prompt's passes
+// apart from the generation requests.
+template <int HD>
+__global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
+    __shared__ Smem smem_;
+    kernel_body<HD>(*ap, (KIE_LDS Smem*)&smem_);
+}
+
+template <int HD>
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const DecodeArgs* __restrict__ ap) {
+    __shared__ Smem smem_;
+    kernel_body<HD>(*ap, (KIE_LDS Smem*)&smem_);
+}
+
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool prefill, int grid, hipStream_t s) {
     void* args[] = {&dev_args};
-    const void* fn = hd == 64 ? (const void*)decode_kernel<64> : (const void*)decode_kernel<128>;
+    const void* fn;
+    if (prefill)
+        fn = hd == 64 ? (const void*)prefill_kernel<64> : (const void*)prefill_kernel<128>;
+    else
+        fn = hd == 64 ? (const void*)decode_kernel<64> : (const void*)decode_kernel<128>;
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 

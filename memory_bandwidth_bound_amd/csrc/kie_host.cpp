@@ -131,12 +131,12 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.kv_bytes = (size_t)D.L * D.Hkv * D.max_seq * D.hd * 2;
     Y.off_k = take(Y.kv_bytes);
     Y.off_v = take(Y.kv_bytes);
-    Y.off_ex_x = take((size_t)D.d / 2 * 8);
+    Y.off_ex_x = take((size_t)D.d * 8);
     Y.off_ex_qkv = take((size_t)(D.H + D.Hkv) * D.hd * 8);
     Y.off_ex_part = take((size_t)D.H * Y.attn_items_per_head * (D.hd + 2) * 8);
-    Y.off_ex_o = take((size_t)D.H * D.hd / 2 * 8);
+    Y.off_ex_o = take((size_t)D.H * D.hd * 8);
     size_t hlen = D.E ? (size_t)D.topk * D.F : (size_t)D.F;
-    Y.off_ex_h = take(hlen / 2 * 8);
+    Y.off_ex_h = take(hlen * 8);
     Y.off_ex_r = take((size_t)(D.E ? D.E : 1) * 8);
     Y.off_ex_am = take((size_t)kGrid * 2 * 8);
     Y.ex_bytes = off - Y.off_ex_x;

@@ -37,14 +37,14 @@ enum : int {
 
 // Flagged-word exchange buffers (64-bit words: phase id << 32 | payload).
 struct Exchange {
-    uint64_t* x;     // [d/2]    residual after Wo / down, fp16 pairs
+    uint64_t* x;     // [d]      residual after Wo / down, fp32
     uint64_t* qkv;   // [Hkv][(G+1)*hd] per KV group (G query heads): the group's
                      //          rotated queries (fp32), then the new key as
                      //          rotary pairs (k[i], k[i+hd/2]) and the new value
                      //          as pairs (v[2i], v[2i+1]), fp16
     uint64_t* part;  // [H][items][hd+2] split attention partials (m, l, o), fp32
-    uint64_t* o;     // [H*hd/2] attention output, fp16 pairs
-    uint64_t* h;     // [max(F, topk*F)/2] SwiGLU output, fp16 pairs
+    uint64_t* o;     // [H*hd]   attention output, fp32
+    uint64_t* h;     // [F or topk*F] SwiGLU output (MoE: times pi), fp32
     uint64_t* r;     // [E] router logits, fp32
     uint64_t* am;    // [grid][2] per-workgroup argmax value, index
 };
@@ -93,7 +93,7 @@ inline int phases_per_layer(const Dims& D) { return D.E ? 7 : 6; }
 inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2; }
 
 // Launchers. dev_args: the argument block already copied to device memory.
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int grid, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool prefill, int grid, hipStream_t s);
 // Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
 // per workgroup, whole rows per wave). Needs K <= kMaxInput.
 hipError_t launch_gemv_stream(const GemvArgs& a, int grid, hipStream_t s);

@@ -154,20 +154,25 @@ class Decoder:
     """
 
     def __init__(self, cfg, tensors: List[np.ndarray], dtype=np.float32,
-                 cache_experts: bool = False):
+                 cache_experts: bool = False, kv_dtype=np.float16):
         self.cfg = cfg
         self.dtype = np.dtype(dtype)
+        # The KV cache holds fp16 keys and values: each k, v is rounded to
+        # fp16 when it is stored and read back exactly. kv_dtype=None keeps
+        # the compute precision instead.
+        self.kv_dtype = self.dtype if kv_dtype is None else np.dtype(kv_dtype)
         self._raw = tensors
         self._cache_experts = cache_experts
         self._conv: Dict[int, np.ndarray] = {}
         self._index = self._build_index()
         L, S, Hkv, hd = cfg.n_layers, cfg.max_seq, cfg.n_kv_heads, cfg.head_dim
-        self.K = np.zeros((L, S, Hkv, hd), dtype=self.dtype)
-        self.V = np.zeros((L, S, Hkv, hd), dtype=self.dtype)
+        self.K = np.zeros((L, S, Hkv, hd), dtype=self.kv_dtype)
+        self.V = np.zeros((L, S, Hkv, hd), dtype=self.kv_dtype)
         self.pos = 0
         self.pending: Optional[int] = None
         self.last_experts: List[np.ndarray] = []
         self.last_router: List[np.ndarray] = []   # MoE: router logits per layer of the last pass
+        self.full_router: List[np.ndarray] = []   # MoE: per layer [T, E], of the last full forward
 
     # ---- weights ---------------------------------------------------------
     def _build_index(self) -> Dict[str, int]:
@@ -200,8 +205,8 @@ class Decoder:
     def set_kv(self, K: np.ndarray, V: np.ndarray, pending_token: int) -> None:
         """Store already-rotated keys and values at positions 0..n-1."""
         n = K.shape[1]
-        self.K[:, :n] = K.astype(self.dtype)
-        self.V[:, :n] = V.astype(self.dtype)
+        self.K[:, :n] = K.astype(self.kv_dtype)
+        self.V[:, :n] = V.astype(self.kv_dtype)
         self.K[:, n:] = 0
         self.V[:, n:] = 0
         self.pos = n
@@ -212,7 +217,9 @@ class Decoder:
         e of pi_te * FFN_e(h_t), with pi_t the softmax of its router logits.
         Rows are grouped by expert so each expert's matrices are read once."""
         cfg = self.cfg
-        probs = softmax(Hn @ self.w(f"l{l}.Wr").T)                    # [T, E]
+        logits = Hn @ self.w(f"l{l}.Wr").T                            # [T, E]
+        self.full_router.append(logits)
+        probs = softmax(logits)
         sel = np.stack([topk_experts(p, cfg.top_k) for p in probs])   # [T, k]
         Y = np.zeros_like(Hn)
         for e in range(cfg.n_experts):
@@ -264,7 +271,7 @@ class Decoder:
             k = apply_rope(k, cos, sin)
             self.K[l, p] = k
             self.V[l, p] = v
-            o = attention_decode(q, self.K[l, :p + 1], self.V[l, :p + 1])
+            o = attention_decode(q, self.K[l, :p + 1].astype(dt), self.V[l, :p + 1].astype(dt))
             x = x + self.w(f"l{l}.Wo") @ o.reshape(-1)
             h = rmsnorm(x, self.w(f"l{l}.g_ffn"), cfg.rms_eps)
             ov = None if expert_override is None else expert_override[l]
@@ -330,6 +337,7 @@ class Decoder:
         cos, sin = rope_angles(np.arange(T), hd, cfg.rope_theta)   # [T, hd/2]
         X = self.w("E")[np.asarray(tokens)].astype(dt)              # [T, d]
         mask = np.triu(np.ones((T, T), dtype=bool), k=1)            # True above diagonal
+        self.full_router = []   # MoE: router logits [T, E] per layer
         for l in range(cfg.n_layers):
             Hn = rmsnorm(X, self.w(f"l{l}.g_attn"), cfg.rms_eps)
             Q = (Hn @ self.w(f"l{l}.Wq").T).reshape(T, H, hd)
@@ -337,6 +345,8 @@ class Decoder:
             Vf = (Hn @ self.w(f"l{l}.Wv").T).reshape(T, Hkv, hd)
             Q = apply_rope(Q, cos[:, None, :], sin[:, None, :])
             Kf = apply_rope(Kf, cos[:, None, :], sin[:, None, :])
+            Kf = Kf.astype(self.kv_dtype).astype(dt)   # attention reads what the cache holds
+            Vf = Vf.astype(self.kv_dtype).astype(dt)
             if store_kv:
                 self.K[l, :T] = Kf
                 self.V[l, :T] = Vf

@@ -40,7 +40,9 @@ def routing_agrees(dev_sel, router_logits, k, tol=ROUTE_TOL, label=""):
     Every layer's choice must be a valid top-k: k distinct in-range experts,
     none of them below an unchosen one by more than tol (in units of the
     layer's logit spread). Returns True when every layer chose exactly the
-    oracle's top-k set, False when some layer differs only inside a near tie.
+    oracle's top-k set, False when some layer differs only inside a near tie;
+    the layers after such a layer are not checked, since from there on the two
+    sides legitimately compute from different states.
     """
     same = True
     for l, (sel, r) in enumerate(zip(dev_sel, router_logits)):
@@ -57,21 +59,25 @@ def routing_agrees(dev_sel, router_logits, k, tol=ROUTE_TOL, label=""):
         if set(sel.tolist()) != want:
             say(f"[{label}] layer {l}: near tie, device {sorted(sel.tolist())} vs oracle {sorted(want)}, "
                 f"margin {worst:.2e}")
-            same = False
+            return False
     return same
 
 
-def moe_request_parity(m, cfg, W, P, n, n_compare, label):
+def moe_request_parity(m, cfg, W, P, n, trials, label):
     """MoE parity of one device model `m` (freshly loaded) against the oracle.
 
     1. The prompt: every pass's routing must be a valid top-k of the oracle's
        router logits; the last logits are compared when no pass hit a near tie.
-    2. From a seeded cache of len(P) positions that both sides store exactly,
-       n teacher-forced passes as ONE launch; the same passes split over debug
-       launches must give the same ids bit for bit, each id must be the argmax
-       of its own logits row, and the first n_compare passes are compared with
-       the oracle element by element until the first near tie in routing.
-    Returns the number of passes compared in step 2.
+    2. Trials from a seeded cache of len(P) positions that both sides store
+       exactly: trial t feeds forced token t, then t+1 (two passes in one
+       launch); logits are compared element by element up to the first near
+       tie in routing.
+    3. The request: n teacher-forced passes as ONE launch; the same passes
+       split over debug launches must give the same ids bit for bit, each id
+       must be the argmax of its own logits row and every pass's routing a
+       valid top-k; the leading passes are compared with the oracle until the
+       first near tie.
+    Returns the number of passes compared with the oracle in steps 2 and 3.
     """
     import synth
     ref = oracle.Decoder(cfg, W)
@@ -91,20 +97,34 @@ def moe_request_parity(m, cfg, W, P, n, n_compare, label):
     K, V = synth.make_kv_prefill(cfg, n_pos=len(P))
     F = synth.make_forced_tokens(cfg, n + 1)
     dec = oracle.Decoder(cfg, W, cache_experts=True)
-    dec.set_kv(K, V, int(F[0]))
-    m.set_kv(K, V, int(F[0]))
+    compared = 0
+
+    def follow(dev_rows, dev_exp, tokens, tag):
+        nonlocal compared
+        for i, tok in enumerate(tokens):
+            row = dec.step(int(tok))
+            if not routing_agrees(dev_exp[i], dec.last_router, cfg.top_k, label=f"{tag} pass {i}"):
+                return
+            check_rows(dev_rows[i:i + 1], row[None], label=f"{tag} pass {i}")
+            compared += 1
+
+    for t in range(trials):
+        dec.set_kv(K, V, int(F[t]))
+        m.set_kv(K, V, int(F[t]))
+        _, rows, exp = m.decode(2, force=F[t + 1:t + 3], logits=True, experts=True)
+        follow(rows, exp, F[t:t + 2], f"{label} trial {t}")
     say(f"{label}: one teacher-forced launch of {n} passes, then the same passes with debug output")
+    m.set_kv(K, V, int(F[0]))
     g_ids, _, _ = m.decode(n, force=F[1:])
     m.rewind(len(P), int(F[0]))
     c_ids, c_rows, c_exp = m.decode(n, force=F[1:], logits=True, experts=True)
     assert np.array_equal(g_ids, c_ids)
     assert np.array_equal(c_ids, np.argmax(c_rows, axis=1))
-    done = 0
-    for i in range(min(n, n_compare)):
-        row = dec.step(int(F[i]))
-        if not routing_agrees(c_exp[i], dec.last_router, cfg.top_k, label=f"{label} pass {i}"):
-            break
-        check_rows(c_rows[i:i + 1], row[None], label=f"{label} pass {i}")
-        done += 1
-    say(f"{label}: {done}/{min(n, n_compare)} passes compared")
-    return done
+    for i in range(n):
+        for l in range(cfg.n_layers):
+            sel = c_exp[i, l]
+            assert sel.min() >= 0 and sel.max() < cfg.n_experts and len(set(sel.tolist())) == cfg.top_k
+    dec.set_kv(K, V, int(F[0]))
+    follow(c_rows, c_exp, F[:min(n, 16)], f"{label} request")
+    say(f"{label}: {compared} passes compared with the oracle")
+    return compared

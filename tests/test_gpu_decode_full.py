@@ -142,7 +142,7 @@ def test_moe_prompt_routing_and_forced_request(torch_cuda):
     P = synth.make_prompt(cfg)
     m = _model(cfg, W)
     try:
-        done = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 32, "moe")
+        done = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 12, "moe")
     finally:
         m.close()
-    assert done >= 4
+    assert done >= 8

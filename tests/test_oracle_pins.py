@@ -236,8 +236,9 @@ def _tiny(**kw):
     return DecoderConfig(**base)
 
 
-def _brute_logits(cfg, W, tokens):
-    """Plain scalar loops in float64 from the written-out definition."""
+def _brute_logits(cfg, W, tokens, kv16=True):
+    """Plain scalar loops in float64 from the written-out definition; with
+    kv16 every cached key and value is rounded to fp16 as it is stored."""
     names = [n for n, _, _ in tensor_specs(cfg)]
     T = {n: np.asarray(t, dtype=np.float64) for n, t in zip(names, W)}
     d, H, Hkv, hd = cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
@@ -279,6 +280,9 @@ def _brute_logits(cfg, W, tokens):
             qh = [rot(q[j * hd:(j + 1) * hd], p) for j in range(H)]
             kh = [rot(k[g * hd:(g + 1) * hd], p) for g in range(Hkv)]
             vh = [v[g * hd:(g + 1) * hd] for g in range(Hkv)]
+            if kv16:
+                kh = [[float(np.float16(a)) for a in row] for row in kh]
+                vh = [[float(np.float16(a)) for a in row] for row in vh]
             cacheK[l].append(kh)
             cacheV[l].append(vh)
             o = []
@@ -320,6 +324,10 @@ def test_decoder_matches_scalar_brute_force(kw):
     got = np.stack([dec.step(t) for t in toks])
     want = _brute_logits(cfg, W, toks)
     np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    # a cache at the compute precision is the same definition without the rounding
+    exact = oracle.Decoder(cfg, W, dtype=np.float64, kv_dtype=None)
+    got = np.stack([exact.step(t) for t in toks])
+    np.testing.assert_allclose(got, _brute_logits(cfg, W, toks, kv16=False), rtol=1e-10, atol=1e-12)
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(n_experts=6, top_k=3, ffn_dim=6)])
