@@ -236,12 +236,41 @@ def bench_gemv(args):
     return line
 
 
+def bench_copy(args):
+    """Counter calibration: a plain device copy of a known size (1 GiB read,
+    1 GiB written per launch), timed like the other workloads."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n // 2, dtype=torch.float16, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"metric": "device copy bandwidth (read + write)", "value": round(gbs, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+            "data": "synthetic",
+            "config": {"workload": "torch copy_ of a 1 GiB fp16 tensor (counter calibration)",
+                       "bytes_read": n, "bytes_written": n},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_GBS, 4), "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="2b", help="2b (default), 2b_32k, moe, tiny or gemv")
+    ap.add_argument("--config", default="2b",
+                    help="2b (default), 2b_32k, moe, tiny, gemv, or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -257,6 +286,8 @@ def main():
         sys.exit("bench.py needs a GPU")
     if args.config == "gemv":
         line = bench_gemv(args)
+    elif args.config == "copy":
+        line = bench_copy(args)
     else:
         line = bench_decode(synth.get_config(args.config), args)
     print(json.dumps(line), flush=True)
