@@ -151,6 +151,7 @@ struct Geo {
     int nseg;   // segments per row (MoE down: top_k)
     int off;    // units from the start of the layer block (LM: of the LM block)
     int row0;   // first row (MoE gate/up: virtual row)
+    int gin;    // words of the exchanged input vector this workgroup gathers (0: none)
 };
 
 // LDS shared by the waves of one workgroup.
@@ -173,33 +174,76 @@ struct Smem {
     uint32_t sel[16];                           // MoE: experts selected for the current layer
     float pi[16];                               //      and their router probabilities
     Geo geo[K_COUNT];
+    float ssp[kWaves];                          // per wave: sum of squares of its share of the input
     uint32_t abort;                             // set when the communication wave gave up
 };
 
-__device__ __forceinline__ void set_geo(KIE_LDS Geo* g, int n, int nrows, int K, int nseg, int off, int row0) {
+__device__ __forceinline__ void set_geo(KIE_LDS Geo* g, int n, int nrows, int K, int nseg, int off, int row0,
+                                        int gin = 0) {
     g->n = n;
     g->nrows = nrows;
     g->K = K;
     g->nseg = nseg;
     g->off = off;
     g->row0 = row0;
+    g->gin = gin;
 }
 
 __device__ __forceinline__ void write_geo(const DecodeArgs& a, const WgPlan& W, int wg, KIE_LDS Geo* geo) {
     const Dims& D = a.D;
     for (int k = 0; k < K_COUNT; ++k) set_geo(geo + k, 0, 0, kUnitHalves, 1, 0, 0);
     const int piece = a.plan[wg];
-    set_geo(geo + K_QKV, W.nq, W.qn, D.d, 1, piece, W.q0);
-    set_geo(geo + K_WO, W.nwo, W.won, D.H * D.hd, 1, piece + W.nq, W.wo0);
+    // the input vector is gathered only where it is used: by workgroups with
+    // units in the phase (MoE: the router's input also feeds gate/up and down)
+    set_geo(geo + K_QKV, W.nq, W.qn, D.d, 1, piece, W.q0, W.nq ? D.d : 0);
+    set_geo(geo + K_WO, W.nwo, W.won, D.H * D.hd, 1, piece + W.nq, W.wo0, W.nwo ? D.H * D.hd : 0);
     if (D.E) {
-        set_geo(geo + K_ROUTER, W.nr, W.rn, D.d, 1, piece + W.nq + W.nwo, W.r0);
+        set_geo(geo + K_ROUTER, W.nr, W.rn, D.d, 1, piece + W.nq + W.nwo, W.r0, (W.nr || W.negu || W.ned) ? D.d : 0);
         set_geo(geo + K_EGU, W.negu, W.egun, D.d, 1, 0, W.egu0);
-        set_geo(geo + K_EDOWN, W.ned, W.won, D.F, D.topk, 0, W.wo0);
+        set_geo(geo + K_EDOWN, W.ned, W.won, D.F, D.topk, 0, W.wo0, W.ned ? D.topk * D.F : 0);
     } else {
-        set_geo(geo + K_GU, W.ngu, W.gun, D.d, 1, piece + W.nq + W.nwo, W.gu0);
-        set_geo(geo + K_DOWN, W.nd, W.won, D.F, 1, piece + W.nq + W.nwo + W.ngu, W.wo0);
+        set_geo(geo + K_GU, W.ngu, W.gun, D.d, 1, piece + W.nq + W.nwo, W.gu0, W.ngu ? D.d : 0);
+        set_geo(geo + K_DOWN, W.nd, W.won, D.F, 1, piece + W.nq + W.nwo + W.ngu, W.wo0, W.nd ? D.F : 0);
     }
-    set_geo(geo + K_LM, W.nlm, W.lmn, D.d, 1, a.plan[kGrid + 1 + wg], W.lm0);
+    set_geo(geo + K_LM, W.nlm, W.lmn, D.d, 1, a.plan[kGrid + 1 + wg], W.lm0, W.nlm ? D.d : 0);
+}
+
+// Stage input element i in LDS as two fp16 terms: xin = fp16(v), xlo =
+// fp16(v - xin). A GEMV sums the products with both, so its input keeps about
+// 22 significant bits while every product is a v_dot2 of fp16 pairs.
+__device__ __forceinline__ void stage1(KIE_LDS Smem* S, int i, float v) {
+    const _Float16 hi = (_Float16)v;
+    S->xin[i] = __builtin_bit_cast(uint16_t, hi);
+    S->xlo[i] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi));
+}
+
+// Every wave of the workgroup gathers its slice of the phase's input vector
+// (x, o or h as flagged fp32 words; all of a wave's loads are in flight at
+// once), stages it and leaves the slice's sum of squares in ssp[w]. The RMS
+// norm scale is applied to the row sums afterwards, which is the same product
+// since a GEMV is linear. Returns 0, or 1 (this wave timed out) / 2 (another
+// workgroup reported a failure).
+__device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S, int kind, int n, uint32_t id,
+                                            int w) {
+    const uint64_t* src = kind == K_WO ? a.ex.o : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
+    const int i0 = n * w / kWaves, i1 = n * (w + 1) / kWaves;
+    float ss = 0.f;
+    const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, [&](int i, uint32_t v) {
+        const float x = __builtin_bit_cast(float, v);
+        ss += x * x;
+        stage1(S, i0 + i, x);
+    });
+    ss = wave_sum(ss);
+    if (lane_id() == 0) S->ssp[w] = ss;
+    return r;
+}
+
+// Does every wave gather a share of this phase's input? Then all waves first
+// meet at a barrier, so that no share overwrites the staged input, the sums of
+// squares or the attention scratch that shares their LDS while the
+// communication wave still finishes the previous phases.
+__device__ __forceinline__ bool shared_gather(KIE_LDS Smem* S, int kind, int layer) {
+    return __builtin_amdgcn_readfirstlane(S->geo[kind].gin) > 0 && !(kind == K_QKV && layer == 0);
 }
 
 // ------------------------------------------------------------------------
@@ -240,57 +284,33 @@ struct Comm {
         return r == 0;
     }
 
-    // Stage v in LDS as two fp16 terms: xin = fp16(v), xlo = fp16(v - xin).
-    // A GEMV sums the products with both, so its input keeps about 22
-    // significant bits while every product is a v_dot2 of fp16 pairs.
-    __device__ __forceinline__ void put1(int i, float v) {
-        const _Float16 hi = (_Float16)v;
-        S->xin[i] = __builtin_bit_cast(uint16_t, hi);
-        S->xlo[i] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi));
-    }
-    __device__ __forceinline__ void put2(int i, float v0, float v1) {
-        const uint32_t hi = pack_h2(v0, v1);
-        const float r0 = v0 - h2f_bits((uint16_t)hi), r1 = v1 - h2f_bits((uint16_t)(hi >> 16));
-        ((KIE_LDS uint32_t*)S->xin)[i] = hi;
-        ((KIE_LDS uint32_t*)S->xlo)[i] = pack_h2(r0, r1);
+    // this wave's slice of the phase input (the compute waves gather theirs)
+    __device__ __forceinline__ void input_share(int kind, uint32_t id) {
+        if (dead) return;
+        const int n = S->geo[kind].gin;
+        const int r = gather_input(a, S, kind, n, id, 0);
+        if (r) fail(r);
     }
 
-    // the d-vector v * rsqrt(mean(v^2) + eps), for v given as flagged fp32
-    // words or (first layer) as the token's embedding row
-    __device__ __forceinline__ void input_norm(const uint64_t* xw, uint32_t id, const uint16_t* emb_row) {
+    // the first layer's input: the token's embedding row, staged whole here
+    __device__ __forceinline__ void input_embedding(const uint16_t* e) {
         const int d = a.D.d;
         float ss = 0.f;
-        if (emb_row) {
-            const KIE_GLOBAL uint32_t* e = (const KIE_GLOBAL uint32_t*)gptr(emb_row);
-            for (int i = lane; i < d / 2; i += 64) {
-                const uint32_t v = e[i];
-                const float x0 = h2f_bits((uint16_t)v), x1 = h2f_bits((uint16_t)(v >> 16));
-                ss += x0 * x0 + x1 * x1;
-                put2(i, x0, x1);
-            }
-        } else {
-            const bool ok = gather(xw, d, id, [&](int i, uint32_t v) {
-                const float x = __builtin_bit_cast(float, v);
-                ss += x * x;
-                put1(i, x);
-            });
-            if (!ok) return;
+        for (int i = lane; i < d; i += 64) {
+            const float x = h2f_bits(gptr(e)[i]);
+            ss += x * x;
+            stage1(S, i, x);
         }
         ss = wave_sum(ss);
-        const float s = 1.0f / sqrtf(ss / (float)d + a.eps);
-        const KIE_LDS uint32_t* hi = (const KIE_LDS uint32_t*)S->xin;
-        const KIE_LDS uint32_t* lo = (const KIE_LDS uint32_t*)S->xlo;
-        for (int i = lane; i < d / 2; i += 64) {
-            const uint32_t h = hi[i], l = lo[i];
-            const float x0 = h2f_bits((uint16_t)h) + h2f_bits((uint16_t)l);
-            const float x1 = h2f_bits((uint16_t)(h >> 16)) + h2f_bits((uint16_t)(l >> 16));
-            put2(i, x0 * s, x1 * s);
-        }
+        if (lane < kWaves) S->ssp[lane] = lane == 0 ? ss : 0.f;
     }
 
-    // n values given as flagged fp32 words, staged as they are
-    __device__ __forceinline__ void input_split(const uint64_t* src, int n, uint32_t id) {
-        gather(src, n, id, [&](int i, uint32_t v) { put1(i, __builtin_bit_cast(float, v)); });
+    // RMS norm scale of the staged input: rsqrt(mean(v^2) + eps)
+    __device__ __forceinline__ float in_scale() {
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) ss += S->ssp[w];
+        return 1.0f / sqrtf(ss / (float)a.D.d + a.eps);
     }
 
     __device__ __forceinline__ void zero_part(int nrows) {
@@ -364,9 +384,9 @@ struct Comm {
             if (it.layer == 0) {
                 const uint16_t* e = a.emb + (size_t)tok * D.d;
                 for (int j = lane; j < W.won; j += 64) S->own_x[j] = h2f_bits(gptr(e)[W.wo0 + j]);
-                if (W.nq) input_norm(nullptr, 0, e);
+                if (W.nq) input_embedding(e);
             } else if (W.nq) {
-                input_norm(a.ex.x, id_of(q - 1), nullptr);   // the previous layer's last phase
+                input_share(kind, id_of(q - 1));   // the previous layer's last phase
             }
             break;
         case K_ATTN: {
@@ -389,31 +409,31 @@ struct Comm {
         }
         case K_WO:
             zero_part(W.won);
-            if (W.nwo) input_split(a.ex.o, D.H * HD, id_of(q - 1));
+            if (W.nwo) input_share(kind, id_of(q - 1));
             break;
         case K_GU:
             zero_part(W.gun);
-            if (W.ngu) input_norm(a.ex.x, id_of(q - 1), nullptr);
+            if (W.ngu) input_share(kind, id_of(q - 1));
             break;
         case K_DOWN:
             zero_part(W.won);
-            if (W.nd) input_split(a.ex.h, D.F, id_of(q - 1));
+            if (W.nd) input_share(kind, id_of(q - 1));
             break;
         case K_ROUTER:
             zero_part(W.rn);
-            if (W.nr || W.negu || W.ned) input_norm(a.ex.x, id_of(q - 1), nullptr);
+            if (W.nr || W.negu || W.ned) input_share(kind, id_of(q - 1));
             break;
         case K_EGU:
             zero_part(W.egun);
-            if (W.negu || W.ned) route(q, it);   // xin still holds the router's normalised input
+            if (W.negu || W.ned) route(q, it);   // xin and ssp still hold the router's input
             break;
         case K_EDOWN:
             zero_part(W.won);
-            if (W.ned) input_split(a.ex.h, D.topk * D.F, id_of(q - 1));
+            if (W.ned) input_share(kind, id_of(q - 1));
             break;
         case K_LM:
             zero_part(W.lmn);
-            if (W.nlm) input_norm(a.ex.x, id_of(q - 1), nullptr);
+            if (W.nlm) input_share(kind, id_of(q - 1));
             break;
         default: break;
         }
@@ -428,13 +448,14 @@ struct Comm {
         switch (kind) {
         case K_QKV: {
             const int qd = D.H * HD, kd = D.Hkv * HD;
+            const float sc = in_scale();
             const KIE_GLOBAL float* rope = gptr(a.rope) + (size_t)pos * HD;   // [hd/2][cos, sin]
             // one lane per group of 4 rows: two rotary pairs, or 4 values
             for (int j = lane; j < W.qn / 4; j += 64) {
                 const int vr = W.q0 + 4 * j;
                 float y[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = rowsum(4 * j + e);
+                for (int e = 0; e < 4; ++e) y[e] = rowsum(4 * j + e) * sc;
                 if (vr < qd + kd) {
                     // rows (4j, 4j+1) = elements (i, i+hd/2), rows (4j+2, 4j+3) = (i+1, i+1+hd/2)
                     const int i = (vr % HD) >> 1;
@@ -513,13 +534,14 @@ struct Comm {
         case K_EDOWN:
             residual_add_publish(id);
             break;
-        case K_GU:
+        case K_GU: {
             // rows (4j .. 4j+3) = (g_m, u_m, g_m+1, u_m+1) with m = (gu0 + 4j) / 2
+            const float sc = in_scale();
             for (int j = lane; j < W.gun / 4; j += 64) {
                 float h[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float gv = rowsum(4 * j + 2 * e), uv = rowsum(4 * j + 2 * e + 1);
+                    const float gv = rowsum(4 * j + 2 * e) * sc, uv = rowsum(4 * j + 2 * e + 1) * sc;
                     h[e] = gv / (1.0f + __expf(-gv)) * uv;
                 }
                 const int m = W.gu0 / 2 + 2 * j;
@@ -527,30 +549,36 @@ struct Comm {
                 fw_store(a.ex.h + m + 1, __builtin_bit_cast(uint32_t, h[1]), id);
             }
             break;
-        case K_ROUTER:
+        }
+        case K_ROUTER: {
+            const float sc = in_scale();
             for (int j = lane; j < W.rn; j += 64)
-                fw_store(a.ex.r + W.r0 + j, __builtin_bit_cast(uint32_t, rowsum(j)), id);
+                fw_store(a.ex.r + W.r0 + j, __builtin_bit_cast(uint32_t, rowsum(j) * sc), id);
             break;
-        case K_EGU:
+        }
+        case K_EGU: {
+            const float sc = in_scale();
             for (int j = lane; j < W.egun / 4; j += 64) {
                 const int vr = W.egu0 + 4 * j;
                 const int k = vr / (2 * D.F), m = (vr % (2 * D.F)) >> 1;
                 float h[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float gv = rowsum(4 * j + 2 * e), uv = rowsum(4 * j + 2 * e + 1);
+                    const float gv = rowsum(4 * j + 2 * e) * sc, uv = rowsum(4 * j + 2 * e + 1) * sc;
                     h[e] = S->pi[k] * (gv / (1.0f + __expf(-gv))) * uv;
                 }
                 fw_store(a.ex.h + k * D.F + m, __builtin_bit_cast(uint32_t, h[0]), id);
                 fw_store(a.ex.h + k * D.F + m + 1, __builtin_bit_cast(uint32_t, h[1]), id);
             }
             break;
+        }
         case K_LM: {
             float bv = -3.0e38f;
             int bi = 0x7fffffff;
             const bool dbg = (a.flags & F_DBG_LOGITS) != 0;
+            const float sc = in_scale();
             for (int j = lane; j < W.lmn; j += 64) {
-                const float v = rowsum(j);
+                const float v = rowsum(j) * sc;
                 const int r = W.lm0 + j;
                 if (dbg) gptr(a.dbg_logits)[(size_t)(it.step % 64) * D.V + r] = v;
                 if (v > bv || (v == bv && r < bi)) { bv = v; bi = r; }
@@ -702,9 +730,11 @@ struct Comm {
             const int pos = a.pos0 + it.step;
             stamp(it.q, 0);
             if (phase_bars(a, kind, it.step, wg)) {
+                if (shared_gather(S, kind, it.layer)) wg_barrier();   // the previous phases are done
                 pre(kind, it);
+                wg_barrier();   // every wave's share of the input is staged
+                if (S->abort) dead = true;
                 stamp(it.q, 1);
-                wg_barrier();
                 wg_barrier();
                 stamp(it.q, 2);
                 post(kind, it, pos);
@@ -883,6 +913,17 @@ struct Compute {
     __device__ __forceinline__ void enter() {
         const int kind = kind_of(a.D, cc);
         if (!phase_bars(a, kind, cc.step, wg)) return;
+        if (shared_gather(S, kind, cc.layer)) {
+            wg_barrier();   // the communication wave is done with the previous phases
+            if (!stop) {
+                const int n = __builtin_amdgcn_readfirstlane(S->geo[kind].gin);
+                const int r = gather_input(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1);
+                if (r && lane == 0) {
+                    if (r == 1) dev_store32(a.status, (uint32_t)kStatusTimeout);
+                    S->abort = 1u;
+                }
+            }
+        }
         wg_barrier();   // the input (and the routing, for MoE gate/up) is in LDS
         stop = S->abort != 0u;
         if (kind == K_EGU) routed = cc.q;
