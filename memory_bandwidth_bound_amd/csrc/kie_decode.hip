@@ -167,8 +167,8 @@ struct Smem {
         float att_o[kCompute * kMaxGroup * 128];   // attention: per compute wave, unnormalised o
     };
     float att_q[kMaxGroup * 128];               // queries of the attention group, pre-scaled (also scratch)
-    alignas(8) uint16_t att_k[128];             // the new position's key and value
-    alignas(8) uint16_t att_v[128];
+    alignas(16) uint16_t att_k[128];            // the new position's key and value
+    alignas(16) uint16_t att_v[128];
     float att_ml[kCompute * kMaxGroup * 2];     // per compute wave: (max, sum)
     float own_x[kMaxOwnRows];                   // this workgroup's residual rows (fp32)
     uint32_t sel[16];                           // MoE: experts selected for the current layer
@@ -934,12 +934,16 @@ struct Compute {
         if (!phase_bars(a, kind, cc.step, wg)) return;
         if (kind == K_ATTN && !stop) {
             const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
-            // register arrays sized for the group (1, 2, 4, 5 or 8 heads)
+            // register arrays sized for the group (1, 2, 4 or 5 heads; 6 to 8
+            // heads in two passes over the positions)
             if (G == 1) attention<1>(l, pos);
             else if (G == 2) attention<2>(l, pos);
             else if (G <= 4) attention<4>(l, pos);
             else if (G == 5) attention<5>(l, pos);
-            else attention<8>(l, pos);
+            else {
+                attention<4>(l, pos, 0);
+                attention<4>(l, pos, 4);
+            }
         }
         wg_barrier();   // partial sums / attention states are in LDS
     }
@@ -1063,41 +1067,41 @@ struct Compute {
     // Attention of this workgroup's chunk: each compute wave takes every 7th
     // block of positions, keeps an online-softmax state per query head of the
     // group (GB >= heads per group), and leaves it in LDS for the
-    // communication wave to merge. Lanes: HD/4 per position, 4 dims each;
-    // U position blocks per round of loads.
+    // communication wave to merge. Lanes: HD/8 per position, 8 dims each; a
+    // round reads the keys and values of 4 x 64/(HD/8) positions in one trip.
     template <int GB>
-    __device__ __forceinline__ void attention(int layer, int pos) {
+    __device__ __forceinline__ void attention(int layer, int pos, int h0 = 0) {
         const Dims& D = a.D;
-        constexpr int LPP = HD / 4;       // lanes per position
+        constexpr int LPP = HD / 8;       // lanes per position
         constexpr int PPI = 64 / LPP;     // positions per wave instruction
         constexpr int U = 4;              // instructions per round
         int CH;
         attn_split(pos + 1, a.items_per_head, &CH);
-        const int Gq = D.H / D.Hkv;
+        const int Gq = (D.H / D.Hkv - h0 < GB) ? D.H / D.Hkv - h0 : GB;   // heads h0 .. h0 + Gq - 1
         const int g = wg % D.Hkv, chunk = wg / D.Hkv;
         const int c = pos + 1;
         const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
-        const int gi = lane / LPP, dl = (lane % LPP) * 4;
-        float qv[GB][4];
+        const int gi = lane / LPP, dl = (lane % LPP) * 8;
+        float qv[GB][8];
 #pragma unroll
         for (int j = 0; j < GB; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qv[j][e] = (j < Gq) ? S->att_q[j * HD + dl + e] : 0.f;
-        float m[GB], ls[GB], o[GB][4];
+            for (int e = 0; e < 8; ++e) qv[j][e] = (j < Gq) ? S->att_q[(h0 + j) * HD + dl + e] : 0.f;
+        float m[GB], ls[GB], o[GB][8];
 #pragma unroll
         for (int j = 0; j < GB; ++j) {
             m[j] = -3.0e38f;
             ls[j] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[j][e] = 0.f;
+            for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
         }
         const uint16_t* Kb = a.kc + ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
         const uint16_t* Vb = a.vc + ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
-        const uint64_t knew = *(const KIE_LDS uint64_t*)(S->att_k + dl);
-        const uint64_t vnew = *(const KIE_LDS uint64_t*)(S->att_v + dl);
+        const uint4 knew = lds_ld16(S->att_k + dl);
+        const uint4 vnew = lds_ld16(S->att_v + dl);
         static_assert(U == 4, "the cache loads below come in fours");
         for (int b = p0 + w * PPI * U; b < p1; b += kCompute * PPI * U) {
-            uint64_t kw[U], vw[U];
+            uint4 kw[U], vw[U];
             const uint16_t* kp[U];
             const uint16_t* vp[U];
 #pragma unroll
@@ -1107,8 +1111,8 @@ struct Compute {
                 kp[u] = Kb + (size_t)src * HD + dl;
                 vp[u] = Vb + (size_t)src * HD + dl;
             }
-            dev_load64x4_sync(kp[0], kp[1], kp[2], kp[3], kw[0], kw[1], kw[2], kw[3]);
-            dev_load64x4_sync(vp[0], vp[1], vp[2], vp[3], vw[0], vw[1], vw[2], vw[3]);
+            dev_load128x8_sync(kp[0], kp[1], kp[2], kp[3], vp[0], vp[1], vp[2], vp[3], kw[0], kw[1], kw[2], kw[3],
+                               vw[0], vw[1], vw[2], vw[3]);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int pp = b + u * PPI + gi;
@@ -1121,27 +1125,30 @@ struct Compute {
             for (int u = 0; u < U; ++u) {
                 const int pp = b + u * PPI + gi;
                 const bool valid = pp < p1;
-                float kf[4], vf[4];
+                float kf[8], vf[8];
+                const uint32_t kk[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w};
+                const uint32_t vv[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    kf[e] = h2f_bits((uint16_t)(kw[u] >> (16 * e)));
-                    vf[e] = h2f_bits((uint16_t)(vw[u] >> (16 * e)));
+                    kf[2 * e] = h2f_bits((uint16_t)kk[e]);
+                    kf[2 * e + 1] = h2f_bits((uint16_t)(kk[e] >> 16));
+                    vf[2 * e] = h2f_bits((uint16_t)vv[e]);
+                    vf[2 * e + 1] = h2f_bits((uint16_t)(vv[e] >> 16));
                 }
 #pragma unroll
                 for (int j = 0; j < GB; ++j) {
                     if (j < Gq) {
-                        float s = qv[j][0] * kf[0] + qv[j][1] * kf[1] + qv[j][2] * kf[2] + qv[j][3] * kf[3];
-                        s = row16_sum(s);
-                        if (LPP == 32)   // swap 16-lane halves of each 32-lane group
-                            s += __builtin_bit_cast(float,
-                                                    __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, s), 0x401F));
+                        float s = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s += qv[j][e] * kf[e];
+                        s = LPP == 16 ? row16_sum(s) : row8_sum(s);
                         if (valid) {
                             const float mn = fmaxf(m[j], s);
                             const float cr = __builtin_amdgcn_exp2f(m[j] - mn);
                             const float pr = __builtin_amdgcn_exp2f(s - mn);
                             ls[j] = ls[j] * cr + pr;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) o[j][e] = o[j][e] * cr + pr * vf[e];
+                            for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * cr + pr * vf[e];
                             m[j] = mn;
                         }
                     }
@@ -1159,7 +1166,7 @@ struct Compute {
                     const float f1 = __builtin_amdgcn_exp2f(m[j] - mn), f2 = __builtin_amdgcn_exp2f(m2 - mn);
                     ls[j] = ls[j] * f1 + l2 * f2;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[j][e] = o[j][e] * f1 + shfl_xor_f(o[j][e], off) * f2;
+                    for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * f1 + shfl_xor_f(o[j][e], off) * f2;
                     m[j] = mn;
                 }
             }
@@ -1169,10 +1176,10 @@ struct Compute {
             for (int j = 0; j < GB; ++j) {
                 if (j < Gq) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) S->att_o[(w * kMaxGroup + j) * HD + dl + e] = o[j][e];
+                    for (int e = 0; e < 8; ++e) S->att_o[(w * kMaxGroup + h0 + j) * HD + dl + e] = o[j][e];
                     if (lane == 0) {
-                        S->att_ml[(w * kMaxGroup + j) * 2] = m[j];
-                        S->att_ml[(w * kMaxGroup + j) * 2 + 1] = ls[j];
+                        S->att_ml[(w * kMaxGroup + h0 + j) * 2] = m[j];
+                        S->att_ml[(w * kMaxGroup + h0 + j) * 2 + 1] = ls[j];
                     }
                 }
             }

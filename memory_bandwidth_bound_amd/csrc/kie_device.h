@@ -229,6 +229,28 @@ __device__ __forceinline__ void dev_load64x4_sync(const void* p0, const void* p1
         : "memory");
 }
 
+// Eight 16-byte device-scope loads (four keys, four values) and the wait for
+// them in one statement, so the compiler neither sees a pending load nor
+// waits for loads it cannot see (the LDS DMA ring) at other places.
+__device__ __forceinline__ void dev_load128x8_sync(const void* k0, const void* k1, const void* k2, const void* k3,
+                                                   const void* v0, const void* v1, const void* v2, const void* v3,
+                                                   uint4& a0, uint4& a1, uint4& a2, uint4& a3, uint4& b0, uint4& b1,
+                                                   uint4& b2, uint4& b3) {
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off sc1\n\t"
+        "global_load_dwordx4 %1, %9, off sc1\n\t"
+        "global_load_dwordx4 %2, %10, off sc1\n\t"
+        "global_load_dwordx4 %3, %11, off sc1\n\t"
+        "global_load_dwordx4 %4, %12, off sc1\n\t"
+        "global_load_dwordx4 %5, %13, off sc1\n\t"
+        "global_load_dwordx4 %6, %14, off sc1\n\t"
+        "global_load_dwordx4 %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+        : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(v0), "v"(v1), "v"(v2), "v"(v3)
+        : "memory");
+}
+
 // Wait until words [0, n) of src all carry `id`, then call f(i, payload) for
 // every word (lane l handles i = l, l + 64, ...). One wave calls this. The
 // words are read in blocks of 64 * kGatherRegs with every load of a block
