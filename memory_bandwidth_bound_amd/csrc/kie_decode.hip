@@ -246,6 +246,47 @@ __device__ __forceinline__ bool shared_gather(KIE_LDS Smem* S, int kind, int lay
     return __builtin_amdgcn_readfirstlane(S->geo[kind].gin) > 0 && !(kind == K_QKV && layer == 0);
 }
 
+// Merge the compute waves' attention states of this chunk and publish o (the
+// whole row is here) or the chunk's partial state. Wave w8 of 8 takes every
+// 8th block of 64 (head, dim pair) slots.
+template <int HD>
+__device__ __forceinline__ void attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, int pos, uint32_t id, int w8) {
+    const Dims& D = a.D;
+    const int lane = lane_id(), wg = blockIdx.x;
+    const int Gq = D.H / D.Hkv;
+    int CH;
+    const int nper = attn_split(pos + 1, a.items_per_head, &CH);
+    const int g = wg % D.Hkv, chunk = wg / D.Hkv;
+    for (int idx = 2 * (w8 * 64 + lane); idx < Gq * HD; idx += 2 * 64 * kWaves) {
+        const int j = idx / HD, dd = idx % HD;
+        float M = -3.0e38f;
+#pragma unroll
+        for (int w = 0; w < kCompute; ++w) M = fmaxf(M, S->att_ml[(w * kMaxGroup + j) * 2]);
+        float L = 0.f, O0 = 0.f, O1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kCompute; ++w) {
+            const float f = __builtin_amdgcn_exp2f(S->att_ml[(w * kMaxGroup + j) * 2] - M);
+            L += f * S->att_ml[(w * kMaxGroup + j) * 2 + 1];
+            O0 += f * S->att_o[(w * kMaxGroup + j) * HD + dd];
+            O1 += f * S->att_o[(w * kMaxGroup + j) * HD + dd + 1];
+        }
+        const int head = g * Gq + j;
+        if (nper == 1) {
+            // the whole row is here: publish o under the combine phase's id
+            fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, O0 / L), id + 1);
+            fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, O1 / L), id + 1);
+        } else {
+            uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + chunk) * (HD + 2);
+            fw_store(pp + 2 + dd, __builtin_bit_cast(uint32_t, O0), id);
+            fw_store(pp + 3 + dd, __builtin_bit_cast(uint32_t, O1), id);
+            if (dd == 0) {
+                fw_store(pp, __builtin_bit_cast(uint32_t, M), id);
+                fw_store(pp + 1, __builtin_bit_cast(uint32_t, L), id);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------------
 // Communication wave.
 // ------------------------------------------------------------------------
@@ -494,41 +535,9 @@ struct Comm {
             }
             break;
         }
-        case K_ATTN: {
-            // merge the compute waves' states; publish o, or this chunk's partial
-            int CH;
-            const int nper = attn_split(pos + 1, a.items_per_head, &CH);
-            const int g = wg % D.Hkv, chunk = wg / D.Hkv;
-            for (int idx = 2 * lane; idx < Gq * HD; idx += 128) {
-                const int j = idx / HD, dd = idx % HD;
-                float M = -3.0e38f;
-#pragma unroll
-                for (int w = 0; w < kCompute; ++w) M = fmaxf(M, S->att_ml[(w * kMaxGroup + j) * 2]);
-                float L = 0.f, O0 = 0.f, O1 = 0.f;
-#pragma unroll
-                for (int w = 0; w < kCompute; ++w) {
-                    const float f = __builtin_amdgcn_exp2f(S->att_ml[(w * kMaxGroup + j) * 2] - M);
-                    L += f * S->att_ml[(w * kMaxGroup + j) * 2 + 1];
-                    O0 += f * S->att_o[(w * kMaxGroup + j) * HD + dd];
-                    O1 += f * S->att_o[(w * kMaxGroup + j) * HD + dd + 1];
-                }
-                const int head = g * Gq + j;
-                if (nper == 1) {
-                    // the whole row is here: publish o under the combine phase's id
-                    fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, O0 / L), id + 1);
-                    fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, O1 / L), id + 1);
-                } else {
-                    uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + chunk) * (HD + 2);
-                    fw_store(pp + 2 + dd, __builtin_bit_cast(uint32_t, O0), id);
-                    fw_store(pp + 3 + dd, __builtin_bit_cast(uint32_t, O1), id);
-                    if (dd == 0) {
-                        fw_store(pp, __builtin_bit_cast(uint32_t, M), id);
-                        fw_store(pp + 1, __builtin_bit_cast(uint32_t, L), id);
-                    }
-                }
-            }
+        case K_ATTN:
+            attn_merge<HD>(a, S, pos, id, 0);   // the compute waves merge the other slices
             break;
-        }
         case K_WO:
         case K_DOWN:
         case K_EDOWN:
@@ -738,6 +747,7 @@ struct Comm {
                 wg_barrier();
                 stamp(it.q, 2);
                 post(kind, it, pos);
+                if (kind == K_ATTN) wg_barrier();   // every slice is merged: att_o is free again
             } else {
                 solo(kind, it, pos);
             }
@@ -946,6 +956,10 @@ struct Compute {
             }
         }
         wg_barrier();   // partial sums / attention states are in LDS
+        if (kind == K_ATTN) {
+            if (!stop) attn_merge<HD>(a, S, a.pos0 + cc.step, a.id0 + (uint32_t)cc.q, w + 1);
+            wg_barrier();
+        }
     }
 
     // Afterwards phase qx is entered and not finished (qx == Q: all finished).
@@ -1121,37 +1135,47 @@ struct Compute {
                     vw[u] = vnew;
                 }
             }
+            // the round's scores first, then one online-softmax update per head
+            float vf[U][8], sc[U][GB];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int pp = b + u * PPI + gi;
-                const bool valid = pp < p1;
-                float kf[8], vf[8];
+                float kf[8];
                 const uint32_t kk[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w};
                 const uint32_t vv[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     kf[2 * e] = h2f_bits((uint16_t)kk[e]);
                     kf[2 * e + 1] = h2f_bits((uint16_t)(kk[e] >> 16));
-                    vf[2 * e] = h2f_bits((uint16_t)vv[e]);
-                    vf[2 * e + 1] = h2f_bits((uint16_t)(vv[e] >> 16));
+                    vf[u][2 * e] = h2f_bits((uint16_t)vv[e]);
+                    vf[u][2 * e + 1] = h2f_bits((uint16_t)(vv[e] >> 16));
                 }
+                const bool valid = b + u * PPI + gi < p1;
 #pragma unroll
                 for (int j = 0; j < GB; ++j) {
-                    if (j < Gq) {
-                        float s = 0.f;
+                    float d = 0.f;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) s += qv[j][e] * kf[e];
-                        s = LPP == 16 ? row16_sum(s) : row8_sum(s);
-                        if (valid) {
-                            const float mn = fmaxf(m[j], s);
-                            const float cr = __builtin_amdgcn_exp2f(m[j] - mn);
-                            const float pr = __builtin_amdgcn_exp2f(s - mn);
-                            ls[j] = ls[j] * cr + pr;
+                    for (int e = 0; e < 8; ++e) d += qv[j][e] * kf[e];
+                    d = LPP == 16 ? row16_sum(d) : row8_sum(d);
+                    sc[u][j] = valid ? d : -3.0e38f;
+                }
+            }
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * cr + pr * vf[e];
-                            m[j] = mn;
-                        }
-                    }
+            for (int j = 0; j < GB; ++j) {
+                if (j < Gq) {
+                    float mx = m[j];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
+                    const float cr = __builtin_amdgcn_exp2f(m[j] - mx);
+                    float pr[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)   // padding positions weigh nothing
+                        pr[u] = sc[u][j] > -1.0e38f ? __builtin_amdgcn_exp2f(sc[u][j] - mx) : 0.f;
+                    ls[j] = ls[j] * cr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        o[j][e] = o[j][e] * cr + ((pr[0] * vf[0][e] + pr[1] * vf[1][e]) +
+                                                  (pr[2] * vf[2][e] + pr[3] * vf[3][e]));
+                    m[j] = mx;
                 }
             }
         }
