@@ -794,7 +794,7 @@ struct Compute {
     PIter cc;          // next phase to enter (or the entered one when `entered`)
     bool entered;
     WaveGeo cg;        // geometry of the phase being consumed
-    int crow, cseg;    // row and unit-in-row of the next unit to consume in it
+    int crow, cseg, ck;   // row, unit in the row segment and segment (MoE down: expert) of the next unit
     float acc;         // running partial dot product of the current row
 
     __device__ __forceinline__ Compute(const DecodeArgs& args, KIE_LDS Smem* s, int wi) : a(args), S(s), w(wi) {
@@ -807,7 +807,7 @@ struct Compute {
         cc = PIter{0, 0, 0, 0};
         entered = false;
         cg.q = -1;
-        crow = cseg = 0;
+        crow = cseg = ck = 0;
         acc = 0.f;
         ic = PIter{0, 0, 0, 0};
         seek(false);
@@ -851,27 +851,43 @@ struct Compute {
         const uint8_t* idle = a.idle + lane * 16;
         const int kind = ig.kind;
         if (kind == K_EGU || kind == K_EDOWN) {
+            // expert units come in contiguous runs (one per selected expert):
+            // the address is worked out at the start of each run only
             const uint8_t* lb = a.experts + (size_t)ig.layer * D.E * a.expert_bytes + lane * 16;
             const int upr = ig.upr;
+            const uint8_t* p = lb;
+            int run = 0;
 #pragma unroll
             for (int s = 0; s < kNB; ++s) {
                 const uint8_t* src = idle + (size_t)s * kUnitBytes;
                 if (s < n) {
-                    const int u = iu + s;
-                    size_t off;
-                    if (kind == K_EGU) {
-                        const int vr = ig.row0 + u / upr, c = u % upr;
-                        const int k = vr / (2 * D.F), rr = vr % (2 * D.F);
+                    if (run == 0) {
+                        const int u = iu + s;
+                        size_t off;
+                        int k;
+                        if (kind == K_EGU) {
+                            // virtual rows k * 2F + r: row r of the gate/up block of expert k
+                            const int vr = ig.row0 + u / upr, c = u - (u / upr) * upr;
+                            k = vr / (2 * D.F);
+                            const int rr = vr - k * 2 * D.F;
+                            int vend = (k + 1) * 2 * D.F;
+                            if (vend > ig.row0 + ig.nrows) vend = ig.row0 + ig.nrows;
+                            run = (vend - vr) * upr - c;
+                            off = ((size_t)rr * D.d + (size_t)c * kUnitHalves) * 2;
+                        } else {
+                            // expert-major: the workgroup's down rows of expert 0, then 1, ...
+                            const int per = ig.nrows * upr;
+                            k = u / per;
+                            const int rem = u - k * per;
+                            run = per - rem;
+                            off = (size_t)2 * D.F * D.d * 2 + (size_t)ig.row0 * D.F * 2 + (size_t)rem * kUnitBytes;
+                        }
                         const int e = __builtin_amdgcn_readfirstlane(S->sel[k]);
-                        off = (size_t)e * a.expert_bytes + ((size_t)rr * D.d + c * kUnitHalves) * 2;
-                    } else {
-                        const int row = u / (D.topk * upr), rem = u % (D.topk * upr);
-                        const int k = rem / upr, c = rem % upr;
-                        const int e = __builtin_amdgcn_readfirstlane(S->sel[k]);
-                        off = (size_t)e * a.expert_bytes + (size_t)2 * D.F * D.d * 2 +
-                              ((size_t)(ig.row0 + row) * D.F + c * kUnitHalves) * 2;
+                        p = lb + (size_t)e * a.expert_bytes + off;
                     }
-                    src = lb + off;
+                    src = p;
+                    p += kUnitBytes;
+                    --run;
                 }
                 dma_unit(src, dst + s * kUnitBytes);
             }
@@ -978,30 +994,40 @@ struct Compute {
     }
 
     // consume the batch at LDS address src: all LDS reads of the batch are
-    // issued before the first product. The input offset of a unit is its
-    // position in its row times 512 (the segments of a MoE down row follow
-    // each other in the input), so the per-unit bookkeeping is one counter.
+    // issued before the first product. Units run through row segments of upr
+    // units, rows 0 .. nrows-1, then (MoE down) the same rows for the next
+    // selected expert, whose input follows in xin; a segment's partial dot
+    // product is added to the (row, wave) partial sum.
     __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
         if (cg.q != sl.q) {
             load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
             if (cg.upr) {
-                const int per_row = cg.nseg * cg.upr;
-                crow = cg.lo / per_row;
-                cseg = cg.lo - crow * per_row;   // unit position within the row
+                const int per_seg = cg.nrows * cg.upr;
+                ck = cg.lo / per_seg;
+                const int rem = cg.lo - ck * per_seg;
+                crow = rem / cg.upr;
+                cseg = rem - crow * cg.upr;   // unit position within the row segment
             }
         }
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
         uint4 wv[kNB], xv[kNB], xl[kNB];
         if (cg.upr) {
-            const int per_row = cg.nseg * cg.upr;
-            int rp = cseg;
+            const int upr = cg.upr, nrows = cg.nrows;
+            int rs = cseg, rr = crow, rk = ck;
 #pragma unroll
             for (int s = 0; s < kNB; ++s) {
                 if (s < sl.n) {
+                    const int xo = rk * cg.K + rs * kUnitHalves + lane * 8;
                     wv[s] = lds_ld16(wb + s * kUnitBytes);
-                    xv[s] = lds_ld16(S->xin + rp * kUnitHalves + lane * 8);
-                    xl[s] = lds_ld16(S->xlo + rp * kUnitHalves + lane * 8);
-                    rp = (rp + 1 == per_row) ? 0 : rp + 1;
+                    xv[s] = lds_ld16(S->xin + xo);
+                    xl[s] = lds_ld16(S->xlo + xo);
+                    if (++rs == upr) {
+                        rs = 0;
+                        if (++rr == nrows) {
+                            rr = 0;
+                            ++rk;
+                        }
+                    }
                 }
             }
             const int last = cg.hi - 1 - sl.u0;   // batch index of the range's last unit
@@ -1009,15 +1035,18 @@ struct Compute {
             for (int s = 0; s < kNB; ++s) {
                 if (s < sl.n) {
                     acc = dot8(wv[s], xl[s], dot8(wv[s], xv[s], acc));
-                    const bool row_done = cseg + 1 == per_row;
-                    if (row_done || s == last) {
+                    const bool seg_done = cseg + 1 == upr;
+                    if (seg_done || s == last) {
                         const float r = wave_sum_to_lane63(acc);
-                        if (lane == 63) S->part[crow * kCompute + w] = r;
+                        if (lane == 63) S->part[crow * kCompute + w] += r;
                         acc = 0.f;
                     }
-                    if (row_done) {
+                    if (seg_done) {
                         cseg = 0;
-                        ++crow;
+                        if (++crow == nrows) {
+                            crow = 0;
+                            ++ck;
+                        }
                     } else {
                         ++cseg;
                     }
