@@ -391,25 +391,27 @@ struct Comm {
         float sum = 0.f;
         for (int e = lane; e < E; e += 64) sum += __expf(lg[e] - mx);
         sum = wave_sum(sum);
-        float pv = 3.0e38f;
-        int pix = -1;
-        for (int k = 0; k < D.topk; ++k) {
-            float bv = -3.0e38f;
-            int bi = 0x7fffffff;
-            for (int e = lane; e < E; e += 64) {
-                const float v = lg[e];
-                const bool below = (v < pv) || (v == pv && e > pix);
-                if (below && (v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
+        // rank of each logit among all E (larger first, ties to the lower
+        // index); the k of rank < top_k are the selection. The logits are
+        // padded to a multiple of 8 so the reads below come in independent 8s.
+        const int E8 = (E + 7) & ~7;
+        for (int e = E + lane; e < E8; e += 64) lg[e] = -3.4e38f;
+        if (lane < 16) S->sel[lane] = 0u;   // in range even if NaN logits leave ranks unfilled
+        for (int e = lane; e < E; e += 64) {
+            const float v = lg[e];
+            int rank = 0;
+            for (int j0 = 0; j0 < E8; j0 += 8) {
+                float u[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) u[jj] = lg[j0 + jj];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) rank += (u[jj] > v || (u[jj] == v && j0 + jj < e)) ? 1 : 0;
             }
-            wave_argmax(bv, bi);
-            if (bi >= E) bi = E - 1;   // only with NaN logits: keep the expert loads in bounds
-            pv = bv;
-            pix = bi;
-            if (lane == 0) {
-                S->sel[k] = (uint32_t)bi;
-                S->pi[k] = __expf(bv - mx) / sum;
+            if (rank < D.topk) {
+                S->sel[rank] = (uint32_t)e;
+                S->pi[rank] = __expf(v - mx) / sum;
                 if ((a.flags & F_DBG_EXPERTS) && wg == 0)
-                    gptr(a.dbg_experts)[((size_t)(it.step % 64) * D.L + it.layer) * D.topk + k] = bi;
+                    gptr(a.dbg_experts)[((size_t)(it.step % 64) * D.L + it.layer) * D.topk + rank] = e;
             }
         }
     }
