@@ -980,6 +980,19 @@ struct Compute {
         }
     }
 
+    // When the batch just consumed was this wave's last of the entered phase
+    // (the next batch belongs to a later phase), finish the phase before the
+    // refill: issuing the refill may wait for the memory pipeline, and the
+    // phase's epilogue should not.
+    __device__ __forceinline__ void finish_if_done(const Slot (&sq)[kNS]) {
+        static_assert(kNS >= 2, "the ring holds at least two batches");
+        if (entered && sq[0].n > 0 && !stop && sq[0].q == cc.q && sq[1].q != cc.q) {
+            finish();
+            advance(a.D, cc);
+            entered = false;
+        }
+    }
+
     // Afterwards phase qx is entered and not finished (qx == Q: all finished).
     __device__ __forceinline__ void goto_phase(int qx) {
         while (true) {
@@ -995,22 +1008,99 @@ struct Compute {
         }
     }
 
+    // Consume one batch with the phase's input segments in registers: xh[j],
+    // xq[j] hold the hi and lo terms of segment (cseg + j) % UPR, so unit s of
+    // the batch uses xh[s % UPR]; a full batch rotates them by kNB % UPR.
+    template <int UPR>
+    __device__ __forceinline__ void consume_reg(uint32_t src, const Slot& sl, uint4 (&xh)[UPR], uint4 (&xq)[UPR]) {
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
+        uint4 wv[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; ++s)
+            if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
+        const int last = cg.hi - 1 - sl.u0;   // batch index of the range's last unit
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) {
+            if (s < sl.n) {
+                acc = dot8(wv[s], xq[s % UPR], dot8(wv[s], xh[s % UPR], acc));
+                const bool seg_done = cseg + 1 == UPR;
+                if (seg_done || s == last) {
+                    const float r = wave_sum_to_lane63(acc);
+                    if (lane == 63) S->part[crow * kCompute + w] += r;
+                    acc = 0.f;
+                }
+                if (seg_done) {
+                    cseg = 0;
+                    ++crow;
+                } else {
+                    ++cseg;
+                }
+            }
+        }
+        constexpr int R = kNB % UPR;
+        if (R && sl.n == kNB) {   // a short batch ends the wave's range: nothing follows in this phase
+            uint4 th[UPR], tq[UPR];
+#pragma unroll
+            for (int j = 0; j < UPR; ++j) {
+                th[j] = xh[(j + R) % UPR];
+                tq[j] = xq[(j + R) % UPR];
+            }
+#pragma unroll
+            for (int j = 0; j < UPR; ++j) {
+                xh[j] = th[j];
+                xq[j] = tq[j];
+            }
+        }
+    }
+
+    // Consume every batch of the current phase at the head of the ring with
+    // the input in registers (rows of UPR units, one input segment for all
+    // rows), refilling each batch as it goes. On return sq[0] belongs to a
+    // later phase (or is idle).
+    template <int UPR>
+    __device__ __forceinline__ void stream_phase(Slot (&sq)[kNS], int& head) {
+        const int q = sq[0].q;
+        if (cg.q != q) enter_geo(sq[0]);
+        uint4 xh[UPR], xq[UPR];
+#pragma unroll
+        for (int j = 0; j < UPR; ++j) {
+            const int c = (cseg + j) % UPR;
+            xh[j] = lds_ld16(S->xin + c * kUnitHalves + lane * 8);
+            xq[j] = lds_ld16(S->xlo + c * kUnitHalves + lane * 8);
+        }
+        while (sq[0].q == q && sq[0].n > 0) {
+            const uint32_t at = ring0 + head * kBatchBytes;
+            wait_vm<(kNS - 1) * kNB>();
+            consume_reg<UPR>(at, sq[0], xh, xq);
+            wait_lgkm0();   // this batch's LDS reads are done before it is overwritten
+            finish_if_done(sq);
+            const Slot t = fill(at);
+#pragma unroll
+            for (int i = 0; i + 1 < kNS; ++i) sq[i] = sq[i + 1];
+            sq[kNS - 1] = t;
+            head = (head + 1 == kNS) ? 0 : head + 1;
+        }
+    }
+
     // consume the batch at LDS address src: all LDS reads of the batch are
     // issued before the first product. Units run through row segments of upr
     // units, rows 0 .. nrows-1, then (MoE down) the same rows for the next
     // selected expert, whose input follows in xin; a segment's partial dot
     // product is added to the (row, wave) partial sum.
-    __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
-        if (cg.q != sl.q) {
-            load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
-            if (cg.upr) {
-                const int per_seg = cg.nrows * cg.upr;
-                ck = cg.lo / per_seg;
-                const int rem = cg.lo - ck * per_seg;
-                crow = rem / cg.upr;
-                cseg = rem - crow * cg.upr;   // unit position within the row segment
-            }
+    // geometry of the phase of batch sl, and the position of its first unit
+    __device__ __forceinline__ void enter_geo(const Slot& sl) {
+        load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
+        if (cg.upr) {
+            const int per_seg = cg.nrows * cg.upr;
+            ck = cg.lo / per_seg;
+            const int rem = cg.lo - ck * per_seg;
+            crow = rem / cg.upr;
+            cseg = rem - crow * cg.upr;   // unit position within the row segment
         }
+    }
+
+    __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
+        if (cg.q != sl.q) enter_geo(sl);
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
         uint4 wv[kNB], xv[kNB], xl[kNB];
         if (cg.upr) {
@@ -1088,10 +1178,17 @@ struct Compute {
             const uint32_t at = ring0 + head * kBatchBytes;
             goto_phase(sq[0].q);   // sq[0].q == Q once nothing is left: finishes every phase
             KIE_T(0)
+            if (sq[0].n > 0 && !stop && sq[0].kind != K_EDOWN) {
+                // rows of at most 5 units share one input segment set: keep it in registers
+                const int upr = __builtin_amdgcn_readfirstlane(S->geo[sq[0].kind].K) / kUnitHalves;
+                if (upr == 5) { stream_phase<5>(sq, head); continue; }
+                if (upr == 4) { stream_phase<4>(sq, head); continue; }
+            }
             wait_vm<(kNS - 1) * kNB>();
             KIE_T(1)
             if (sq[0].n > 0 && !stop) consume(at, sq[0]);
             wait_lgkm0();          // this batch's LDS reads are done before it is overwritten
+            finish_if_done(sq);
             KIE_T(2)
             const Slot t = fill(at);
             KIE_T(3)
