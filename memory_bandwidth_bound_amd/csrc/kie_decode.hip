@@ -987,7 +987,8 @@ struct Compute {
     __device__ __forceinline__ void finish_if_done(const Slot (&sq)[kNS]) {
         static_assert(kNS >= 2, "the ring holds at least two batches");
         if (entered && sq[0].n > 0 && !stop && sq[0].q == cc.q && sq[1].q != cc.q) {
-            finish();
+            // a GEMV phase (the batch had units): finishing it is its second barrier
+            if (phase_bars(a, kind_of(a.D, cc), cc.step, wg)) wg_barrier();
             advance(a.D, cc);
             entered = false;
         }
