@@ -297,6 +297,7 @@ struct Comm {
     WgPlan W;
     int wg, lane, tok;
     bool dead;
+    float rq[4];   // QKV epilogue: (cos, sin) of this lane's two rotary pairs, loaded before the input gather
 
     __device__ __forceinline__ Comm(const DecodeArgs& args, KIE_LDS Smem* s, const WgPlan& plan)
         : a(args), S(s), W(plan) {
@@ -422,7 +423,16 @@ struct Comm {
         if (dead) return;
         const int q = it.q;
         switch (kind) {
-        case K_QKV:
+        case K_QKV: {
+            // the epilogue's RoPE table entries, read now so that their trip
+            // overlaps the input gather instead of following the compute
+            const int qk = D.H * HD + D.Hkv * HD, vr = W.q0 + 4 * lane;
+            if (lane < W.qn / 4 && vr < qk) {
+                const int i = (vr % HD) >> 1;
+                const KIE_GLOBAL float* r = gptr(a.rope) + ((size_t)(a.pos0 + it.step) * HD + 2 * i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rq[e] = r[e];
+            }
             zero_part(W.qn);
             if (it.layer == 0) {
                 const uint16_t* e = a.emb + (size_t)tok * D.d;
@@ -432,6 +442,7 @@ struct Comm {
                 input_share(kind, id_of(q - 1));   // the previous layer's last phase
             }
             break;
+        }
         case K_ATTN: {
             const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = wg % D.Hkv;
             const float qs = kLog2e / sqrtf((float)HD);
@@ -492,8 +503,7 @@ struct Comm {
         case K_QKV: {
             const int qd = D.H * HD, kd = D.Hkv * HD;
             const float sc = in_scale();
-            const KIE_GLOBAL float* rope = gptr(a.rope) + (size_t)pos * HD;   // [hd/2][cos, sin]
-            // one lane per group of 4 rows: two rotary pairs, or 4 values
+            // one lane per group of 4 rows (at most 64 groups): two rotary pairs, or 4 values
             for (int j = lane; j < W.qn / 4; j += 64) {
                 const int vr = W.q0 + 4 * j;
                 float y[4];
@@ -505,7 +515,7 @@ struct Comm {
                     float r[4];
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        const float c = rope[2 * (i + e)], s = rope[2 * (i + e) + 1];
+                        const float c = rq[2 * e], s = rq[2 * e + 1];
                         const float x0 = y[2 * e], x1 = y[2 * e + 1];
                         r[2 * e] = x0 * c - x1 * s;
                         r[2 * e + 1] = x1 * c + x0 * s;
