@@ -189,3 +189,69 @@ def test_moe_teacher_forced_parity(torch_cuda, name):
     finally:
         m.close()
     assert done >= 8
+
+
+# ---- degenerate inputs ----------------------------------------------------------
+def test_one_token_prompt_and_empty_cache(torch_cuda):
+    """A one-token prompt, and decoding from an empty cache (set_kv with no
+    positions): the first pass attends only to itself."""
+    cfg = TINY.with_(prompt_len=1, decode_steps=6)
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    ref = oracle.Decoder(cfg, W)
+    first, last = ref.prefill(P)
+    ids, rows, _ = ref.decode(cfg.decode_steps, keep_logits=True)
+    m = _model(cfg, W)
+    try:
+        g_first, g_logits, _ = m.prefill(P, logits=True)
+        check_rows(g_logits[-1:], last[None], label="one-token prefill")
+        m.rewind(1, first)
+        _, g_rows, _ = m.decode(cfg.decode_steps, force=ids, logits=True)
+        check_rows(g_rows, rows, label="one-token prompt decode")
+
+        K = np.zeros((cfg.n_layers, 0, cfg.n_kv_heads, cfg.head_dim), dtype=np.float16)
+        pend = int(P[0])
+        ref2 = oracle.Decoder(cfg, W)
+        ref2.set_kv(K, K, pend)
+        ids2, rows2, _ = ref2.decode(4, keep_logits=True)
+        m.set_kv(K, K, pend)
+        _, g_rows2, _ = m.decode(4, force=ids2, logits=True)
+        check_rows(g_rows2, rows2, label="empty-cache decode")
+    finally:
+        m.close()
+
+
+def test_empty_requests_are_rejected(torch_cuda):
+    from memory_bandwidth_bound_amd import kie
+    cfg = TINY.with_(decode_steps=4)
+    m = _model(cfg, synth.make_weights(cfg))
+    try:
+        with pytest.raises(kie.KieError) as e:
+            m.prefill(np.zeros(0, dtype=np.int32))
+        assert e.value.code == -1
+        m.prefill(synth.make_prompt(cfg))
+        with pytest.raises(kie.KieError) as e:
+            m.decode(0)
+        assert e.value.code == -1
+        assert m.state()[0] == cfg.prompt_len      # a rejected call changes nothing
+    finally:
+        m.close()
+
+
+def test_two_token_vocabulary(torch_cuda):
+    """The smallest vocabulary: two LM rows, so all but two workgroups have no
+    LM rows and the device argmax reduces mostly empty entries."""
+    cfg = TINY.with_(name="tiny_v2", vocab=2, decode_steps=10)
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    first, last, ids, rows = _oracle_run(cfg, W, P, cfg.decode_steps)
+    m = _model(cfg, W)
+    try:
+        g_first, g_logits, _ = m.prefill(P, logits=True)
+        check_rows(g_logits[-1:], last[None], label="vocab 2 prefill")
+        m.rewind(len(P), first)
+        g_ids, g_rows, _ = m.decode(cfg.decode_steps, force=ids, logits=True)
+        check_rows(g_rows, rows, label="vocab 2 decode")
+        assert np.array_equal(g_ids, np.argmax(g_rows, axis=1))
+    finally:
+        m.close()
