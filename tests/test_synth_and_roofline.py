@@ -103,3 +103,14 @@ def test_decode_bytes_sums_kv_per_pass():
     # the 70 % MBU target of the 2.1B decoder at 8 TB/s, about 1,355 tok/s
     mean_kv = per * (129 + 1152) / 2
     assert 0.7 * 8e12 / (w + mean_kv) == pytest.approx(1355, rel=0.002)
+
+
+def test_bench_refuses_more_than_one_gpu(root_dir):
+    """The benchmark measures one GPU; asking for several exits with a message
+    (before touching a device)."""
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root_dir, capture_output=True, text=True,
+                       timeout=300)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
