@@ -646,6 +646,58 @@ struct Comm {
         }
     }
 
+    // One trip of the combine gather: states t0 .. t0 + 64R - 1 (clamped to
+    // T - 1, so every poll issues the same 4R loads and the compiler waits for
+    // them once), polled until all carry ida, then staged in LDS as
+    // [t][m, l, o0, o1]. Returns false when the wave gave up.
+    template <int R>
+    __device__ __forceinline__ bool combine_trip(int t0, int T, int p0, int nper, int g, int Gq, uint32_t ida,
+                                                 KIE_LDS float* st) {
+        const uint64_t* ad[R][4];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int t = t0 + r * 64 + lane;
+            t = t < T ? t : T - 1;
+            const int pr = p0 + t / nper, ch = t % nper;
+            const int idx = 2 * pr, head = g * Gq + idx / HD, dd = idx % HD;
+            const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + ch) * (HD + 2);
+            ad[r][0] = pp;
+            ad[r][1] = pp + 1;
+            ad[r][2] = pp + 2 + dd;
+            ad[r][3] = pp + 3 + dd;
+        }
+        uint64_t w[R][4];
+        uint32_t spins = 0;
+        while (true) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[r][e] = fw_load(ad[r][e]);
+            bool ok = true;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ok = fw_ok(w[r][e], ida) && ok;
+            if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+            if (++spins > a.spin) {
+                fail(1);
+                return false;
+            }
+            if ((spins & 63) == 0 && dev_load32(a.status) != 0) {
+                fail(2);
+                return false;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int t = t0 + r * 64 + lane;
+            if (t < T)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[t * 4 + e] = __builtin_bit_cast(float, fw_val(w[r][e]));
+        }
+        return true;
+    }
+
     // Split attention: the workgroup of chunk c of KV group g combines the
     // nper partial states of its slice of the group's output pairs. Every
     // (pair, chunk) state is read in one trip (lanes over pairs x chunks),
@@ -661,63 +713,13 @@ struct Comm {
         const int T = np * nper;   // (pair, chunk) states, at most P + nper <= 768
         const uint32_t ida = id_of(q - 1);
         KIE_LDS float* st = S->att_o;   // scratch: [T][4] (m, l, o0, o1)
-        constexpr int R = 8;            // states per lane per trip
-        for (int t0 = 0; t0 < T; t0 += R * 64) {   // one trip unless T > 512
-            uint64_t w[R][4];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int t = t0 + r * 64 + lane;
-                if (t < T) {
-                    const int pr = p0 + t / nper, ch = t % nper;
-                    const int idx = 2 * pr, head = g * Gq + idx / HD, dd = idx % HD;
-                    const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + ch) * (HD + 2);
-                    w[r][0] = fw_load(pp);
-                    w[r][1] = fw_load(pp + 1);
-                    w[r][2] = fw_load(pp + 2 + dd);
-                    w[r][3] = fw_load(pp + 3 + dd);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[r][e] = (uint64_t)ida << 32;
-                }
-            }
-            uint32_t spins = 0;
-            while (true) {
-                bool ok = true;
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ok = fw_ok(w[r][e], ida) && ok;
-                if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-                if (++spins > a.spin) {
-                    fail(1);
-                    return;
-                }
-                if ((spins & 63) == 0 && dev_load32(a.status) != 0) {
-                    fail(2);
-                    return;
-                }
-                __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int t = t0 + r * 64 + lane;
-                    if (t < T) {
-                        const int pr = p0 + t / nper, ch = t % nper;
-                        const int idx = 2 * pr, head = g * Gq + idx / HD, dd = idx % HD;
-                        const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + ch) * (HD + 2);
-                        if (!fw_ok(w[r][0], ida)) w[r][0] = fw_load(pp);
-                        if (!fw_ok(w[r][1], ida)) w[r][1] = fw_load(pp + 1);
-                        if (!fw_ok(w[r][2], ida)) w[r][2] = fw_load(pp + 2 + dd);
-                        if (!fw_ok(w[r][3], ida)) w[r][3] = fw_load(pp + 3 + dd);
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int t = t0 + r * 64 + lane;
-                if (t < T)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) st[t * 4 + e] = __builtin_bit_cast(float, fw_val(w[r][e]));
-            }
+        for (int t0 = 0; t0 < T; t0 += 8 * 64) {   // one trip unless T > 512
+            const int per = (T - t0 + 63) / 64;
+            bool ok;
+            if (per <= 2) ok = combine_trip<2>(t0, T, p0, nper, g, Gq, ida, st);
+            else if (per <= 4) ok = combine_trip<4>(t0, T, p0, nper, g, Gq, ida, st);
+            else ok = combine_trip<8>(t0, T, p0, nper, g, Gq, ida, st);
+            if (!ok) return;
         }
         for (int j = lane; j < np; j += 64) {
             float m = -3.0e38f, l = 0.f, o0 = 0.f, o1 = 0.f;

@@ -252,45 +252,62 @@ __device__ __forceinline__ void dev_load128x8_sync(const void* k0, const void* k
 }
 
 // Wait until words [0, n) of src all carry `id`, then call f(i, payload) for
-// every word (lane l handles i = l, l + 64, ...). One wave calls this. The
-// words are read in blocks of 64 * kGatherRegs with every load of a block
-// issued at once, so when the data is already published one trip through the
-// memory pipeline per block suffices; words not yet published are re-read
-// until they are.
+// every word (lane l handles i = l, l + 64, ...). One wave calls this.
+//
+// A block of 64R words is polled as a whole: every poll issues the same R
+// loads per lane (lanes past the end re-read word 0; a word that carries `id`
+// keeps it until this wave has published something its producer waits for,
+// so re-reading it is harmless) and waits for them once. Loads that depend on
+// what the previous poll returned would sit in divergent branches, where the
+// compiler's wait counting gives up and waits after each load, one trip
+// through the memory pipeline per load instead of one per poll.
 // Returns 0, or 1 when spin_limit polls went by, or 2 when *status became
 // non-zero (another workgroup gave up).
-constexpr int kGatherRegs = 32;   // words per lane per block
+constexpr int kGatherRegs = 16;     // words per lane per block (at most)
+
+template <int R, class F>
+__device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
+                                               const uint32_t* status, uint32_t& spins, F& f) {
+    const int lane = lane_id();
+    const uint64_t* p[R];
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+        const int i = c * 64 + lane;
+        p[c] = src + (i < n ? i : 0);
+    }
+    uint64_t x[R];
+    while (true) {
+#pragma unroll
+        for (int c = 0; c < R; ++c) x[c] = fw_load(p[c]);
+        bool ok = true;
+#pragma unroll
+        for (int c = 0; c < R; ++c) ok = fw_ok(x[c], id) && ok;
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+        if (++spins > spin_limit) return 1;
+        if ((spins & 63) == 0 && dev_load32(status) != 0) return 2;
+    }
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+        const int i = c * 64 + lane;
+        if (i < n) f(i, fw_val(x[c]));
+    }
+    return 0;
+}
+
 template <class F>
 __device__ __forceinline__ int fw_gather(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
                                          const uint32_t* status, F f) {
-    const int lane = lane_id();
     uint32_t spins = 0;
     for (int base = 0; base < n; base += 64 * kGatherRegs) {
-        uint64_t w[kGatherRegs];
-#pragma unroll
-        for (int c = 0; c < kGatherRegs; ++c) {
-            const int i = base + c * 64 + lane;
-            w[c] = (i < n) ? fw_load(src + i) : ((uint64_t)id << 32);
-        }
-        while (true) {
-            bool ok = true;
-#pragma unroll
-            for (int c = 0; c < kGatherRegs; ++c) ok = fw_ok(w[c], id) && ok;
-            if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-            if (++spins > spin_limit) return 1;
-            if ((spins & 63) == 0 && dev_load32(status) != 0) return 2;
-            __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int c = 0; c < kGatherRegs; ++c) {
-                const int i = base + c * 64 + lane;
-                if (i < n && !fw_ok(w[c], id)) w[c] = fw_load(src + i);
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kGatherRegs; ++c) {
-            const int i = base + c * 64 + lane;
-            if (i < n) f(i, fw_val(w[c]));
-        }
+        const int m = (n - base < 64 * kGatherRegs) ? n - base : 64 * kGatherRegs;
+        const int per = (m + 63) / 64;
+        auto g = [&](int i, uint32_t v) { f(base + i, v); };
+        int r;
+        if (per <= 2) r = fw_gather_block<2>(src + base, m, id, spin_limit, status, spins, g);
+        else if (per <= 4) r = fw_gather_block<4>(src + base, m, id, spin_limit, status, spins, g);
+        else if (per <= 8) r = fw_gather_block<8>(src + base, m, id, spin_limit, status, spins, g);
+        else r = fw_gather_block<16>(src + base, m, id, spin_limit, status, spins, g);
+        if (r) return r;
     }
     return 0;
 }
