@@ -196,9 +196,10 @@ const char* kie_status_str(int status);
  * [copies][M] (device), products accumulated in fp32 with v_dot2.
  * variant 0: the persistent 256-workgroup GEMV streaming weights the way
  *            the decode kernel does (LDS DMA into a per-wave ring of
- *            batches kept in flight, 8 waves per workgroup, whole rows per
- *            wave, x staged in LDS); K above 8192 runs as column blocks of
- *            8192, one launch each, accumulated into y.
+ *            batches kept in flight, 8 waves per workgroup, a contiguous
+ *            range of the matrices' 1 KiB units per wave, x staged in LDS,
+ *            row partial sums added into y); K above 8192 runs as column
+ *            blocks of 8192, one launch each, accumulated into y.
  * variant 1: a plain many-wave GEMV (4 rows per wave, all loads in flight).
  * K must be a multiple of 512, at most 65536, and copies*M*K*2 >= 4096.
  * *ms_out (host, may be NULL) receives the device time of the launches.

@@ -421,6 +421,8 @@ int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K,
     a.K = K;
     a.copies = copies;
     a.accumulate = 0;
+    // the streaming variant adds row partial sums into y
+    if (variant == 0) HIP_TRY(nullptr, hipMemsetAsync(y, 0, (size_t)M * copies * sizeof(float), s));
     HIP_TRY(nullptr, hipEventRecord(e0, s));
     if (variant == 0) {
         // the streaming kernel keeps x in LDS: column blocks of at most kMaxInput

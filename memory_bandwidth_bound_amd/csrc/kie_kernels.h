@@ -95,7 +95,8 @@ inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2
 // Launchers. dev_args: the argument block already copied to device memory.
 hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool prefill, int grid, hipStream_t s);
 // Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
-// per workgroup, whole rows per wave). Needs K <= kMaxInput.
+// per workgroup, a contiguous range of units per wave, row sums added into y,
+// which the caller zeroes). Needs K <= kMaxInput.
 hipError_t launch_gemv_stream(const GemvArgs& a, int grid, hipStream_t s);
 // Plain GEMV: one wave per 4 rows, all loads of a row block in flight.
 hipError_t launch_gemv_direct(const GemvArgs& a, hipStream_t s);

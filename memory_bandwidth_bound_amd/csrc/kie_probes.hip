@@ -10,84 +10,103 @@
 
 namespace kie {
 
-// Persistent GEMV with the decode kernel's weight streaming: every wave
-// streams whole rows (row r by global wave r mod 2048) through its own LDS
-// ring of kNS batches of kNB units filled by LDS DMA, consumes the oldest
-// batch after vmcnt((kNS-1)*kNB) and refills it at once. x (K <= 8192) is
-// staged in LDS; A has row stride lda; y = A x, or y += A x when accumulate.
+// Persistent GEMV with the decode kernel's weight streaming: wave gw of the
+// grid streams the contiguous unit range [U gw / W, U (gw + 1) / W) of the
+// row-major matrices (U units of 512 fp16 in all, W waves), through its own
+// LDS ring of kNS batches of kNB units filled by LDS DMA; it consumes the
+// oldest batch after vmcnt((kNS-1)*kNB) and refills it at once. Unit
+// positions (row, segment) advance by counting, without divisions per unit.
+// A row's partial sum is added to y[row] with a no-return atomic when the
+// row or the wave's range ends (y is zeroed by the caller); a row is split
+// over at most a few waves. x (K <= 8192) is staged in LDS; A has row stride
+// lda elements.
 __global__ void __launch_bounds__(512, 1) gemv_stream_kernel(GemvArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[8 * kNS * kBatchBytes];
     __shared__ __attribute__((aligned(16))) uint16_t xs[kMaxInput];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
-    const int nwaves = gridDim.x * 8;
-    const int gw = blockIdx.x * 8 + w;
+    const long nwaves = (long)gridDim.x * 8;
+    const long gw = (long)blockIdx.x * 8 + w;
     for (int i = threadIdx.x; i < a.K / 8; i += blockDim.x)
         lds_st16((KIE_LDS void*)(xs + 8 * i), *(const uint4*)(a.x + 8 * i));
     __syncthreads();
-    const long rows_total = (long)a.M * a.copies;
     const int upr = a.K / kUnitHalves;
-    const long my_rows = rows_total > gw ? (rows_total - gw + nwaves - 1) / nwaves : 0;
-    const long n = my_rows * upr;   // units of this wave
+    const long U = (long)a.M * a.copies * upr;
+    const long u0 = U * gw / nwaves;
+    const int n = (int)(U * (gw + 1) / nwaves - u0);   // units of this wave
     const uint32_t ring0 = lds_addr_of((KIE_LDS void*)ring) + (uint32_t)(w * kNS * kBatchBytes);
     const uint8_t* idle = a.idle + lane * 16;
-    long iu = 0;
-    auto unit_src = [&](long t) {
-        const long row = gw + (t / upr) * (long)nwaves;
-        return a.A + ((size_t)row * a.lda + (size_t)(t % upr) * kUnitHalves) * 2 + lane * 16;
-    };
-    auto fill = [&](uint32_t dst, long* u0, int* cnt) {
-        const long m = n - iu;
-        const int c = m < kNB ? (int)m : kNB;
-        *u0 = iu;
-        *cnt = c;
+    // fill cursor: next unit to load, as (row, segment) and its row's address
+    long frow = u0 / upr;
+    int fseg = (int)(u0 - frow * upr);
+    const uint8_t* fbase = a.A + (size_t)frow * a.lda * 2 + lane * 16;
+    int iu = 0;
+    auto fill = [&](uint32_t dst) {
+        const int c = (n - iu < kNB) ? n - iu : kNB;
 #pragma unroll
-        for (int s = 0; s < kNB; ++s)
-            dma_unit(s < c ? unit_src(iu + s) : idle + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+        for (int s = 0; s < kNB; ++s) {
+            if (s < c) {
+                dma_unit(fbase + (size_t)fseg * kUnitBytes, dst + s * kUnitBytes);
+                if (++fseg == upr) {
+                    fseg = 0;
+                    fbase += (size_t)a.lda * 2;
+                }
+            } else {
+                dma_unit(idle + (size_t)s * kUnitBytes, dst + s * kUnitBytes);
+            }
+        }
         iu += c;
+        return c;
     };
-    long su[kNS];
     int sn[kNS];
 #pragma unroll
-    for (int i = 0; i < kNS; ++i) fill(ring0 + i * kBatchBytes, &su[i], &sn[i]);
+    for (int i = 0; i < kNS; ++i) sn[i] = fill(ring0 + i * kBatchBytes);
+    // consume cursor
+    long crow = u0 / upr;
+    int cseg = (int)(u0 - crow * upr);
+    int left = n;
     int head = 0;
     float acc = 0.f;
     while (sn[0] > 0) {
         const uint32_t at = ring0 + head * kBatchBytes;
         wait_vm<(kNS - 1) * kNB>();
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)at + lane * 16;
+        // every LDS read of the batch first, then the products
+        uint4 wv[kNB], xv[kNB];
+        {
+            int sg = cseg;
+#pragma unroll
+            for (int s = 0; s < kNB; ++s) {
+                if (s < sn[0]) {
+                    wv[s] = lds_ld16(wb + s * kUnitBytes);
+                    xv[s] = lds_ld16((const KIE_LDS void*)(xs + sg * kUnitHalves + lane * 8));
+                    if (++sg == upr) sg = 0;
+                }
+            }
+        }
 #pragma unroll
         for (int s = 0; s < kNB; ++s) {
             if (s < sn[0]) {
-                const long t = su[0] + s;
-                const int c = (int)(t % upr);
-                acc = dot8(lds_ld16(wb + s * kUnitBytes), lds_ld16((const KIE_LDS void*)(xs + c * kUnitHalves + lane * 8)),
-                           acc);
-                if (c == upr - 1) {
+                acc = dot8(wv[s], xv[s], acc);
+                --left;
+                if (cseg == upr - 1 || left == 0) {
                     const float r = wave_sum_to_lane63(acc);
-                    if (lane == 63) {
-                        // stores and no-return atomics only: a load here would make the
-                        // compiler wait for every LDS DMA in flight
-                        float* yp = a.y + gw + (t / upr) * (long)nwaves;
-                        if (a.accumulate)
-                            __hip_atomic_fetch_add(gptr(yp), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        else
-                            *gptr(yp) = r;
-                    }
+                    // a no-return atomic: a load here would make the compiler wait for
+                    // every LDS DMA in flight
+                    if (lane == 63)
+                        __hip_atomic_fetch_add(gptr(a.y + crow), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     acc = 0.f;
+                }
+                if (++cseg == upr) {
+                    cseg = 0;
+                    ++crow;
                 }
             }
         }
         wait_lgkm0();
-        long u0;
-        int cnt;
-        fill(at, &u0, &cnt);
+        const int c = fill(at);
 #pragma unroll
-        for (int i = 0; i + 1 < kNS; ++i) {
-            su[i] = su[i + 1];
-            sn[i] = sn[i + 1];
-        }
-        su[kNS - 1] = u0;
-        sn[kNS - 1] = cnt;
+        for (int i = 0; i + 1 < kNS; ++i) sn[i] = sn[i + 1];
+        sn[kNS - 1] = c;
         head = (head + 1 == kNS) ? 0 : head + 1;
     }
     wait_vm0();
