@@ -108,11 +108,12 @@ def cpu_baseline_decode(cfg, W, prompt, target_s: float):
     t0 = time.perf_counter()
     dec.decode(1)
     t1 = time.perf_counter() - t0
-    n = int(max(2, min(64, round(target_s / max(t1, 1e-3)))))
+    start = (cfg.kv_prefill or cfg.prompt_len) + 1
+    room = cfg.max_seq - start          # positions left in the oracle's KV cache
+    n = int(max(1, min(64, room, round(target_s / max(t1, 1e-3)))))
     t0 = time.perf_counter()
     dec.decode(n)
     dt = time.perf_counter() - t0
-    start = (cfg.kv_prefill or cfg.prompt_len) + 1
     return {"value": n / dt, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{n} greedy decode passes of the {cfg.name} decoder at positions "
                       f"{start}..{start + n - 1} (numpy fp32 on fp16 weights), after one untimed pass; "

@@ -114,3 +114,18 @@ def test_bench_refuses_more_than_one_gpu(root_dir):
                        timeout=300)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_bench_cpu_baseline_stays_within_the_cache(root_dir):
+    """The oracle sample the benchmark times never runs past the workload's
+    KV capacity (the tiny decoder has 80 positions: 16 prompt + 64 decode)."""
+    import sys
+    sys.path.insert(0, root_dir)
+    import bench
+    cfg = synth.get_config("tiny")
+    line = bench.cpu_baseline_decode(cfg, synth.make_weights(cfg), synth.make_prompt(cfg), target_s=30.0)
+    first = cfg.prompt_len + 1
+    assert line["kind"] == "oracle" and line["value"] > 0
+    assert f"positions {first}..{cfg.max_seq - 1}" in line["sample"] or "passes" in line["sample"]
+    n = int(line["sample"].split()[0])
+    assert 1 <= n <= cfg.max_seq - first
