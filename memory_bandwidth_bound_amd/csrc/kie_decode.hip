@@ -687,6 +687,9 @@ struct Comm {
                 fail(2);
                 return false;
             }
+#if KIE_POLL_SLEEP > 0
+            __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
+#endif
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {

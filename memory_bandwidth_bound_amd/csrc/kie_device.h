@@ -264,6 +264,13 @@ __device__ __forceinline__ void dev_load128x8_sync(const void* k0, const void* k
 // Returns 0, or 1 when spin_limit polls went by, or 2 when *status became
 // non-zero (another workgroup gave up).
 constexpr int kGatherRegs = 16;     // words per lane per block (at most)
+// Back-off after a poll that found words still unpublished, in units of 64
+// clocks: a waiting workgroup re-reads its whole slice every trip, and with
+// most of the grid waiting on the last producers that traffic slows the ones
+// still streaming. 4 (256 clocks, a fraction of a poll trip) measured best.
+#ifndef KIE_POLL_SLEEP
+#define KIE_POLL_SLEEP 4
+#endif
 
 template <int R, class F>
 __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
@@ -285,6 +292,9 @@ __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint3
         if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
         if (++spins > spin_limit) return 1;
         if ((spins & 63) == 0 && dev_load32(status) != 0) return 2;
+#if KIE_POLL_SLEEP > 0
+        __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
+#endif
     }
 #pragma unroll
     for (int c = 0; c < R; ++c) {
