@@ -33,7 +33,9 @@ def _run(torch, A, x, variant):
 
 
 @pytest.mark.parametrize("variant", [0, 1])
-@pytest.mark.parametrize("shape", [(512, 2560, 3), (300, 1024, 2), (2560, 8192, 1), (257, 512, 2)])
+# (5, 8192, 2): 160 units over 2048 stream waves, so each 16-unit row is summed
+# from the partial sums of 16 waves
+@pytest.mark.parametrize("shape", [(512, 2560, 3), (300, 1024, 2), (2560, 8192, 1), (257, 512, 2), (5, 8192, 2)])
 def test_gemv_probe_matches_f64(torch_cuda, variant, shape):
     M, K, C = shape
     say(f"gemv probe variant={variant} M={M} K={K} copies={C}")
