@@ -20,6 +20,10 @@
 #define KIE_HD inline
 #endif
 
+#ifndef KIE_HEAD_MODE_MAX
+#define KIE_HEAD_MODE_MAX 1152
+#endif
+
 namespace kie {
 
 constexpr int kGrid = 256;                 // persistent workgroups: one per MI355X compute unit
@@ -27,6 +31,8 @@ constexpr int kUnitBytes = 1024;           // one 16-byte-per-lane load of a wav
 constexpr int kUnitHalves = 512;           // fp16 elements per unit
 constexpr int kMaxGroup = 8;               // query heads per KV head supported
 constexpr int kAttnChunkMin = 32;          // fewest positions per attention work item
+constexpr int kAttnHeadModeMax = KIE_HEAD_MODE_MAX;   // up to this many attended positions, one work
+                                           // item per (KV group, query head) over all positions
 constexpr int kMaxSeq = 65536;
 constexpr int kMaxRowsWg = 256;            // rows of one phase per workgroup
 constexpr int kMaxOwnRows = 32;            // residual rows per workgroup

@@ -88,6 +88,22 @@ __device__ __forceinline__ int attn_split(int c, int items, int* CH) {
     return ceil_div(c, *CH);
 }
 
+// Head mode (short context, groups of 2 to 8 query heads): one work item per
+// (KV group g, query head j of the group) attends all c positions, so its
+// result is final and no chunk states need combining. Work item i is
+// (g, j) = (i % Hkv, i / Hkv), as chunk i / Hkv of group i % Hkv otherwise.
+__device__ __forceinline__ bool head_mode(const Dims& D, int c) {
+    const int Gq = D.H / D.Hkv;
+    return Gq >= 2 && Gq <= kMaxGroup && c <= kAttnHeadModeMax;
+}
+
+// Attention work items (one workgroup each) for c attended positions.
+__device__ __forceinline__ int attn_items(const DecodeArgs& a, int c) {
+    if (head_mode(a.D, c)) return a.D.H;
+    int CH;
+    return a.D.Hkv * attn_split(c, a.items_per_head, &CH);
+}
+
 __device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
     return (a.flags & F_SKIP_LM) && step != a.n_steps - 1;
 }
@@ -95,10 +111,7 @@ __device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
 // Do this workgroup's waves meet at the two barriers of a phase? Every wave
 // evaluates the same test, so the barrier sequences match.
 __device__ __forceinline__ bool phase_bars(const DecodeArgs& a, int kind, int step, int wg) {
-    if (kind == K_ATTN) {
-        int CH;
-        return wg < a.D.Hkv * attn_split(a.pos0 + step + 1, a.items_per_head, &CH);
-    }
+    if (kind == K_ATTN) return wg < attn_items(a, a.pos0 + step + 1);
     if (kind == K_LM) return !lm_skipped(a, step);
     return is_gemv(kind);
 }
@@ -255,9 +268,12 @@ __device__ __forceinline__ void attn_merge(const DecodeArgs& a, KIE_LDS Smem* S,
     const int lane = lane_id(), wg = blockIdx.x;
     const int Gq = D.H / D.Hkv;
     int CH;
-    const int nper = attn_split(pos + 1, a.items_per_head, &CH);
-    const int g = wg % D.Hkv, chunk = wg / D.Hkv;
-    for (int idx = 2 * (w8 * 64 + lane); idx < Gq * HD; idx += 2 * 64 * kWaves) {
+    const bool hm = head_mode(D, pos + 1);
+    const int nper = hm ? 1 : attn_split(pos + 1, a.items_per_head, &CH);
+    const int g = wg % D.Hkv, chunk = hm ? 0 : wg / D.Hkv;
+    // head mode: this workgroup holds head wg / Hkv of the group only
+    const int i0 = hm ? (wg / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
+    for (int idx = i0 + 2 * (w8 * 64 + lane); idx < i1; idx += 2 * 64 * kWaves) {
         const int j = idx / HD, dd = idx % HD;
         float M = -3.0e38f;
 #pragma unroll
@@ -708,6 +724,7 @@ struct Comm {
     __device__ __forceinline__ void combine(int q, int pos) {
         const Dims& D = a.D;
         int CH;
+        if (head_mode(D, pos + 1)) return;   // every workgroup published its heads' o
         const int nper = attn_split(pos + 1, a.items_per_head, &CH);
         if (nper == 1 || wg >= D.Hkv * nper) return;
         const int Gq = D.H / D.Hkv, g = wg % D.Hkv, chunk = wg / D.Hkv;
@@ -975,7 +992,9 @@ struct Compute {
     __device__ __forceinline__ void finish() {
         const int kind = kind_of(a.D, cc);
         if (!phase_bars(a, kind, cc.step, wg)) return;
-        if (kind == K_ATTN && !stop) {
+        if (kind == K_ATTN && !stop && head_mode(a.D, a.pos0 + cc.step + 1)) {
+            attention<1>(cc.layer, a.pos0 + cc.step, wg / a.D.Hkv);   // one head, every position
+        } else if (kind == K_ATTN && !stop) {
             const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
             // register arrays sized for the group (1, 2, 4 or 5 heads; 6 to 8
             // heads in two passes over the positions)
@@ -1234,10 +1253,12 @@ struct Compute {
         constexpr int PPI = 64 / LPP;     // positions per wave instruction
         constexpr int U = 4;              // instructions per round
         int CH;
-        attn_split(pos + 1, a.items_per_head, &CH);
-        const int Gq = (D.H / D.Hkv - h0 < GB) ? D.H / D.Hkv - h0 : GB;   // heads h0 .. h0 + Gq - 1
-        const int g = wg % D.Hkv, chunk = wg / D.Hkv;
         const int c = pos + 1;
+        const bool hm = head_mode(D, c);
+        if (hm) CH = c;
+        else attn_split(c, a.items_per_head, &CH);
+        const int Gq = (D.H / D.Hkv - h0 < GB) ? D.H / D.Hkv - h0 : GB;   // heads h0 .. h0 + Gq - 1
+        const int g = wg % D.Hkv, chunk = hm ? 0 : wg / D.Hkv;
         const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
         const int gi = lane / LPP, dl = (lane % LPP) * 8;
         float qv[GB][8];
