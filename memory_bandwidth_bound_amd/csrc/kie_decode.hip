@@ -25,6 +25,8 @@
 //   per layer:  QKV | ATTN | COMB | WO | GU | DOWN               (dense FFN)
 //               QKV | ATTN | COMB | WO | ROUTER | EGU | EDOWN     (top-k MoE)
 //   then        LM | SAMPLE
+// Up to kAttnHeadModeMax attended positions, ATTN runs one workgroup per query
+// head over every position and publishes o itself; COMB then has no work.
 // There is no grid-wide barrier: a phase waits only for the words it reads.
 // A workgroup reads a phase's input only when it has work in that phase; then
 // every overwrite of a buffer it reads depends, through the words the
@@ -92,9 +94,11 @@ __device__ __forceinline__ int attn_split(int c, int items, int* CH) {
 // (KV group g, query head j of the group) attends all c positions, so its
 // result is final and no chunk states need combining. Work item i is
 // (g, j) = (i % Hkv, i / Hkv), as chunk i / Hkv of group i % Hkv otherwise.
+// (Configurations hold at most 128 query heads, since n_heads * head_dim is at
+// most 8192 and head_dim at least 64, so the items always fit the grid.)
 __device__ __forceinline__ bool head_mode(const Dims& D, int c) {
     const int Gq = D.H / D.Hkv;
-    return Gq >= 2 && Gq <= kMaxGroup && c <= kAttnHeadModeMax;
+    return Gq >= 2 && Gq <= kMaxGroup && D.H <= kGrid && c <= kAttnHeadModeMax;
 }
 
 // Attention work items (one workgroup each) for c attended positions.
