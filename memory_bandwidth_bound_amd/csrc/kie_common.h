@@ -23,6 +23,9 @@
 #ifndef KIE_HEAD_MODE_MAX
 #define KIE_HEAD_MODE_MAX 1152
 #endif
+#ifndef KIE_HEAD_CHUNK
+#define KIE_HEAD_CHUNK 384
+#endif
 
 namespace kie {
 
@@ -31,8 +34,9 @@ constexpr int kUnitBytes = 1024;           // one 16-byte-per-lane load of a wav
 constexpr int kUnitHalves = 512;           // fp16 elements per unit
 constexpr int kMaxGroup = 8;               // query heads per KV head supported
 constexpr int kAttnChunkMin = 32;          // fewest positions per attention work item
-constexpr int kAttnHeadModeMax = KIE_HEAD_MODE_MAX;   // up to this many attended positions, one work
-                                           // item per (KV group, query head) over all positions
+constexpr int kAttnHeadModeMax = KIE_HEAD_MODE_MAX;   // up to this many attended positions, work
+                                           // items per (KV group, query head)
+constexpr int kAttnHeadChunk = KIE_HEAD_CHUNK;   // most positions per head-mode work item
 constexpr int kMaxSeq = 65536;
 constexpr int kMaxRowsWg = 256;            // rows of one phase per workgroup
 constexpr int kMaxOwnRows = 32;            // residual rows per workgroup

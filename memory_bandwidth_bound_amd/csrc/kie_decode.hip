@@ -90,20 +90,31 @@ __device__ __forceinline__ int attn_split(int c, int items, int* CH) {
     return ceil_div(c, *CH);
 }
 
-// Head mode (short context, groups of 2 to 8 query heads): one work item per
-// (KV group g, query head j of the group) attends all c positions, so its
-// result is final and no chunk states need combining. Work item i is
-// (g, j) = (i % Hkv, i / Hkv), as chunk i / Hkv of group i % Hkv otherwise.
-// (Configurations hold at most 128 query heads, since n_heads * head_dim is at
-// most 8192 and head_dim at least 64, so the items always fit the grid.)
+// Head mode (short context, groups of 2 to 8 query heads): the work items of
+// query head h = (KV group h % Hkv, head h / Hkv of the group) split its c
+// positions into nch chunks of at most kAttnHeadChunk; item i is chunk
+// i / H of head i % H (so g = i % Hkv, as in the split over positions).
+// Chunk 0 combines the other chunks' states of its head and publishes o
+// itself: no combine phase over the grid. (Configurations hold at most 128
+// query heads, since n_heads * head_dim is at most 8192 and head_dim at least
+// 64, so the items fit the grid.)
 __device__ __forceinline__ bool head_mode(const Dims& D, int c) {
     const int Gq = D.H / D.Hkv;
     return Gq >= 2 && Gq <= kMaxGroup && D.H <= kGrid && c <= kAttnHeadModeMax;
 }
 
+// Chunks per head in head mode.
+__device__ __forceinline__ int head_chunks(const DecodeArgs& a, int c) {
+    int nch = ceil_div(c, kAttnHeadChunk);
+    const int cap = kGrid / a.D.H;
+    if (nch > cap) nch = cap;
+    if (nch > a.items_per_head) nch = a.items_per_head;
+    return nch;
+}
+
 // Attention work items (one workgroup each) for c attended positions.
 __device__ __forceinline__ int attn_items(const DecodeArgs& a, int c) {
-    if (head_mode(a.D, c)) return a.D.H;
+    if (head_mode(a.D, c)) return a.D.H * head_chunks(a, c);
     int CH;
     return a.D.Hkv * attn_split(c, a.items_per_head, &CH);
 }
@@ -267,16 +278,17 @@ __device__ __forceinline__ bool shared_gather(KIE_LDS Smem* S, int kind, int lay
 // whole row is here) or the chunk's partial state. Wave w8 of 8 takes every
 // 8th block of 64 (head, dim pair) slots.
 template <int HD>
-__device__ __forceinline__ void attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, int pos, uint32_t id, int w8) {
+__device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, int pos, uint32_t id, int w8) {
     const Dims& D = a.D;
     const int lane = lane_id(), wg = blockIdx.x;
     const int Gq = D.H / D.Hkv;
     int CH;
     const bool hm = head_mode(D, pos + 1);
-    const int nper = hm ? 1 : attn_split(pos + 1, a.items_per_head, &CH);
-    const int g = wg % D.Hkv, chunk = hm ? 0 : wg / D.Hkv;
-    // head mode: this workgroup holds head wg / Hkv of the group only
-    const int i0 = hm ? (wg / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
+    const int nch = hm ? head_chunks(a, pos + 1) : 1;
+    // head mode: chunk wg / H of head wg % H, whose states are all 1..nch-1 publish
+    const int nper = hm ? nch : attn_split(pos + 1, a.items_per_head, &CH);
+    const int g = wg % D.Hkv, chunk = hm ? wg / D.H : wg / D.Hkv;
+    const int i0 = hm ? ((wg % D.H) / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
     for (int idx = i0 + 2 * (w8 * 64 + lane); idx < i1; idx += 2 * 64 * kWaves) {
         const int j = idx / HD, dd = idx % HD;
         float M = -3.0e38f;
@@ -291,7 +303,35 @@ __device__ __forceinline__ void attn_merge(const DecodeArgs& a, KIE_LDS Smem* S,
             O1 += f * S->att_o[(w * kMaxGroup + j) * HD + dd + 1];
         }
         const int head = g * Gq + j;
-        if (nper == 1) {
+        if (hm && chunk == 0 && nch > 1) {
+            // head mode: fold in the other chunks' states of this head, then publish o
+            for (int k = 1; k < nch; ++k) {
+                const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + k) * (HD + 2);
+                uint64_t w0, w1, w2, w3;
+                uint32_t spins = 0;
+                while (true) {
+                    w0 = fw_load(pp);
+                    w1 = fw_load(pp + 1);
+                    w2 = fw_load(pp + 2 + dd);
+                    w3 = fw_load(pp + 3 + dd);
+                    const bool ok = fw_ok(w0, id) && fw_ok(w1, id) && fw_ok(w2, id) && fw_ok(w3, id);
+                    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+                    if (++spins > a.spin) return 1;
+                    if ((spins & 63) == 0 && dev_load32(a.status) != 0) return 2;
+#if KIE_POLL_SLEEP > 0
+                    __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
+#endif
+                }
+                const float m2 = __builtin_bit_cast(float, fw_val(w0)), l2 = __builtin_bit_cast(float, fw_val(w1));
+                const float Mn = fmaxf(M, m2);
+                const float f1 = __builtin_amdgcn_exp2f(M - Mn), f2 = __builtin_amdgcn_exp2f(m2 - Mn);
+                L = L * f1 + l2 * f2;
+                O0 = O0 * f1 + __builtin_bit_cast(float, fw_val(w2)) * f2;
+                O1 = O1 * f1 + __builtin_bit_cast(float, fw_val(w3)) * f2;
+                M = Mn;
+            }
+        }
+        if (nper == 1 || (hm && chunk == 0)) {
             // the whole row is here: publish o under the combine phase's id
             fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, O0 / L), id + 1);
             fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, O1 / L), id + 1);
@@ -305,6 +345,7 @@ __device__ __forceinline__ void attn_merge(const DecodeArgs& a, KIE_LDS Smem* S,
             }
         }
     }
+    return 0;
 }
 
 // ------------------------------------------------------------------------
@@ -567,9 +608,11 @@ struct Comm {
             }
             break;
         }
-        case K_ATTN:
-            attn_merge<HD>(a, S, pos, id, 0);   // the compute waves merge the other slices
+        case K_ATTN: {
+            const int r = attn_merge<HD>(a, S, pos, id, 0);   // the compute waves merge the other slices
+            if (r) fail(r);
             break;
+        }
         case K_WO:
         case K_DOWN:
         case K_EDOWN:
@@ -997,7 +1040,7 @@ struct Compute {
         const int kind = kind_of(a.D, cc);
         if (!phase_bars(a, kind, cc.step, wg)) return;
         if (kind == K_ATTN && !stop && head_mode(a.D, a.pos0 + cc.step + 1)) {
-            attention<1>(cc.layer, a.pos0 + cc.step, wg / a.D.Hkv);   // one head, every position
+            attention<1>(cc.layer, a.pos0 + cc.step, (wg % a.D.H) / a.D.Hkv);   // one head, one chunk
         } else if (kind == K_ATTN && !stop) {
             const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
             // register arrays sized for the group (1, 2, 4 or 5 heads; 6 to 8
@@ -1013,7 +1056,7 @@ struct Compute {
         }
         wg_barrier();   // partial sums / attention states are in LDS
         if (kind == K_ATTN) {
-            if (!stop) attn_merge<HD>(a, S, a.pos0 + cc.step, a.id0 + (uint32_t)cc.q, w + 1);
+            if (!stop) (void)attn_merge<HD>(a, S, a.pos0 + cc.step, a.id0 + (uint32_t)cc.q, w + 1);   // no polls here
             wg_barrier();
         }
     }
@@ -1259,10 +1302,10 @@ struct Compute {
         int CH;
         const int c = pos + 1;
         const bool hm = head_mode(D, c);
-        if (hm) CH = c;
+        if (hm) CH = ceil_div(c, head_chunks(a, c));
         else attn_split(c, a.items_per_head, &CH);
         const int Gq = (D.H / D.Hkv - h0 < GB) ? D.H / D.Hkv - h0 : GB;   // heads h0 .. h0 + Gq - 1
-        const int g = wg % D.Hkv, chunk = hm ? 0 : wg / D.Hkv;
+        const int g = wg % D.Hkv, chunk = hm ? wg / D.H : wg / D.Hkv;
         const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
         const int gi = lane / LPP, dl = (lane % LPP) * 8;
         float qv[GB][8];

@@ -40,9 +40,15 @@ CASES = {
     # 6 query heads per KV head, head_dim 128, one workgroup per query head
     "gqa6_hd128": synth.DecoderConfig(name="gqa6_hd128", n_layers=2, d_model=1024, n_heads=12, n_kv_heads=2,
                                       head_dim=128, ffn_dim=1024, vocab=3000, prompt_len=70, decode_steps=10),
-    # 4 query heads per KV head, 1137..1168 attended positions: the decode launch
-    # crosses the 1152-position limit of one workgroup per query head, and goes
-    # on with the split over positions and its combine
+    # 2 query heads per KV head, head_dim 64, 379..394 attended positions: each
+    # query head's positions go from one work item to two chunks of at most 384
+    # mid-launch, the first chunk's workgroup folding in the second's state
+    "gqa2_chunks_hd64": synth.DecoderConfig(name="gqa2_chunks_hd64", n_layers=2, d_model=512, n_heads=8,
+                                            n_kv_heads=4, head_dim=64, ffn_dim=1024, vocab=2048,
+                                            prompt_len=378, decode_steps=16),
+    # 4 query heads per KV head, 1137..1168 attended positions: three chunks per
+    # query head, then the launch crosses the 1152-position limit of work items
+    # per query head and goes on with the split over positions and its combine
     "gqa4_long_hd128": synth.DecoderConfig(name="gqa4_long_hd128", n_layers=2, d_model=512, n_heads=4,
                                            n_kv_heads=1, head_dim=128, ffn_dim=1024, vocab=2048,
                                            prompt_len=1136, decode_steps=32),
