@@ -46,6 +46,12 @@ CASES = {
     "gqa2_chunks_hd64": synth.DecoderConfig(name="gqa2_chunks_hd64", n_layers=2, d_model=512, n_heads=8,
                                             n_kv_heads=4, head_dim=64, ffn_dim=1024, vocab=2048,
                                             prompt_len=378, decode_steps=16),
+    # the 2.1B decoder's attention shape (20 query / 4 KV heads x 128, 5 per
+    # group) at 761..776 attended positions: two chunks per query head, then
+    # three from 769 on
+    "gqa5_chunks_hd128": synth.DecoderConfig(name="gqa5_chunks_hd128", n_layers=2, d_model=512, n_heads=20,
+                                             n_kv_heads=4, head_dim=128, ffn_dim=1024, vocab=2048,
+                                             prompt_len=760, decode_steps=16),
     # 4 query heads per KV head, 1137..1168 attended positions: three chunks per
     # query head, then the launch crosses the 1152-position limit of work items
     # per query head and goes on with the split over positions and its combine
