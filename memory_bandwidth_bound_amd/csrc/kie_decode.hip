@@ -25,8 +25,10 @@
 //   per layer:  QKV | ATTN | COMB | WO | GU | DOWN               (dense FFN)
 //               QKV | ATTN | COMB | WO | ROUTER | EGU | EDOWN     (top-k MoE)
 //   then        LM | SAMPLE
-// Up to kAttnHeadModeMax attended positions, ATTN runs one workgroup per query
-// head over every position and publishes o itself; COMB then has no work.
+// Up to kAttnHeadModeMax attended positions, ATTN runs per query head: its
+// positions in chunks of at most kAttnHeadChunk, one workgroup each, and the
+// first chunk's workgroup folds in the others' states and publishes o itself;
+// COMB then has no work.
 // There is no grid-wide barrier: a phase waits only for the words it reads.
 // A workgroup reads a phase's input only when it has work in that phase; then
 // every overwrite of a buffer it reads depends, through the words the
@@ -285,7 +287,8 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
     int CH;
     const bool hm = head_mode(D, pos + 1);
     const int nch = hm ? head_chunks(a, pos + 1) : 1;
-    // head mode: chunk wg / H of head wg % H, whose states are all 1..nch-1 publish
+    // head mode: this workgroup holds chunk wg / H of query head wg % H; chunks
+    // 1 .. nch-1 publish their states, chunk 0 combines them
     const int nper = hm ? nch : attn_split(pos + 1, a.items_per_head, &CH);
     const int g = wg % D.Hkv, chunk = hm ? wg / D.H : wg / D.Hkv;
     const int i0 = hm ? ((wg % D.H) / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
