@@ -16,7 +16,8 @@
  *    No exception crosses the ABI. kie_last_error() gives a message.
  *  - Host pointers are plain CPU memory owned by the caller. Device pointers
  *    are device memory owned by the caller (for example a torch tensor); the
- *    library never allocates or frees device memory.
+ *    library never allocates or frees device memory (kie_load takes one
+ *    64-byte word of pinned host memory for the watchdog, see kie_set_limits).
  *  - All device work is enqueued on the HIP stream given to kie_load (NULL =
  *    the default stream). Calls that return data to host buffers synchronise
  *    that stream before returning.
@@ -86,6 +87,9 @@ typedef struct kie_config {
  *  logits:    if non-NULL, [n][vocab] fp32 logits of every pass.
  *  experts:   if non-NULL (MoE only), [n][n_layers][top_k] selected expert
  *             ids of every pass, in descending router probability.
+ *  router:    if non-NULL (MoE only), [n][n_layers][n_experts] fp32 router
+ *             logits of every pass, the values the device ranked to choose
+ *             `experts` (larger first, ties to the lower expert index).
  *  trace:     if non-NULL, [KIE_TRACE_PHASES][256][4] int64 phase timeline of
  *             the call's first launch: for each of its first
  *             KIE_TRACE_PHASES phases (see kie_phases_per_pass) and each
@@ -102,6 +106,7 @@ typedef struct kie_debug {
     float* logits;
     int32_t* experts;
     int64_t* trace;
+    float* router;
 } kie_debug;
 
 /* Phases of one forward pass: n_layers * (6 dense | 7 MoE) + 2, in the order
@@ -151,9 +156,15 @@ int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_t
 
 /*
  * Store already-rotated keys and values for positions 0..n_pos-1 directly in
- * the cache (host fp16 arrays [n_layers][n_pos][n_kv_heads][head_dim]), set
- * the position to n_pos and the pending token to pending_token. Used to start
- * decoding at long context without a prefill.
+ * the cache (host fp16 arrays [n_layers][n_pos][n_kv_heads][head_dim], each
+ * n_layers*n_pos*n_kv_heads*head_dim elements; read, not kept), set the
+ * position to n_pos and the pending token to pending_token. Every other
+ * cache entry is zeroed. Used to start decoding at long context without a
+ * prefill: the paper-digest.app digest ("Core Mechanics") counts the key and
+ * value bytes of the context next to the weights in the bytes each decoded
+ * token must read, so a long cache is a workload of its own. KIE_ERR_ARG for
+ * null arrays, a negative n_pos or a token outside [0, vocab);
+ * KIE_ERR_CAPACITY if n_pos > max_seq.
  */
 int kie_set_kv(kie_model* m, const void* k_fp16, const void* v_fp16, int32_t n_pos,
                int32_t pending_token);
@@ -169,19 +180,47 @@ int kie_decode(kie_model* m, int32_t n_tokens, int32_t* out_ids, const kie_debug
 
 /* Move back to an earlier position pos (0 <= pos <= current) with the given
  * pending token; cache entries at positions >= pos are overwritten by later
- * passes. Lets a benchmark repeat the same decode request. */
+ * passes, and the attention of a pass never reads beyond its own position
+ * (the causal decode of the news.creeta.com monokernel article, "Inside the
+ * monokernel": each step attends over the cached keys and values so far).
+ * Lets a benchmark repeat the same decode request. No device work.
+ * KIE_ERR_ARG if pos is out of range or the token outside [0, vocab). */
 int kie_rewind(kie_model* m, int32_t pos, int32_t pending_token);
 
-/* Clear the KV cache and device state; position 0, no pending token. */
+/* Clear the KV cache and the exchange words on the model's stream (and wait
+ * for it); position 0, no pending token. The state a request starts from in
+ * the pages' batch-1 decode (paper-digest.app digest, "Core Mechanics": one
+ * request, no batching). Also the way back after KIE_ERR_TIMEOUT. */
 int kie_reset(kie_model* m);
 
-/* Current position and pending token (-1 if none). */
+/* Current position and pending token (-1 if none), both host-side values:
+ * the decode loop's state between calls (news.creeta.com monokernel
+ * article, "Inside the monokernel": the position advances on the device
+ * inside a launch and is handed back at its end). KIE_ERR_ARG on a null
+ * argument. */
 int kie_state(const kie_model* m, int32_t* pos, int32_t* pending_token);
 
 /* Device time in milliseconds of the last kernel launch made by
  * kie_decode/kie_prefill, measured with HIP events on the model's stream
  * around that one launch. */
 float kie_last_kernel_ms(const kie_model* m);
+
+/*
+ * Failure detection (not from the pages: the persistent kernel's workgroups
+ * wait on each other, so a broken dependency must end in an error, not a
+ * hang). spin_limit: polls a device-side wait makes before it gives up
+ * (0 = the default, 2^22); the workgroup then flags the failure, every other
+ * workgroup's waits give up too and the kernel exits; the call returns
+ * KIE_ERR_TIMEOUT. watchdog_ms: the host's wall-clock limit per launch
+ * (0 = automatic: 10 s plus 20 ms per pass; < 0 = none). The host polls the
+ * launch's completion; past the limit it raises a word in pinned host memory
+ * (allocated by kie_load, 64 bytes) that the kernel's waits read once they
+ * have polled in vain, lets the launch end and returns KIE_ERR_TIMEOUT. A
+ * launch still making progress is not cut short; its overrun is reported the
+ * same way. Applies to later kie_prefill / kie_decode calls. KIE_ERR_ARG for a
+ * null model.
+ */
+int kie_set_limits(kie_model* m, uint32_t spin_limit, int32_t watchdog_ms);
 
 /* Workgroups of the persistent grid (one per compute unit). */
 int32_t kie_grid_size(const kie_model* m);

@@ -7,6 +7,7 @@
 
 #include <chrono>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/kie.h"
@@ -25,8 +26,21 @@ struct kie_model {
     uint32_t id_next;   // phase id of the next launch's first phase (ids never repeat)
     hipEvent_t ev0, ev1;
     float last_ms;
+    uint32_t spin_limit;    // polls before a device-side wait gives up
+    int32_t watchdog_ms;    // host limit per launch: 0 automatic, < 0 none
+    uint32_t* habort;       // pinned host word the kernel's long waits read
     std::string err;
 };
+
+constexpr uint32_t kDefaultSpin = 1u << 22;
+
+// Wall-clock limit of one launch of n passes: the automatic limit allows
+// 10 s plus 20 ms per pass (a pass takes about 1.3 ms on the ~2.1B decoder).
+static double watchdog_limit_ms(const kie_model* m, int n) {
+    if (m->watchdog_ms < 0) return -1.0;
+    if (m->watchdog_ms > 0) return (double)m->watchdog_ms;
+    return 10000.0 + 20.0 * n;
+}
 
 static thread_local std::string g_err;
 
@@ -146,6 +160,9 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     m->id_next = 1;
     m->last_ms = 0.f;
     m->ev0 = m->ev1 = nullptr;
+    m->spin_limit = kDefaultSpin;
+    m->watchdog_ms = 0;
+    m->habort = nullptr;
     if (ws_bytes < m->lay.total) {
         rc = fail(nullptr, KIE_ERR_WORKSPACE, "workspace smaller than kie_workspace_bytes()");
         delete m;
@@ -198,10 +215,14 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     if ((rc = clear_state(m, true)) != KIE_OK) return bail(rc);
     hipError_t e = hipEventCreate(&m->ev0);
     if (e == hipSuccess) e = hipEventCreate(&m->ev1);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&m->habort, 64, hipHostMallocDefault);
     if (e != hipSuccess) {
-        hip_fail(m, e, "hipEventCreate");
+        hip_fail(m, e, "hipEventCreate / hipHostMalloc");
+        if (m->ev0) (void)hipEventDestroy(m->ev0);
+        if (m->ev1) (void)hipEventDestroy(m->ev1);
         return bail(KIE_ERR_HIP);
     }
+    __atomic_store_n(m->habort, 0u, __ATOMIC_SEQ_CST);
     *out = m;
     return KIE_OK;
 }
@@ -210,10 +231,10 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
 // of pass i where force[i] >= 0. One launch unless debug rows are requested,
 // then launches of at most kDebugRows passes.
 static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_ids, float* dbg_logits,
-                      int32_t* dbg_experts, int64_t* trace, bool skip_lm) {
+                      int32_t* dbg_experts, float* dbg_router, int64_t* trace, bool skip_lm) {
     const Layout& L = m->lay;
     const Dims& D = L.D;
-    const bool debug = dbg_logits || dbg_experts;
+    const bool debug = dbg_logits || dbg_experts || dbg_router;
     const int chunk = debug ? kDebugRows : n;
     int tok = m->pending;
     for (int s0 = 0; s0 < n; s0 += chunk) {
@@ -233,7 +254,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.D = D;
         a.eps = m->cfg.rms_eps;
         a.items_per_head = L.attn_items_per_head;
-        a.spin = 1u << 22;
+        a.spin = m->spin_limit;
         a.layers = m->ws + L.off_layers;
         a.layer_bytes = L.layer_bytes;
         a.lm = m->ws + L.off_lm;
@@ -251,30 +272,56 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.ex.r = (uint64_t*)(m->ws + L.off_ex_r);
         a.ex.am = (uint64_t*)(m->ws + L.off_ex_am);
         a.status = (uint32_t*)(m->ws + L.off_status);
+        a.habort = m->habort;
         a.out_ids = (int32_t*)(m->ws + L.off_out);
         a.force_ids = (const int32_t*)(m->ws + L.off_force);
         a.dbg_logits = (float*)(m->ws + L.off_dbg_logits);
         a.dbg_experts = (int32_t*)(m->ws + L.off_dbg_experts);
+        a.dbg_router = (float*)(m->ws + L.off_dbg_router);
         a.plan = (const int32_t*)(m->ws + L.off_plan);
         a.idle = m->ws + L.off_idle;
         a.trace = (int64_t*)(m->ws + L.off_trace);
         a.pos0 = m->pos + s0;
         a.pending = tok;
         a.n_steps = nc;
-        a.flags = (force ? F_FORCE : 0) | (dbg_logits ? F_DBG_LOGITS : 0) | (dbg_experts ? F_DBG_EXPERTS : 0) |
+        a.flags = (force ? F_FORCE : 0) | (dbg_logits ? F_DBG_LOGITS : 0) | ((dbg_experts || dbg_router) ? F_DBG_EXPERTS : 0) |
                   ((skip_lm && !debug) ? F_SKIP_LM : 0) | ((trace && s0 == 0) ? F_TRACE : 0);
         a.id0 = m->id_next;
         m->id_next += nphase;
         static_assert(sizeof(DecodeArgs) <= 4096, "argument block");
         static_assert(KIE_TRACE_PHASES == kTracePhases, "trace length");
         HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
+        __atomic_store_n(m->habort, 0u, __ATOMIC_SEQ_CST);
         HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
         HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, skip_lm, kGrid, m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
-        HIP_TRY(m, hipEventSynchronize(m->ev1));
+        // Host watchdog: poll the launch's end event against a wall-clock
+        // limit. Past it, raise the host word the kernel's long waits read
+        // (workgroups that wait on each other then give up and exit), let the
+        // launch end and report KIE_ERR_TIMEOUT. A kernel that still makes
+        // progress runs to its end; the overrun is reported all the same.
+        const double limit = watchdog_limit_ms(m, nc);
+        const auto t0 = std::chrono::steady_clock::now();
+        bool fired = false;
+        while (true) {
+            hipError_t q = hipEventQuery(m->ev1);
+            if (q == hipSuccess) break;
+            if (q != hipErrorNotReady) return hip_fail(m, q, "hipEventQuery");
+            const double el = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+            if (!fired && limit >= 0.0 && el > limit) {
+                __atomic_store_n(m->habort, 1u, __ATOMIC_SEQ_CST);
+                fired = true;
+            }
+            if (el < 5.0) std::this_thread::yield();   // short launches: no sleep granularity
+            else std::this_thread::sleep_for(std::chrono::microseconds(20));
+        }
         HIP_TRY(m, hipEventElapsedTime(&m->last_ms, m->ev0, m->ev1));
         uint32_t status = 0;
         HIP_TRY(m, hipMemcpy(&status, m->ws + L.off_status, 4, hipMemcpyDeviceToHost));
+        if (fired) {
+            m->pending = -1;
+            return fail(m, KIE_ERR_TIMEOUT, "the launch exceeded the host watchdog's wall-clock limit");
+        }
         if (status != 0) {
             m->pending = -1;
             return fail(m, KIE_ERR_TIMEOUT, "a device-side wait for another workgroup hit its spin limit");
@@ -286,6 +333,9 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         if (dbg_experts)
             HIP_TRY(m, hipMemcpy(dbg_experts + (size_t)s0 * D.L * D.topk, m->ws + L.off_dbg_experts,
                                  (size_t)nc * D.L * D.topk * 4, hipMemcpyDeviceToHost));
+        if (dbg_router)
+            HIP_TRY(m, hipMemcpy(dbg_router + (size_t)s0 * D.L * D.E, m->ws + L.off_dbg_router,
+                                 (size_t)nc * D.L * D.E * 4, hipMemcpyDeviceToHost));
         if (trace && s0 == 0) {
             size_t np = (size_t)nphase < (size_t)kTracePhases ? (size_t)nphase : (size_t)kTracePhases;
             HIP_TRY(m, hipMemcpy(trace, m->ws + L.off_trace, np * kGrid * 4 * 8, hipMemcpyDeviceToHost));
@@ -304,7 +354,8 @@ int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_t
     if (n > m->cfg.max_seq) return fail(m, KIE_ERR_CAPACITY, "prompt longer than max_seq");
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "prompt token out of range");
-    if (dbg && dbg->experts && m->cfg.n_experts == 0) return fail(m, KIE_ERR_ARG, "experts requested for a dense model");
+    if (dbg && (dbg->experts || dbg->router) && m->cfg.n_experts == 0)
+        return fail(m, KIE_ERR_ARG, "experts or router logits requested for a dense model");
     std::vector<int32_t> force(n);
     for (int i = 0; i + 1 < n; ++i) force[i] = tokens[i + 1];
     force[n - 1] = -1;
@@ -312,7 +363,7 @@ int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_t
     m->pos = 0;
     m->pending = tokens[0];
     int rc = run_passes(m, n, force.data(), ids.data(), dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr,
-                        dbg ? dbg->trace : nullptr, true);
+                        dbg ? dbg->router : nullptr, dbg ? dbg->trace : nullptr, true);
     if (rc != KIE_OK) return rc;
     *first_token = ids[n - 1];
     return KIE_OK;
@@ -323,13 +374,14 @@ int kie_decode(kie_model* m, int32_t n, int32_t* out_ids, const kie_debug* dbg) 
     if (!out_ids || n < 1) return fail(m, KIE_ERR_ARG, "need n_tokens >= 1 and an output buffer");
     if (m->pending < 0) return fail(m, KIE_ERR_STATE, "no pending token: call kie_prefill or kie_set_kv first");
     if ((long)m->pos + n > m->cfg.max_seq) return fail(m, KIE_ERR_CAPACITY, "position + n_tokens exceeds max_seq");
-    if (dbg && dbg->experts && m->cfg.n_experts == 0) return fail(m, KIE_ERR_ARG, "experts requested for a dense model");
+    if (dbg && (dbg->experts || dbg->router) && m->cfg.n_experts == 0)
+        return fail(m, KIE_ERR_ARG, "experts or router logits requested for a dense model");
     const int32_t* force = dbg ? dbg->force_ids : nullptr;
     if (force)
         for (int i = 0; i < n; ++i)
             if (force[i] >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "forced token out of range");
     return run_passes(m, n, force, out_ids, dbg ? dbg->logits : nullptr, dbg ? dbg->experts : nullptr,
-                      dbg ? dbg->trace : nullptr, false);
+                      dbg ? dbg->router : nullptr, dbg ? dbg->trace : nullptr, false);
 }
 
 int kie_set_kv(kie_model* m, const void* k, const void* v, int32_t n_pos, int32_t pending) {
@@ -391,10 +443,18 @@ int kie_state(const kie_model* m, int32_t* pos, int32_t* pending) {
 float kie_last_kernel_ms(const kie_model* m) { return m ? m->last_ms : 0.f; }
 int32_t kie_grid_size(const kie_model* m) { return m ? kGrid : 0; }
 
+int kie_set_limits(kie_model* m, uint32_t spin_limit, int32_t watchdog_ms) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    m->spin_limit = spin_limit ? spin_limit : kDefaultSpin;
+    m->watchdog_ms = watchdog_ms;
+    return KIE_OK;
+}
+
 void kie_free(kie_model* m) {
     if (!m) return;
     if (m->ev0) (void)hipEventDestroy(m->ev0);
     if (m->ev1) (void)hipEventDestroy(m->ev1);
+    if (m->habort) (void)hipHostFree(m->habort);
     delete m;
 }
 

@@ -258,7 +258,7 @@ __device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S
     const uint64_t* src = kind == K_WO ? a.ex.o : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
     const int i0 = n * w / kWaves, i1 = n * (w + 1) / kWaves;
     float ss = 0.f;
-    const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, [&](int i, uint32_t v) {
+    const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, a.habort, [&](int i, uint32_t v) {
         const float x = __builtin_bit_cast(float, v);
         ss += x * x;
         stage1(S, i0 + i, x);
@@ -320,7 +320,7 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
                     const bool ok = fw_ok(w0, id) && fw_ok(w1, id) && fw_ok(w2, id) && fw_ok(w3, id);
                     if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
                     if (++spins > a.spin) return 1;
-                    if ((spins & 63) == 0 && dev_load32(a.status) != 0) return 2;
+                    if ((spins & 63) == 0 && stop_requested(a.status, a.habort)) return 2;
 #if KIE_POLL_SLEEP > 0
                     __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
 #endif
@@ -385,7 +385,7 @@ struct Comm {
     template <class F>
     __device__ __forceinline__ bool gather(const uint64_t* src, int n, uint32_t id, F f) {
         if (dead) return false;
-        const int r = fw_gather(src, n, id, a.spin, a.status, f);
+        const int r = fw_gather(src, n, id, a.spin, a.status, a.habort, f);
         if (r) fail(r);
         return r == 0;
     }
@@ -450,6 +450,9 @@ struct Comm {
         KIE_LDS float* lg = S->att_q;   // scratch (E <= 1024): no attention is running
         if (!gather(a.ex.r, E, id_of(q - 1), [&](int i, uint32_t v) { lg[i] = __builtin_bit_cast(float, v); }))
             return;
+        if ((a.flags & F_DBG_EXPERTS) && wg == 0)
+            for (int e = lane; e < E; e += 64)
+                gptr(a.dbg_router)[((size_t)(it.step % 64) * D.L + it.layer) * E + e] = lg[e];
         float mx = -3.0e38f;
         for (int e = lane; e < E; e += 64) mx = fmaxf(mx, lg[e]);
         mx = wave_max(mx);
@@ -749,7 +752,7 @@ struct Comm {
                 fail(1);
                 return false;
             }
-            if ((spins & 63) == 0 && dev_load32(a.status) != 0) {
+            if ((spins & 63) == 0 && stop_requested(a.status, a.habort)) {
                 fail(2);
                 return false;
             }

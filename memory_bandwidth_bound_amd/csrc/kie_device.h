@@ -251,6 +251,16 @@ __device__ __forceinline__ void dev_load128x8_sync(const void* k0, const void* k
         : "memory");
 }
 
+// Should a waiting wave give up? *status is set by a workgroup that timed out;
+// *habort (host memory, may be null) by the host's watchdog. Read only by
+// waits that have already polled in vain many times, so the host round trip
+// is off every normal path.
+__device__ __forceinline__ bool stop_requested(const uint32_t* status, const uint32_t* habort) {
+    if (dev_load32(status) != 0) return true;
+    return habort &&
+           __hip_atomic_load(gptr(const_cast<uint32_t*>(habort)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0;
+}
+
 // Wait until words [0, n) of src all carry `id`, then call f(i, payload) for
 // every word (lane l handles i = l, l + 64, ...). One wave calls this.
 //
@@ -261,8 +271,8 @@ __device__ __forceinline__ void dev_load128x8_sync(const void* k0, const void* k
 // what the previous poll returned would sit in divergent branches, where the
 // compiler's wait counting gives up and waits after each load, one trip
 // through the memory pipeline per load instead of one per poll.
-// Returns 0, or 1 when spin_limit polls went by, or 2 when *status became
-// non-zero (another workgroup gave up).
+// Returns 0, or 1 when spin_limit polls went by, or 2 when stop_requested()
+// (another workgroup gave up, or the host's watchdog fired).
 constexpr int kGatherRegs = 16;     // words per lane per block (at most)
 // Back-off after a poll that found words still unpublished, in units of 64
 // clocks: a waiting workgroup re-reads its whole slice every trip, and with
@@ -274,7 +284,8 @@ constexpr int kGatherRegs = 16;     // words per lane per block (at most)
 
 template <int R, class F>
 __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
-                                               const uint32_t* status, uint32_t& spins, F& f) {
+                                               const uint32_t* status, const uint32_t* habort, uint32_t& spins,
+                                               F& f) {
     const int lane = lane_id();
     const uint64_t* p[R];
 #pragma unroll
@@ -291,7 +302,7 @@ __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint3
         for (int c = 0; c < R; ++c) ok = fw_ok(x[c], id) && ok;
         if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
         if (++spins > spin_limit) return 1;
-        if ((spins & 63) == 0 && dev_load32(status) != 0) return 2;
+        if ((spins & 63) == 0 && stop_requested(status, habort)) return 2;
 #if KIE_POLL_SLEEP > 0
         __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
 #endif
@@ -306,17 +317,17 @@ __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint3
 
 template <class F>
 __device__ __forceinline__ int fw_gather(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
-                                         const uint32_t* status, F f) {
+                                         const uint32_t* status, const uint32_t* habort, F f) {
     uint32_t spins = 0;
     for (int base = 0; base < n; base += 64 * kGatherRegs) {
         const int m = (n - base < 64 * kGatherRegs) ? n - base : 64 * kGatherRegs;
         const int per = (m + 63) / 64;
         auto g = [&](int i, uint32_t v) { f(base + i, v); };
         int r;
-        if (per <= 2) r = fw_gather_block<2>(src + base, m, id, spin_limit, status, spins, g);
-        else if (per <= 4) r = fw_gather_block<4>(src + base, m, id, spin_limit, status, spins, g);
-        else if (per <= 8) r = fw_gather_block<8>(src + base, m, id, spin_limit, status, spins, g);
-        else r = fw_gather_block<16>(src + base, m, id, spin_limit, status, spins, g);
+        if (per <= 2) r = fw_gather_block<2>(src + base, m, id, spin_limit, status, habort, spins, g);
+        else if (per <= 4) r = fw_gather_block<4>(src + base, m, id, spin_limit, status, habort, spins, g);
+        else if (per <= 8) r = fw_gather_block<8>(src + base, m, id, spin_limit, status, habort, spins, g);
+        else r = fw_gather_block<16>(src + base, m, id, spin_limit, status, habort, spins, g);
         if (r) return r;
     }
     return 0;

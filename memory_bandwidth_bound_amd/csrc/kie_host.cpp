@@ -145,6 +145,7 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_force = take((size_t)D.max_seq * 4);
     Y.off_dbg_logits = take((size_t)kDebugRows * D.V * 4);
     Y.off_dbg_experts = take((size_t)kDebugRows * D.L * (D.topk ? D.topk : 1) * 4);
+    Y.off_dbg_router = take((size_t)kDebugRows * D.L * (D.E ? D.E : 1) * 4);
     Y.off_plan = take((size_t)2 * (kGrid + 1) * 4);
     Y.off_args = take(4096);
     Y.off_idle = take(16384);

@@ -41,6 +41,7 @@ struct Layout {
     size_t off_force;             // i32 [max_seq]
     size_t off_dbg_logits;        // f32 [kDebugRows][V]
     size_t off_dbg_experts;       // i32 [kDebugRows][L][topk]
+    size_t off_dbg_router;        // f32 [kDebugRows][L][E] (MoE router logits)
     size_t off_plan;              // i32 piece_off[kGrid+1], lm_off[kGrid+1]
     size_t off_args;              // kernel argument block (4 KiB)
     size_t off_idle;              // 16 KiB read by weight batches that have nothing to stream

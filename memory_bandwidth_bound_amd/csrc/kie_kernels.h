@@ -30,7 +30,7 @@ constexpr int kMaxIn = kMaxInput;
 enum : int {
     F_FORCE = 1,        // force_ids drives the next input where >= 0
     F_DBG_LOGITS = 2,   // write every pass's logits to dbg_logits
-    F_DBG_EXPERTS = 4,  // write every pass's expert ids to dbg_experts
+    F_DBG_EXPERTS = 4,  // write every pass's expert ids and router logits to dbg_experts, dbg_router
     F_SKIP_LM = 8,      // skip the LM head on every pass but the last (prefill)
     F_TRACE = 16        // record the phase timeline in trace
 };
@@ -65,10 +65,12 @@ struct DecodeArgs {
     uint16_t* vc;
     Exchange ex;
     uint32_t* status;
+    const uint32_t* habort;  // host memory: non-zero once the host's watchdog fired (may be null)
     int32_t* out_ids;
     const int32_t* force_ids;
     float* dbg_logits;
     int32_t* dbg_experts;
+    float* dbg_router;
     const int32_t* plan;     // piece_off[kGrid+1], lm_off[kGrid+1]
     const uint8_t* idle;     // kIdleBytes of zeros: target of loads that keep a batch slot busy
     int64_t* trace;          // [kTracePhases][kGrid][4] phase timeline (F_TRACE)

@@ -33,7 +33,8 @@ class KieConfig(ctypes.Structure):
 
 class KieDebug(ctypes.Structure):
     _fields_ = [("force_ids", POINTER(c_int32)), ("logits", POINTER(c_float)),
-                ("experts", POINTER(c_int32)), ("trace", POINTER(ctypes.c_int64))]
+                ("experts", POINTER(c_int32)), ("trace", POINTER(ctypes.c_int64)),
+                ("router", POINTER(c_float))]
 
 
 class KieError(RuntimeError):
@@ -71,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_last_kernel_ms": (c_float, [c_void_p]),
         "kie_grid_size": (c_int32, [c_void_p]),
         "kie_free": (None, [c_void_p]),
+        "kie_set_limits": (c_int32, [c_void_p, ctypes.c_uint32, c_int32]),
         "kie_last_error": (ctypes.c_char_p, [c_void_p]),
         "kie_status_str": (ctypes.c_char_p, [c_int32]),
         "kie_gemv_probe": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
@@ -99,6 +101,58 @@ def make_config(cfg) -> KieConfig:
     return KieConfig(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                      cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k if cfg.n_experts else 0,
                      cfg.rms_eps, cfg.rope_theta, cfg.max_seq)
+
+
+def expected_shapes(cfg):
+    """Shapes of kie_load's tensors in the canonical order include/kie.h
+    documents (row-major [out][in] matrices, [d] gains)."""
+    d, q, kv, f = cfg.d_model, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.ffn_dim
+    shapes = [(cfg.vocab, d)]
+    for _ in range(cfg.n_layers):
+        shapes += [(d,), (q, d), (kv, d), (kv, d), (d, q), (d,)]
+        if cfg.n_experts:
+            shapes.append((cfg.n_experts, d))
+            shapes += [(f, d), (f, d), (d, f)] * cfg.n_experts
+        else:
+            shapes += [(f, d), (f, d), (d, f)]
+    return shapes + [(d,), (cfg.vocab, d)]
+
+
+def check_tensors(cfg, tensors) -> None:
+    """Raise KieError(KIE_ERR_ARG) unless ``tensors`` are fp16 arrays of the
+    canonical shapes: the library reads exactly that many bytes from each."""
+    want = expected_shapes(cfg)
+    if len(tensors) != len(want):
+        raise KieError(-1, f"expected {len(want)} tensors, got {len(tensors)}")
+    for i, (t, s) in enumerate(zip(tensors, want)):
+        if getattr(t, "dtype", None) != np.float16:
+            raise KieError(-1, f"tensor {i}: dtype {getattr(t, 'dtype', type(t))}, expected float16")
+        if tuple(t.shape) != s:
+            raise KieError(-1, f"tensor {i}: shape {tuple(t.shape)}, expected {s}")
+
+
+def check_kv(cfg, K, V) -> int:
+    """Raise KieError(KIE_ERR_ARG) unless K and V are fp16 [n_layers][n_pos]
+    [n_kv_heads][head_dim] of the same shape; returns n_pos."""
+    for name, a in (("K", K), ("V", V)):
+        if getattr(a, "dtype", None) != np.float16:
+            raise KieError(-1, f"{name}: dtype {getattr(a, 'dtype', type(a))}, expected float16")
+        if a.ndim != 4 or a.shape[0] != cfg.n_layers or a.shape[2:] != (cfg.n_kv_heads, cfg.head_dim):
+            raise KieError(-1, f"{name}: shape {a.shape}, expected ({cfg.n_layers}, n_pos, "
+                               f"{cfg.n_kv_heads}, {cfg.head_dim})")
+    if K.shape != V.shape:
+        raise KieError(-1, f"K shape {K.shape} != V shape {V.shape}")
+    return int(K.shape[1])
+
+
+def check_tokens(tokens, n: int, name: str) -> np.ndarray:
+    """A 1-D int32 copy of at least n token ids (raises KieError otherwise)."""
+    t = np.asarray(tokens)
+    if t.ndim != 1 or (t.size and not np.issubdtype(t.dtype, np.integer)):
+        raise KieError(-1, f"{name} must be a 1-D array of integer token ids")
+    if t.size < n:
+        raise KieError(-1, f"{name} holds {t.size} tokens, {n} needed")
+    return np.ascontiguousarray(t[:n] if n else t, dtype=np.int32)
 
 
 def workspace_bytes(cfg) -> int:
@@ -137,7 +191,8 @@ class Model:
         n = int(lib.kie_tensor_count(ctypes.byref(kc)))
         if n != len(tensors):
             raise KieError(-1, f"expected {n} tensors, got {len(tensors)}")
-        host = [np.ascontiguousarray(t, dtype=np.float16) for t in tensors]
+        check_tensors(cfg, tensors)
+        host = [np.ascontiguousarray(t) for t in tensors]
         ptrs = (c_void_p * n)(*[t.ctypes.data for t in host])
         with torch.cuda.device(self.device):
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
@@ -150,11 +205,11 @@ class Model:
         self._lib = lib
 
     # ---- calls -------------------------------------------------------------
-    def _dbg(self, n, force, logits, experts):
+    def _dbg(self, n, force, logits, experts, router=False):
         dbg = KieDebug()
         keep = {}
         if force is not None:
-            f = np.ascontiguousarray(force, dtype=np.int32)
+            f = check_tokens(force, n, "force")
             keep["force"] = f
             dbg.force_ids = _i32p(f)
         if logits:
@@ -165,26 +220,37 @@ class Model:
             ex = np.zeros((n, self.cfg.n_layers, self.cfg.top_k), dtype=np.int32)
             keep["experts"] = ex
             dbg.experts = _i32p(ex)
+        if router:
+            rt = np.zeros((n, self.cfg.n_layers, self.cfg.n_experts), dtype=np.float32)
+            keep["router"] = rt
+            dbg.router = rt.ctypes.data_as(POINTER(c_float))
         return dbg, keep
 
-    def prefill(self, tokens, logits: bool = False, experts: bool = False):
-        """Returns (first token, logits [n][vocab] or None, experts or None)."""
-        t = np.ascontiguousarray(tokens, dtype=np.int32)
+    def prefill(self, tokens, logits: bool = False, experts: bool = False, router: bool = False):
+        """Returns (first token, logits [n][vocab] or None, experts or None).
+        With router=True the router logits [n][n_layers][n_experts] of the
+        passes are left in ``last_router``."""
+        t = check_tokens(tokens, 0, "tokens")
         first = c_int32()
-        dbg, keep = self._dbg(len(t), None, logits, experts)
+        dbg, keep = self._dbg(len(t), None, logits, experts, router)
         with self._torch.cuda.device(self.device):
             rc = self._lib.kie_prefill(self._h, _i32p(t), len(t), ctypes.byref(first),
                                        ctypes.byref(dbg) if keep else None)
         _check(rc, self._h)
+        self.last_router = keep.get("router")
         return first.value, keep.get("logits"), keep.get("experts")
 
-    def decode(self, n: int, force=None, logits: bool = False, experts: bool = False):
-        """Returns (ids [n], logits [n][vocab] or None, experts or None)."""
-        out = np.zeros(n, dtype=np.int32)
-        dbg, keep = self._dbg(n, force, logits, experts)
+    def decode(self, n: int, force=None, logits: bool = False, experts: bool = False, router: bool = False):
+        """Returns (ids [n], logits [n][vocab] or None, experts or None).
+        force, if given, must hold at least n tokens (the first n are used).
+        With router=True the router logits [n][n_layers][n_experts] of the
+        passes are left in ``last_router``."""
+        out = np.zeros(max(int(n), 0), dtype=np.int32)
+        dbg, keep = self._dbg(n, force, logits, experts, router)
         with self._torch.cuda.device(self.device):
             rc = self._lib.kie_decode(self._h, n, _i32p(out), ctypes.byref(dbg) if keep else None)
         _check(rc, self._h)
+        self.last_router = keep.get("router")
         return out, keep.get("logits"), keep.get("experts")
 
     def trace_decode(self, n: int):
@@ -205,12 +271,18 @@ class Model:
         return out, tr[:min(n * pp, 2048)]
 
     def set_kv(self, K: np.ndarray, V: np.ndarray, pending: int):
-        K = np.ascontiguousarray(K, dtype=np.float16)
-        V = np.ascontiguousarray(V, dtype=np.float16)
+        n_pos = check_kv(self.cfg, K, V)
+        K = np.ascontiguousarray(K)
+        V = np.ascontiguousarray(V)
         with self._torch.cuda.device(self.device):
             rc = self._lib.kie_set_kv(self._h, c_void_p(K.ctypes.data), c_void_p(V.ctypes.data),
-                                      K.shape[1], int(pending))
+                                      n_pos, int(pending))
         _check(rc, self._h)
+
+    def set_limits(self, spin_limit: int = 0, watchdog_ms: int = 0):
+        """Device wait limit (polls; 0 = default) and host watchdog per launch
+        (ms; 0 = automatic, negative = none) for later calls."""
+        _check(self._lib.kie_set_limits(self._h, int(spin_limit), int(watchdog_ms)), self._h)
 
     def rewind(self, pos: int, pending: int):
         _check(self._lib.kie_rewind(self._h, int(pos), int(pending)), self._h)

@@ -9,11 +9,11 @@ itself: closed forms, invariants, brute force on tiny inputs and the numbers
 the pages print. No function here is left unpinned.
 """
 from .decoder import (Decoder, rmsnorm, rope_angles, apply_rope, softmax, attention_decode,
-                      silu, swiglu_ffn, topk_experts, greedy_argmax, gemv_f64, greedy_generate)
+                      silu, swiglu_ffn, topk_experts, greedy_argmax, gemv_f64)
 from .compare import zscore_error, top2_gap, compare_logits
 
 __all__ = [
     "Decoder", "rmsnorm", "rope_angles", "apply_rope", "softmax", "attention_decode",
-    "silu", "swiglu_ffn", "topk_experts", "greedy_argmax", "gemv_f64", "greedy_generate",
+    "silu", "swiglu_ffn", "topk_experts", "greedy_argmax", "gemv_f64",
     "zscore_error", "top2_gap", "compare_logits",
 ]

@@ -212,15 +212,20 @@ class Decoder:
         self.pos = n
         self.pending = int(pending_token)
 
-    def _moe_rows(self, l: int, Hn: np.ndarray) -> np.ndarray:
+    def _moe_rows(self, l: int, Hn: np.ndarray, override: Optional[np.ndarray] = None) -> np.ndarray:
         """The MoE FFN of every row of Hn: row t gets sum over its top-k experts
         e of pi_te * FFN_e(h_t), with pi_t the softmax of its router logits.
-        Rows are grouped by expert so each expert's matrices are read once."""
+        ``override`` [T, k], if given, replaces row t's top-k set (the same
+        probabilities pi_t weigh it). Rows are grouped by expert so each
+        expert's matrices are read once."""
         cfg = self.cfg
         logits = Hn @ self.w(f"l{l}.Wr").T                            # [T, E]
         self.full_router.append(logits)
         probs = softmax(logits)
-        sel = np.stack([topk_experts(p, cfg.top_k) for p in probs])   # [T, k]
+        if override is None:
+            sel = np.stack([topk_experts(p, cfg.top_k) for p in probs])   # [T, k]
+        else:
+            sel = np.asarray(override, dtype=np.int64).reshape(len(Hn), -1)
         Y = np.zeros_like(Hn)
         for e in range(cfg.n_experts):
             rows = np.nonzero((sel == e).any(axis=1))[0]
@@ -294,11 +299,12 @@ class Decoder:
         self.pending = first
         return first, logits
 
-    def prefill_batched(self, prompt: Sequence[int]):
+    def prefill_batched(self, prompt: Sequence[int], expert_overrides=None):
         """Same result as ``prefill`` (up to rounding order), computed with one
-        causal forward over the whole prompt; returns (first token, last logits)."""
+        causal forward over the whole prompt; returns (first token, last logits).
+        ``expert_overrides`` as in ``forward_full``."""
         self.reset()
-        logits = self.forward_full(list(prompt), store_kv=True)[-1]
+        logits = self.forward_full(list(prompt), store_kv=True, expert_overrides=expert_overrides)[-1]
         self.pos = len(prompt)
         first = greedy_argmax(logits)
         self.pending = first
@@ -322,13 +328,16 @@ class Decoder:
         return np.asarray(ids, dtype=np.int32), (np.stack(rows) if keep_logits else None), exps
 
     # ---- non-incremental reference ----------------------------------------
-    def forward_full(self, tokens: Sequence[int], store_kv: bool = False) -> np.ndarray:
+    def forward_full(self, tokens: Sequence[int], store_kv: bool = False,
+                     expert_overrides: Optional[np.ndarray] = None) -> np.ndarray:
         """Logits at every position of ``tokens`` by a full causal recompute.
 
         All positions are projected at once and attention applies an explicit
         causal mask; the incremental path is checked against it. With
         ``store_kv`` the rotated keys and the values of positions 0..T-1 are
-        also written to the cache (a batched prefill).
+        also written to the cache (a batched prefill). MoE:
+        ``expert_overrides`` [T][n_layers][top_k], if given, is the expert set
+        of every (position, layer), used instead of the router's own top-k.
         """
         cfg, dt = self.cfg, self.dtype
         T = len(tokens)
@@ -359,7 +368,8 @@ class Decoder:
             X = X + O.reshape(T, H * hd) @ self.w(f"l{l}.Wo").T
             Hn = rmsnorm(X, self.w(f"l{l}.g_ffn"), cfg.rms_eps)
             if cfg.n_experts:
-                Y = self._moe_rows(l, Hn)
+                ov = None if expert_overrides is None else np.asarray(expert_overrides)[:, l]
+                Y = self._moe_rows(l, Hn, ov)
             else:
                 G = Hn @ self.w(f"l{l}.Wg").T
                 U = Hn @ self.w(f"l{l}.Wu").T
@@ -367,10 +377,3 @@ class Decoder:
             X = X + Y
         return rmsnorm(X, self.w("g_final"), cfg.rms_eps) @ self.w("W_lm").T
 
-
-def greedy_generate(cfg, tensors, prompt, n, dtype=np.float32):
-    """Free-running greedy decode: prefill, then n passes. Returns (first, ids)."""
-    dec = Decoder(cfg, tensors, dtype=dtype)
-    first, _ = dec.prefill(prompt)
-    ids, _, _ = dec.decode(n)
-    return first, ids

@@ -7,6 +7,9 @@ import oracle
 
 TOL = 2e-2   # z-scored logits error and top-2 gap threshold
 
+# worst z-scored logits error seen per workload (the first word of a label)
+WORST = {}
+
 
 def say(*a):
     print(*a, flush=True)
@@ -17,10 +20,16 @@ def check_rows(dev, ref, tol=TOL, label=""):
     """Element-wise parity of logits rows: max z-scored error <= tol and the
     argmax equal wherever the oracle's top-2 gap exceeds tol."""
     worst, must, bad, n = oracle.compare_logits(dev, ref, tol)
+    key = label.split()[0] if label else "?"
+    WORST[key] = max(WORST.get(key, 0.0), worst) if worst == worst else float("inf")
     say(f"[{label}] rows={n} max_zerr={worst:.3e} argmax_checked={must} argmax_bad={bad}")
     assert worst <= tol, f"{label}: z-scored logits error {worst:.3e} > {tol}"
     assert bad == 0, f"{label}: {bad} argmax mismatches above the gap threshold"
     return worst
+
+
+def report_worst(key):
+    say(f"[worst] {key}: max z-scored logits error {WORST.get(key, float('nan')):.3e}")
 
 
 def gemv_bound(A, x):
@@ -33,18 +42,18 @@ def gemv_bound(A, x):
 ROUTE_TOL = 2e-2   # z-scored router-logit margin below which either expert is a valid choice
 
 
-def routing_agrees(dev_sel, router_logits, k, tol=ROUTE_TOL, label=""):
+def routing_valid(dev_sel, router_logits, k, tol=ROUTE_TOL, label=""):
     """Check one pass's device routing against the oracle's router logits.
 
-    dev_sel [L][k]: experts the device chose; router_logits [L][E]: oracle.
-    Every layer's choice must be a valid top-k: k distinct in-range experts,
-    none of them below an unchosen one by more than tol (in units of the
-    layer's logit spread). Returns True when every layer chose exactly the
-    oracle's top-k set, False when some layer differs only inside a near tie;
-    the layers after such a layer are not checked, since from there on the two
-    sides legitimately compute from different states.
+    dev_sel [L][k]: experts the device chose; router_logits [L][E]: the
+    oracle's, computed from the oracle's own state. Every layer's choice must
+    be a valid top-k: k distinct in-range experts, none of them below an
+    unchosen one by more than tol (in units of the layer's logit spread).
+    Returns the number of layers whose set differs from the oracle's own
+    top-k (near ties). The caller has the oracle adopt the device's sets, so
+    the comparison goes on past them.
     """
-    same = True
+    ties = 0
     for l, (sel, r) in enumerate(zip(dev_sel, router_logits)):
         r = np.asarray(r, dtype=np.float64)
         sel = np.asarray(sel, dtype=np.int64)
@@ -52,79 +61,129 @@ def routing_agrees(dev_sel, router_logits, k, tol=ROUTE_TOL, label=""):
         assert len(set(sel.tolist())) == k, f"{label} layer {l}: repeated expert {sel}"
         rest = np.setdiff1d(np.arange(len(r)), sel)
         sd = r.std()
+        margin = 0.0
         if rest.size:
-            worst = (r[rest].max() - r[sel].min()) / sd
-            assert worst <= tol, f"{label} layer {l}: experts {sel} are not a top-{k} (margin {worst:.3e})"
+            margin = (r[rest].max() - r[sel].min()) / sd
+            assert margin <= tol, f"{label} layer {l}: experts {sel} are not a top-{k} (margin {margin:.3e})"
         want = set(oracle.topk_experts(oracle.softmax(r), k).tolist())
         if set(sel.tolist()) != want:
+            ties += 1
             say(f"[{label}] layer {l}: near tie, device {sorted(sel.tolist())} vs oracle {sorted(want)}, "
-                f"margin {worst:.2e}")
-            return False
-    return same
+                f"margin {margin:.2e}; the oracle adopts the device's set")
+    return ties
 
 
-def moe_request_parity(m, cfg, W, P, n, trials, label):
+def device_topk_exact(dev_exp, dev_router, k, label=""):
+    """Every pass's device expert ids are exactly the top-k of the device's
+    own router logits, in rank order (larger first, ties to the lower expert
+    index), decided in fp32 as the device decides them. A property that holds
+    at any size, so it covers passes the oracle does not recompute."""
+    r = np.asarray(dev_router, dtype=np.float32)
+    assert np.isfinite(r).all(), f"{label}: non-finite router logits"
+    order = np.argsort(-r, axis=-1, kind="stable")[..., :k]
+    bad = np.argwhere((order != np.asarray(dev_exp)).any(axis=-1))
+    assert bad.size == 0, f"{label}: (pass, layer) {bad[:4].tolist()} is not the top-{k} of its router logits"
+
+
+def _router_zerr(dev_router_pass, ref_router_pass):
+    """max over layers of the z-scored router-logit difference (diagnostic)."""
+    w = 0.0
+    for d, r in zip(dev_router_pass, ref_router_pass):
+        r = np.asarray(r, dtype=np.float64)
+        w = max(w, float(np.max(np.abs(np.asarray(d, dtype=np.float64) - r)) / r.std()))
+    return w
+
+
+def follow(dec, dev_rows, dev_exp, dev_router, tokens, k, tag):
+    """Oracle passes fed `tokens`, each adopting the device's expert sets;
+    every pass's routing must be a valid top-k and its logits within TOL.
+    Returns (passes compared, near-tie layers adopted)."""
+    ties = 0
+    for i, tok in enumerate(tokens):
+        row = dec.step(int(tok), expert_override=dev_exp[i])
+        ties += routing_valid(dev_exp[i], dec.last_router, k, label=f"{tag} pass {i}")
+        if dev_router is not None:
+            say(f"[{tag} pass {i}] router max_zerr={_router_zerr(dev_router[i], dec.last_router):.3e}")
+        check_rows(dev_rows[i:i + 1], row[None], label=f"{tag} pass {i}")
+    return len(tokens), ties
+
+
+def moe_request_parity(m, cfg, W, P, n, trials, label, deep=32):
     """MoE parity of one device model `m` (freshly loaded) against the oracle.
 
-    1. The prompt: every pass's routing must be a valid top-k of the oracle's
-       router logits; the last logits are compared when no pass hit a near tie.
+    Wherever the device's expert set differs from the oracle's own top-k by a
+    near tie (a swap of experts whose router logits lie within ROUTE_TOL of
+    the k-th), the oracle adopts the device's set for that layer and goes on;
+    every layer of every compared pass must be such a valid choice.
+
+    1. The prompt: the oracle's batched causal forward with the device's
+       expert sets of every (position, layer); the last logits are compared
+       and every set checked against the oracle's router logits.
     2. Trials from a seeded cache of len(P) positions that both sides store
        exactly: trial t feeds forced token t, then t+1 (two passes in one
-       launch); logits are compared element by element up to the first near
-       tie in routing.
-    3. The request: n teacher-forced passes as ONE launch; the same passes
-       split over debug launches must give the same ids bit for bit, each id
-       must be the argmax of its own logits row and every pass's routing a
-       valid top-k; the leading passes are compared with the oracle until the
-       first near tie.
-    Returns the number of passes compared with the oracle in steps 2 and 3.
+       launch); both passes compared element by element.
+    3. Deep in the context: both sides start from a seeded cache of
+       max_seq - deep positions; `deep` consecutive teacher-forced passes in
+       one launch, all compared element by element.
+    4. The request: n teacher-forced passes as ONE launch from the seeded
+       len(P)-position cache; the same passes split over debug launches must
+       give the same ids bit for bit; each id is the argmax of its own logits
+       row and every pass's experts are the exact top-k of its own router
+       logits; the leading 16 passes are compared with the oracle.
+    Returns (passes compared with the oracle, near-tie layers adopted).
     """
     import synth
+    k = cfg.top_k
+    compared, ties = 0, 0
     ref = oracle.Decoder(cfg, W)
-    say(f"{label}: oracle batched prefill of {len(P)} tokens")
-    first, last = ref.prefill_batched(P)
+    g_first, g_logits, g_exp = m.prefill(P, logits=True, experts=True, router=True)
+    device_topk_exact(g_exp, m.last_router, k, label=f"{label} prompt")
+    say(f"{label}: oracle batched prefill of {len(P)} tokens with the device's expert sets")
+    first, last = ref.prefill_batched(P, expert_overrides=g_exp)
     routes = ref.full_router
-    g_first, g_logits, g_exp = m.prefill(P, logits=True, experts=True)
-    same = [routing_agrees(g_exp[i], [r[i] for r in routes], cfg.top_k, label=f"{label} prompt {i}")
-            for i in range(len(P))]
-    if all(same):
-        check_rows(g_logits[-1:], last[None], label=f"{label} prefill")
-        if oracle.top2_gap(last) > TOL:
-            assert g_first == first
-    else:
-        say(f"{label}: near tie in the prompt's routing; its last logits are not compared")
+    for i in range(len(P)):
+        ties += routing_valid(g_exp[i], [r[i] for r in routes], k, label=f"{label} prompt {i}")
+    check_rows(g_logits[-1:], last[None], label=f"{label} prefill")
+    if oracle.top2_gap(last) > TOL:
+        assert g_first == first
+    compared += 1
     del ref
     K, V = synth.make_kv_prefill(cfg, n_pos=len(P))
     F = synth.make_forced_tokens(cfg, n + 1)
     dec = oracle.Decoder(cfg, W, cache_experts=True)
-    compared = 0
-
-    def follow(dev_rows, dev_exp, tokens, tag):
-        nonlocal compared
-        for i, tok in enumerate(tokens):
-            row = dec.step(int(tok))
-            if not routing_agrees(dev_exp[i], dec.last_router, cfg.top_k, label=f"{tag} pass {i}"):
-                return
-            check_rows(dev_rows[i:i + 1], row[None], label=f"{tag} pass {i}")
-            compared += 1
-
     for t in range(trials):
         dec.set_kv(K, V, int(F[t]))
         m.set_kv(K, V, int(F[t]))
-        _, rows, exp = m.decode(2, force=F[t + 1:t + 3], logits=True, experts=True)
-        follow(rows, exp, F[t:t + 2], f"{label} trial {t}")
+        _, rows, exp = m.decode(2, force=F[t + 1:t + 3], logits=True, experts=True, router=True)
+        device_topk_exact(exp, m.last_router, k, label=f"{label} trial {t}")
+        c, tt = follow(dec, rows, exp, m.last_router, F[t:t + 2], k, f"{label} trial {t}")
+        compared += c
+        ties += tt
+    deep = min(deep, n)
+    p0 = cfg.max_seq - deep
+    say(f"{label}: {deep} teacher-forced passes in one launch from a seeded cache of {p0} positions")
+    Kd, Vd = synth.make_kv_prefill(cfg, n_pos=p0)
+    dec.set_kv(Kd, Vd, int(F[0]))
+    m.set_kv(Kd, Vd, int(F[0]))
+    del Kd, Vd
+    _, rows, exp = m.decode(deep, force=F[1:deep + 1], logits=True, experts=True, router=True)
+    device_topk_exact(exp, m.last_router, k, label=f"{label} deep")
+    c, tt = follow(dec, rows, exp, m.last_router, F[:deep], k, f"{label} deep")
+    compared += c
+    ties += tt
     say(f"{label}: one teacher-forced launch of {n} passes, then the same passes with debug output")
     m.set_kv(K, V, int(F[0]))
     g_ids, _, _ = m.decode(n, force=F[1:])
     m.rewind(len(P), int(F[0]))
-    c_ids, c_rows, c_exp = m.decode(n, force=F[1:], logits=True, experts=True)
+    c_ids, c_rows, c_exp = m.decode(n, force=F[1:], logits=True, experts=True, router=True)
     assert np.array_equal(g_ids, c_ids)
     assert np.array_equal(c_ids, np.argmax(c_rows, axis=1))
-    for i in range(n):
-        for l in range(cfg.n_layers):
-            sel = c_exp[i, l]
-            assert sel.min() >= 0 and sel.max() < cfg.n_experts and len(set(sel.tolist())) == cfg.top_k
+    device_topk_exact(c_exp, m.last_router, k, label=f"{label} request")
     dec.set_kv(K, V, int(F[0]))
-    follow(c_rows, c_exp, F[:min(n, 16)], f"{label} request")
-    say(f"{label}: {compared} passes compared with the oracle")
-    return compared
+    lead = min(n, 16)
+    c, tt = follow(dec, c_rows, c_exp, m.last_router, F[:lead], k, f"{label} request")
+    compared += c
+    ties += tt
+    say(f"{label}: {compared} passes compared with the oracle, {ties} near-tie layers adopted")
+    report_worst(label)
+    return compared, ties

@@ -92,6 +92,7 @@ def test_null_model_calls(lib):
     assert lib.kie_reset(None) == -1
     assert lib.kie_rewind(None, 0, 0) == -1
     assert lib.kie_last_kernel_ms(None) == 0.0
+    assert lib.kie_set_limits(None, 1, 1) == -1
     lib.kie_free(None)
 
 
@@ -115,3 +116,52 @@ def test_probe_argument_errors(lib):
     assert lib.kie_barrier_probe(ctypes.c_void_p(1), 2, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
     assert lib.kie_barrier_probe(ctypes.c_void_p(1), 1, 0, None, ctypes.byref(ms), ctypes.byref(err)) == -1
     assert lib.kie_launch_probe(0, None, ctypes.byref(ms)) == -1
+
+
+# ---- the Python binding checks shapes and lengths before any ctypes call ----
+def test_binding_shape_order_matches_tensor_specs():
+    for name in ("tiny", "2b", "moe"):
+        cfg = synth.get_config(name)
+        assert kie.expected_shapes(cfg) == [tuple(s) for _, s, _ in synth.tensor_specs(cfg)]
+
+
+def test_binding_rejects_bad_tensors():
+    cfg = synth.get_config("tiny")
+    W = synth.make_weights(cfg)
+    kie.check_tensors(cfg, W)
+    with pytest.raises(kie.KieError) as e:
+        kie.check_tensors(cfg, W[:-1])
+    assert e.value.code == -1
+    bad = list(W)
+    bad[3] = bad[3][:, :-1]                       # a truncated Wk
+    with pytest.raises(kie.KieError):
+        kie.check_tensors(cfg, bad)
+    moe = synth.DecoderConfig(name="m", n_layers=1, d_model=512, n_heads=4, n_kv_heads=2, head_dim=128,
+                              ffn_dim=1024, vocab=300, n_experts=2, top_k=1)
+    Wm = [np.zeros(s, dtype=np.float16) for s in kie.expected_shapes(moe)]
+    kie.check_tensors(moe, Wm)
+    Wm[-4] = Wm[-4].T                             # an expert's Wd transposed: same bytes, wrong shape
+    with pytest.raises(kie.KieError):
+        kie.check_tensors(moe, Wm)
+    bad = list(W)
+    bad[5] = bad[5].astype(np.float32)            # fp32 would be read as twice the elements
+    with pytest.raises(kie.KieError):
+        kie.check_tensors(cfg, bad)
+
+
+def test_binding_rejects_bad_kv_and_tokens():
+    cfg = synth.get_config("tiny")
+    K, V = synth.make_kv_prefill(cfg, n_pos=5)
+    assert kie.check_kv(cfg, K, V) == 5
+    assert kie.check_kv(cfg, K[:, :0], V[:, :0]) == 0
+    for k, v in [(K, V[:, :4]), (K[:1], V[:1]), (K.astype(np.float32), V), (K[..., :32], V[..., :32]),
+                 (K[0], V[0])]:
+        with pytest.raises(kie.KieError) as e:
+            kie.check_kv(cfg, k, v)
+        assert e.value.code == -1
+    assert kie.check_tokens([1, 2, 3], 2, "force").tolist() == [1, 2]
+    assert kie.check_tokens(np.arange(4), 0, "tokens").dtype == np.int32
+    for t, n in [([1, 2], 3), (np.zeros((2, 2), dtype=np.int32), 1), (np.array([0.5, 1.0]), 1)]:
+        with pytest.raises(kie.KieError) as e:
+            kie.check_tokens(t, n, "force")
+        assert e.value.code == -1

@@ -3,12 +3,15 @@
 The ~2.1B dense decoder (25 layers, d 2560, 20/4 heads x 128, SwiGLU 8192,
 vocab 32768), the same decoder over a 32768-position cache, and the top-8 of
 64 experts MoE decoder (24 layers, d 2048). Each test compares device logits
-with the oracle's element by element on a few passes, then checks the token ids
-of ONE launch of the benchmark's request length (1024, 256 and 512 passes)
-against oracle results that do not depend on the device: a teacher-forced
-request whose every pass the oracle computes (dense), the leading passes of a
-request (32K context, MoE), and the properties that hold at any size (a single
-launch equals the same passes split over several launches, bit for bit).
+with the oracle's element by element on passes after the prompt AND deep in
+the context (both sides starting from the same seeded cache of 1100, 33000 or
+608 positions), then checks the token ids of ONE launch of the benchmark's
+request length (1024, 256 and 512 passes) against oracle results that do not
+depend on the device: a teacher-forced request whose every pass the oracle
+computes (dense: every logits row of the request compared element by element),
+the leading passes of a request (32K context, MoE), and the properties that
+hold at any size (a single launch equals the same passes split over several
+launches, bit for bit; MoE experts are the exact top-k of the router logits).
 
 Teacher forcing uses the seeded token stream of `synth.make_forced_tokens`:
 pass i of a request is fed token i of the stream whatever pass i-1 produced.
@@ -20,7 +23,7 @@ import pytest
 
 import oracle
 import synth
-from tests.parity import TOL, check_rows, moe_request_parity, say
+from tests.parity import TOL, check_rows, moe_request_parity, report_worst, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
 
@@ -75,6 +78,16 @@ def test_2b_prompt_and_forced_passes(torch_cuda):
         m.rewind(len(P), first)
         _, g_rows, _ = m.decode(4, force=ids, logits=True)
         check_rows(g_rows, rows, label="2b decode")
+        # deep in the context: both sides from the same seeded 1100-position cache
+        K, V = synth.make_kv_prefill(cfg, n_pos=1100)
+        F = synth.make_forced_tokens(cfg, 5)
+        deep = oracle.Decoder(cfg, W)
+        deep.set_kv(K, V, int(F[0]))
+        say("2b: oracle 4 teacher-forced passes at positions 1100..1103")
+        _, drows, _ = deep.decode(4, force=F[1:], keep_logits=True)
+        m.set_kv(K, V, int(F[0]))
+        _, g_drows, _ = m.decode(4, force=F[1:], logits=True)
+        check_rows(g_drows, drows, label="2b deep")
     finally:
         m.close()
 
@@ -96,43 +109,63 @@ def test_2b_request_launch_teacher_forced(torch_cuda):
         c_ids, c_rows, _ = m.decode(n, force=F[1:], logits=True)
         assert np.array_equal(g_ids, c_ids)
         assert np.array_equal(c_ids, np.argmax(c_rows, axis=1))
-        del c_rows
     finally:
         m.close()
     say(f"2b: oracle full causal forward over {len(P) + n} tokens")
     rows = oracle.Decoder(cfg, W).forward_full(list(P) + list(F[:n]))[len(P):]
+    # every logits row of the request, element by element (the debug launches
+    # of 64 passes, whose ids equal the single launch's bit for bit)
+    check_rows(c_rows, rows, label="2b request-rows")
+    del c_rows
     checked, total = _ids_agree(g_ids, rows, "2b request")
     assert checked >= total * 0.75
+    report_worst("2b")
 
 
 # ---- the same decoder after a 32768-position cache, 256-pass requests -------------
 def test_2b_32k_forced_passes_and_request(torch_cuda):
     cfg = synth.get_config("2b_32k")
+    n = cfg.decode_steps
     W = _weights("2b")          # the same tensors as the 2b workload (same seed and shapes)
     K, V = synth.make_kv_prefill(cfg)
     pend = synth.make_pending_token(cfg)
+    F = synth.make_forced_tokens(cfg, n)
     ref = oracle.Decoder(cfg, W)
     ref.set_kv(K, V, pend)
-    say("2b_32k: oracle 3 greedy passes over the 32768-position cache")
-    ids, rows, _ = ref.decode(3, keep_logits=True)
+    say("2b_32k: oracle 8 teacher-forced passes over the 32768-position cache")
+    _, rows, _ = ref.decode(8, force=F[:8], keep_logits=True)
+    del ref
     m = _model(cfg, W)
     try:
         m.set_kv(K, V, pend)
-        _, g_rows, _ = m.decode(3, force=ids, logits=True)
+        _, g_rows, _ = m.decode(8, force=F[:8], logits=True)
         check_rows(g_rows, rows, label="2b_32k decode")
-        say(f"2b_32k: one free-running launch of {cfg.decode_steps} passes")
+        say(f"2b_32k: one teacher-forced launch of {n} passes")
         m.rewind(cfg.kv_prefill, pend)
-        a, _, _ = m.decode(cfg.decode_steps)
+        g_ids, _, _ = m.decode(n, force=F)
+        _ids_agree(g_ids[:8], rows, "2b_32k request")
+        say(f"2b_32k: free-running launches of {n} passes, twice")
         m.rewind(cfg.kv_prefill, pend)
-        b, _, _ = m.decode(cfg.decode_steps)
+        a, _, _ = m.decode(n)
+        m.rewind(cfg.kv_prefill, pend)
+        b, _, _ = m.decode(n)
         assert np.array_equal(a, b)
+        # deep: both sides from the same seeded 33000-position cache
+        del K, V
+        deep_cfg = cfg.with_(kv_prefill=33000, decode_steps=cfg.max_seq - 33000)
+        Kd, Vd = synth.make_kv_prefill(deep_cfg)
+        ref = oracle.Decoder(cfg, W)
+        ref.set_kv(Kd, Vd, int(F[0]))
+        say("2b_32k: oracle 4 teacher-forced passes at positions 33000..33003")
+        _, drows, _ = ref.decode(4, force=F[1:5], keep_logits=True)
+        del ref
+        m.set_kv(Kd, Vd, int(F[0]))
+        del Kd, Vd
+        _, g_drows, _ = m.decode(4, force=F[1:5], logits=True)
+        check_rows(g_drows, drows, label="2b_32k deep")
     finally:
         m.close()
-    # leading tokens of the request equal the oracle's while no near tie occurred
-    for i in range(3):
-        if oracle.top2_gap(rows[i]) <= TOL:
-            break
-        assert a[i] == ids[i], f"pass {i}"
+    report_worst("2b_32k")
 
 
 # ---- top-8 of 64 experts MoE, 512-pass requests ------------------------------------
@@ -142,7 +175,7 @@ def test_moe_prompt_routing_and_forced_request(torch_cuda):
     P = synth.make_prompt(cfg)
     m = _model(cfg, W)
     try:
-        done = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 12, "moe")
+        done, ties = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 12, "moe")
     finally:
         m.close()
-    assert done >= 8
+    assert done >= 8 + 32

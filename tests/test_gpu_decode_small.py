@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from tests.parity import check_rows, moe_request_parity, say
+from tests.parity import check_rows, moe_request_parity, report_worst, say
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +96,7 @@ def test_teacher_forced_parity(torch_cuda, name):
     check_rows(g_rows, rows, label=f"{name} decode")
     assert m.state() == (len(P) + n, int(ids[-1]))
     m.close()
+    report_worst(name)
 
 
 def test_free_run_tokens_and_determinism(torch_cuda):
@@ -203,7 +204,7 @@ def test_moe_teacher_forced_parity(torch_cuda, name):
     P = synth.make_prompt(cfg)
     m = _model(cfg, W)
     try:
-        done = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 6, name)
+        done, _ = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 6, name)
     finally:
         m.close()
     assert done >= 8
@@ -271,5 +272,62 @@ def test_two_token_vocabulary(torch_cuda):
         g_ids, g_rows, _ = m.decode(cfg.decode_steps, force=ids, logits=True)
         check_rows(g_rows, rows, label="vocab 2 decode")
         assert np.array_equal(g_ids, np.argmax(g_rows, axis=1))
+    finally:
+        m.close()
+
+
+# ---- failure handling: every wait is bounded, the kernel always exits ----------
+def test_spin_limit_timeout_then_recovery(torch_cuda):
+    """A device wait limit of one poll: the first wait that finds its input
+    unpublished gives up, flags the failure, every other workgroup's waits
+    give up too and the kernel exits normally; the call returns
+    KIE_ERR_TIMEOUT. After kie_reset the model decodes exactly as before."""
+    from memory_bandwidth_bound_amd import kie
+    cfg = TINY.with_(decode_steps=8)
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    m = _model(cfg, W)
+    try:
+        first, _, _ = m.prefill(P)
+        want, _, _ = m.decode(8)
+        m.set_limits(spin_limit=1)
+        m.rewind(len(P), first)
+        say("spin limit 1: expecting KIE_ERR_TIMEOUT")
+        with pytest.raises(kie.KieError) as e:
+            m.decode(8)
+        assert e.value.code == -7
+        assert m.state()[1] == -1              # no pending token after a timeout
+        m.set_limits(0, 0)
+        m.reset()
+        assert m.prefill(P)[0] == first
+        got, _, _ = m.decode(8)
+        assert np.array_equal(got, want)
+    finally:
+        m.close()
+
+
+def test_host_watchdog_reports_overrun_then_recovery(torch_cuda):
+    """A host watchdog of 1 ms around a launch of 1500 passes (about 80 ms):
+    the host raises its abort word and the call returns KIE_ERR_TIMEOUT once
+    the launch has ended; after kie_reset the model decodes as before."""
+    from memory_bandwidth_bound_amd import kie
+    cfg = TINY.with_(name="tiny_long", prompt_len=4, decode_steps=1500)
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    m = _model(cfg, W)
+    try:
+        first, _, _ = m.prefill(P)
+        want, _, _ = m.decode(16)
+        m.set_limits(watchdog_ms=1)
+        m.rewind(len(P), first)
+        say("watchdog 1 ms over 1500 passes: expecting KIE_ERR_TIMEOUT")
+        with pytest.raises(kie.KieError) as e:
+            m.decode(cfg.decode_steps)
+        assert e.value.code == -7 and "watchdog" in str(e.value)
+        m.set_limits(0, 0)
+        m.reset()
+        assert m.prefill(P)[0] == first
+        got, _, _ = m.decode(16)
+        assert np.array_equal(got, want)
     finally:
         m.close()

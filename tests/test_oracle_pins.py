@@ -236,9 +236,11 @@ def _tiny(**kw):
     return DecoderConfig(**base)
 
 
-def _brute_logits(cfg, W, tokens, kv16=True):
+def _brute_logits(cfg, W, tokens, kv16=True, experts=None):
     """Plain scalar loops in float64 from the written-out definition; with
-    kv16 every cached key and value is rounded to fp16 as it is stored."""
+    kv16 every cached key and value is rounded to fp16 as it is stored.
+    MoE: experts[p][l], if given, is the expert set mixed at position p and
+    layer l (with the router's probabilities) instead of the router's top-k."""
     names = [n for n, _, _ in tensor_specs(cfg)]
     T = {n: np.asarray(t, dtype=np.float64) for n, t in zip(names, W)}
     d, H, Hkv, hd = cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
@@ -304,6 +306,8 @@ def _brute_logits(cfg, W, tokens, kv16=True):
                 ex = [math.exp(a - mx) for a in r]
                 pi = [a / sum(ex) for a in ex]
                 order = sorted(range(cfg.n_experts), key=lambda e: (-pi[e], e))[:cfg.top_k]
+                if experts is not None:
+                    order = [int(e) for e in experts[p][l]]
                 y = [0.0] * d
                 for e in order:
                     ye = ffn(h, T[f"l{l}.e{e}.Wg"], T[f"l{l}.e{e}.Wu"], T[f"l{l}.e{e}.Wd"])
@@ -357,6 +361,32 @@ def test_batched_prefill_equals_incremental_prefill():
     ib, rb, _ = b.decode(3, keep_logits=True)
     np.testing.assert_array_equal(ia, ib)
     np.testing.assert_allclose(ra, rb, rtol=1e-10, atol=1e-12)
+
+
+def test_moe_expert_overrides_follow_the_definition():
+    """An overridden expert set is mixed with the router's own probabilities,
+    in the incremental pass and in the full causal forward alike."""
+    cfg = _tiny(n_experts=6, top_k=2, ffn_dim=6, n_layers=2, vocab=30)
+    W = make_weights(cfg)
+    toks = [4, 11, 29, 0, 7]
+    rng = np.random.default_rng(16)
+    ov = [[sorted(rng.choice(cfg.n_experts, cfg.top_k, replace=False).tolist()) for _ in range(cfg.n_layers)]
+          for _ in toks]
+    want = _brute_logits(cfg, W, toks, experts=ov)
+    dec = oracle.Decoder(cfg, W, dtype=np.float64)
+    inc = np.stack([dec.step(t, expert_override=ov[i]) for i, t in enumerate(toks)])
+    np.testing.assert_allclose(inc, want, rtol=1e-10, atol=1e-12)
+    full = oracle.Decoder(cfg, W, dtype=np.float64).forward_full(toks, expert_overrides=np.array(ov))
+    np.testing.assert_allclose(full, want, rtol=1e-10, atol=1e-12)
+    # overriding with the router's own choice changes nothing
+    plain = oracle.Decoder(cfg, W, dtype=np.float64)
+    rows, own = [], []
+    for t in toks:
+        rows.append(plain.step(t))
+        own.append([e.tolist() for e in plain.last_experts])
+    again = oracle.Decoder(cfg, W, dtype=np.float64).forward_full(toks, expert_overrides=np.array(own))
+    np.testing.assert_allclose(again, np.stack(rows), rtol=1e-10, atol=1e-12)
+    assert not np.allclose(want, np.stack(rows))   # the overrides above do change the result
 
 
 def test_decoder_causal_mask_ignores_future_cache():
@@ -467,3 +497,23 @@ def test_compare_measures():
     assert oracle.top2_gap(ref) == pytest.approx(7.0 / sd)
     worst, must, bad, n = oracle.compare_logits(dev[None], ref[None])
     assert (must, bad, n) == (1, 0, 1)
+
+
+@pytest.mark.parametrize("bad_value", [np.nan, np.inf, -np.inf])
+def test_compare_non_finite_device_rows_fail(bad_value):
+    """A NaN or infinite device logit is an infinite error, also in a row whose
+    top-2 gap is below the tolerance (no argmax check there) and when it sits
+    after a finite row."""
+    ref = np.array([[0.0, 1.0, 2.0, 3.0, 10.0], [0.0, 1.0, 2.0, 5.0, 5.0001]])
+    assert oracle.top2_gap(ref[1]) <= 2e-2
+    for row in (0, 1):
+        dev = ref.copy()
+        dev[row, 1] = bad_value
+        assert oracle.zscore_error(dev[row], ref[row]) == float("inf")
+        worst, must, bad, n = oracle.compare_logits(dev, ref)
+        assert worst == float("inf") and not worst <= 2e-2
+    dev = np.full_like(ref, np.nan)
+    worst, _, _, _ = oracle.compare_logits(dev, ref)
+    assert worst == float("inf")
+    # a shape mismatch is no pass either
+    assert oracle.compare_logits(ref[:, :4], ref)[0] == float("inf")
