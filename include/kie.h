@@ -267,6 +267,24 @@ size_t kie_barrier_probe_bytes(void);
 int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                       int32_t* errors);
 
+/*
+ * Allocation-free variant of kie_barrier_probe, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same probe kernel, with its words,
+ * status and error count in a 64 KiB array that the library holds in device
+ * memory, one per GPU, until the process ends (its address is looked up once
+ * per device, at the first call on it). The caller passes no scratch. Each
+ * call clears the array with a fill kernel (no hipMemsetAsync), then runs the
+ * probe on hip_stream and waits for it. Calls that overlap on one GPU share
+ * the array and race: issue them one at a time per device. *us_per_round is
+ * host wall time of the launch (from launch to completion, no HIP events)
+ * divided by rounds; *errors as for kie_barrier_probe. KIE_ERR_ARG for bad
+ * arguments, KIE_ERR_WORKSPACE if the probe ever needs more than the 64 KiB.
+ * Calls no hipMalloc or hipFree.
+ */
+int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
+                              int32_t* errors);
+
 /* Launch-overhead probe: `launches` back-to-back launches of an empty kernel;
  * *us_per_launch receives host wall time per launch including completion. */
 int kie_launch_probe(int32_t launches, void* hip_stream, float* us_per_launch);

@@ -538,6 +538,32 @@ int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_
     return KIE_OK;
 }
 
+int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
+                              int32_t* errors) {
+    if (!us_per_round || !errors || rounds < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (fenced) or 1 (flagged)");
+    if (kie_barrier_probe_bytes() > noalloc_scratch_bytes())
+        return fail(nullptr, KIE_ERR_WORKSPACE, "the probe needs more scratch than the library's 64 KiB array");
+    void* ptr = nullptr;
+    HIP_TRY(nullptr, noalloc_scratch(&ptr));
+    hipStream_t s = (hipStream_t)hip_stream;
+    uint8_t* b = (uint8_t*)ptr;
+    uint64_t* words = (uint64_t*)b;               // same layout as kie_barrier_probe's scratch
+    uint32_t* status = (uint32_t*)(b + 32768);
+    int32_t* err = (int32_t*)(b + 32768 + 256);
+    // the previous call's words, status and count are still there: clear them
+    HIP_TRY(nullptr, launch_fill_zero((uint32_t*)ptr, (int)(kie_barrier_probe_bytes() / 4), s));
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    const auto t0 = std::chrono::steady_clock::now();
+    hipError_t le = launch_barrier_probe(variant, words, status, err, rounds, kGrid, s);
+    if (le != hipSuccess) return hip_fail(nullptr, le, "barrier probe launch");
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    const auto t1 = std::chrono::steady_clock::now();
+    HIP_TRY(nullptr, hipMemcpy(errors, err, 4, hipMemcpyDeviceToHost));
+    *us_per_round = (float)(std::chrono::duration<double, std::micro>(t1 - t0).count() / rounds);
+    return KIE_OK;
+}
+
 int kie_launch_probe(int32_t launches, void* hip_stream, float* us_per_launch) {
     if (launches < 1 || !us_per_launch) return fail(nullptr, KIE_ERR_ARG, "bad argument");
     hipStream_t s = (hipStream_t)hip_stream;

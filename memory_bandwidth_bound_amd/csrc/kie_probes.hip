@@ -4,6 +4,8 @@
 // empty kernel for the launch cost. None of them is on the decode path.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kie_common.h"
 #include "kie_device.h"
 #include "kie_kernels.h"
@@ -196,6 +198,49 @@ __global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint6
 }
 
 __global__ void empty_kernel() {}
+
+// Zero n 32-bit words (a kernel, so that a caller may capture it in a graph;
+// no hipMemsetAsync).
+__global__ void fill_zero_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// ------------------------------------------- scratch for the no-alloc probe
+// The exchange probe's words, status and error count for callers that cannot
+// allocate device memory: one array per GPU, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not the device array: its
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever handed to a kernel.
+constexpr size_t kNoAllocScratchBytes = 65536;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_dev[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_fill_zero(uint32_t* p, int n, hipStream_t s) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(64), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemv_stream(const GemvArgs& a, int grid, hipStream_t s) {
     GemvArgs copy = a;

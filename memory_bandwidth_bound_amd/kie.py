@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_barrier_probe_bytes": (c_size_t, []),
         "kie_barrier_probe": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
         "kie_launch_probe": (c_int32, [c_int32, c_void_p, POINTER(c_float)]),
+        "kie_barrier_probe_noalloc": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -352,6 +353,20 @@ def barrier_probe(rounds: int, variant: int = 1, device: str = "cuda:0"):
         rc = lib.kie_barrier_probe(c_void_p(scratch.data_ptr()), variant, rounds,
                                    _stream_handle(torch, scratch.device, None), ctypes.byref(us),
                                    ctypes.byref(err))
+    _check(rc)
+    return float(us.value), int(err.value)
+
+
+def barrier_probe_noalloc(rounds: int, variant: int = 1, device: str = "cuda:0"):
+    """kie_barrier_probe without a caller workspace: the library's own scratch
+    array. Returns (host-timed microseconds per round, wrong values)."""
+    import torch
+    lib = load_library()
+    us, err = c_float(), c_int32()
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        rc = lib.kie_barrier_probe_noalloc(variant, rounds, _stream_handle(torch, dev, None), ctypes.byref(us),
+                                           ctypes.byref(err))
     _check(rc)
     return float(us.value), int(err.value)
 
