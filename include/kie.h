@@ -259,6 +259,14 @@ int kie_gemv_probe(const void* A, const void* x, float* y, int32_t M, int32_t K,
  *            one 64-bit store) and gathers all 1280 words, waiting only until
  *            every word carries the round's id - the residual exchange of the
  *            decode kernel.
+ * variant 2: an XCD-aware barrier (the die-topology-aware barrier of the
+ *            news.creeta.com monokernel article, "MI300X die topology and the
+ *            256-CU mapping", re-made for MI355X's 8 XCDs): every workgroup
+ *            stores one value and arrives at its own XCD's counter; the XCD's
+ *            first workgroup waits for its peers there, exchanges one flag
+ *            per XCD across the chip and releases its XCD through one word;
+ *            then all 256 values are read. The XCD of every workgroup is
+ *            read from the hardware.
  * scratch is device memory of at least kie_barrier_probe_bytes() bytes.
  * *us_per_round receives the mean time of one round; *errors the number of
  * values read wrong (must be 0), plus 1000000 per workgroup that gave up.
@@ -284,6 +292,12 @@ int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_
  */
 int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                               int32_t* errors);
+
+/* XCD placement probe: out_xcd (host, [256]) receives the XCD (0..7 on
+ * MI355X) that workgroup w of a 256-workgroup cooperative launch ran on, read
+ * from the hardware register. Uses the library's own 64 KiB device array (no
+ * allocation); waits for the launch. */
+int kie_xcd_map(int32_t* out_xcd, void* hip_stream);
 
 /* Launch-overhead probe: `launches` back-to-back launches of an empty kernel;
  * *us_per_launch receives host wall time per launch including completion. */

@@ -514,7 +514,8 @@ size_t kie_barrier_probe_bytes(void) { return 65536; }
 int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                       int32_t* errors) {
     if (!scratch || !us_per_round || !errors || rounds < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
-    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (fenced) or 1 (flagged)");
+    if (variant < 0 || variant > 2)
+        return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (fenced), 1 (flagged) or 2 (XCD-aware)");
     hipStream_t s = (hipStream_t)hip_stream;
     uint8_t* b = (uint8_t*)scratch;
     uint64_t* words = (uint64_t*)b;               // 2 x 5 x 256 words = 20 KiB
@@ -541,7 +542,8 @@ int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_
 int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                               int32_t* errors) {
     if (!us_per_round || !errors || rounds < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
-    if (variant != 0 && variant != 1) return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (fenced) or 1 (flagged)");
+    if (variant < 0 || variant > 2)
+        return fail(nullptr, KIE_ERR_ARG, "variant must be 0 (fenced), 1 (flagged) or 2 (XCD-aware)");
     if (kie_barrier_probe_bytes() > noalloc_scratch_bytes())
         return fail(nullptr, KIE_ERR_WORKSPACE, "the probe needs more scratch than the library's 64 KiB array");
     void* ptr = nullptr;
@@ -561,6 +563,18 @@ int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream,
     const auto t1 = std::chrono::steady_clock::now();
     HIP_TRY(nullptr, hipMemcpy(errors, err, 4, hipMemcpyDeviceToHost));
     *us_per_round = (float)(std::chrono::duration<double, std::micro>(t1 - t0).count() / rounds);
+    return KIE_OK;
+}
+
+int kie_xcd_map(int32_t* out_xcd, void* hip_stream) {
+    if (!out_xcd) return fail(nullptr, KIE_ERR_ARG, "null output");
+    hipStream_t s = (hipStream_t)hip_stream;
+    void* ptr = nullptr;   // the no-alloc scratch: kGrid words of output
+    HIP_TRY(nullptr, noalloc_scratch(&ptr));
+    hipError_t le = launch_xcd_map((int32_t*)ptr, kGrid, s);
+    if (le != hipSuccess) return hip_fail(nullptr, le, "xcd map launch");
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    HIP_TRY(nullptr, hipMemcpy(out_xcd, ptr, kGrid * sizeof(int32_t), hipMemcpyDeviceToHost));
     return KIE_OK;
 }
 

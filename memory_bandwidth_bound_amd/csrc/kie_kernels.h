@@ -108,6 +108,8 @@ hipError_t launch_gemv_direct(const GemvArgs& a, hipStream_t s);
 hipError_t launch_barrier_probe(int variant, uint64_t* words, uint32_t* status, int32_t* errors, int rounds,
                                 int grid, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);
+// out[w] = the XCD workgroup w of a grid-sized cooperative launch ran on.
+hipError_t launch_xcd_map(int32_t* out, int grid, hipStream_t s);
 // Zero n 32-bit words with a kernel.
 hipError_t launch_fill_zero(uint32_t* p, int n, hipStream_t s);
 // Device address of the no-alloc probe's scratch array on the current device

@@ -156,17 +156,119 @@ __global__ void __launch_bounds__(256) gemv_direct_kernel(GemvArgs a) {
 }
 
 // ------------------------------------------------------------ exchange probe
+// The XCD (accelerator complex die) this wave runs on, from the hardware.
+__device__ __forceinline__ int xcc_id() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+    return (int)v;
+}
+
+
+// XCD-aware barrier state in the probe's scratch (bytes from the scratch base).
+constexpr int kXcdMax = 16;
+constexpr size_t kHierCnt = 36864;              // u32 per XCD, each on its own 256 bytes
+constexpr size_t kHierGen = kHierCnt + 4096;    // u32 per XCD, own 256 bytes
+constexpr size_t kHierFlag = kHierGen + 4096;   // u32 per XCD, own 64-byte line (read across XCDs)
+constexpr size_t kHierMap = kHierFlag + 1024;   // u64 [grid]: flagged XCD id of every workgroup
+constexpr size_t kHierEnd = kHierMap + 8 * 1024;
+static_assert(kHierEnd <= 65536, "the XCD-aware barrier's state fits the probe's 64 KiB scratch");
+
 // variant 0: per round, publish one value with a plain store, fenced grid
 // barrier, read every workgroup's value.
 // variant 1: per round, publish 5 flagged words and gather all 5 x grid words
 // (buffers alternate by round parity, so a workgroup that runs a round ahead
 // cannot overwrite words another one is still reading).
+// variant 2: the XCD-aware barrier. Per round every workgroup stores its
+// value (device scope, so it reaches memory), waits for the store, and
+// arrives at its own XCD's counter (an atomic add); the XCD's
+// lowest-numbered workgroup waits on that counter for all of its XCD's
+// workgroups, publishes one flag per XCD, waits for the other XCDs' flags,
+// and releases its XCD through one word; then every workgroup reads all
+// values. Each workgroup polls one word (its XCD's release) instead of one
+// per workgroup, and only the 8 XCD leaders poll across XCDs. Every poll is a
+// device-scope load: a workgroup-scope load may be served from the compute
+// unit's own L1 and never see another unit's update. The placement of
+// workgroups on XCDs is read from the hardware (XCC_ID) and exchanged once
+// before the first round.
 __global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint64_t* words, uint32_t* status,
                                                               int32_t* errors, int rounds) {
     const int wg = blockIdx.x, nwg = gridDim.x, lane = lane_id();
     int err = 0;
+    // XCD-aware barrier: who shares this workgroup's XCD, and who leads it
+    uint8_t* base = (uint8_t*)words;
+    uint32_t* hcnt = nullptr;
+    uint32_t* hgen = nullptr;
+    uint32_t* hflag = (uint32_t*)(base + kHierFlag);
+    int members = 0, leader = 0, xcd = 0;
+    uint32_t xcd_mask = 0;
+    if (variant == 2) {
+        xcd = xcc_id();
+        uint64_t* map = (uint64_t*)(base + kHierMap);
+        if (lane == 0) fw_store(map + wg, (uint32_t)xcd, 1u);
+        int mem = 0, lead = nwg;
+        uint32_t mask = 0;
+        const int e = fw_gather(map, nwg, 1u, 1u << 22, status, nullptr, [&](int i, uint32_t v) {
+            mask |= 1u << (v & 15);
+            if ((int)v == xcd) {
+                ++mem;
+                lead = i < lead ? i : lead;
+            }
+        });
+        for (int off = 32; off; off >>= 1) {
+            mem += shfl_xor_i(mem, off);
+            const int o = shfl_xor_i(lead, off);
+            lead = o < lead ? o : lead;
+            mask |= (uint32_t)shfl_xor_i((int)mask, off);
+        }
+        if (e) {
+            if (lane == 0) atomicAdd(errors, 1000000);
+            return;
+        }
+        members = mem;
+        leader = lead;
+        xcd_mask = mask;
+        hcnt = (uint32_t*)(base + kHierCnt + 256 * xcd);
+        hgen = (uint32_t*)(base + kHierGen + 256 * xcd);
+    }
     for (int r = 1; r <= rounds; ++r) {
-        if (variant == 0) {
+        if (variant == 2) {
+            uint32_t* vals = (uint32_t*)words + (size_t)(r & 1) * nwg;
+            bool ok = true;
+            uint32_t spins = 0;
+            if (lane == 0) {
+                dev_store32(vals + wg, (uint32_t)(wg * 4096 + r));
+                wait_vm0();   // the value is in memory before this workgroup arrives
+                __hip_atomic_fetch_add(gptr(hcnt), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (wg == leader) {
+                // one lane waits for the XCD's arrivals, then lane x watches XCD x's flag
+                if (lane == 0) {
+                    while (dev_load32(hcnt) < (uint32_t)(members * r)) {
+                        if (++spins > (1u << 22)) { ok = false; break; }
+                    }
+                    if (ok) dev_store32(hflag + 16 * xcd, (uint32_t)r);
+                }
+                ok = __builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0;
+                const bool mine = lane < kXcdMax && (xcd_mask & (1u << lane));
+                while (ok) {
+                    const bool here = !mine || (int)(dev_load32(hflag + 16 * (lane & (kXcdMax - 1))) - (uint32_t)r) >= 0;
+                    if (__builtin_amdgcn_ballot_w64(!here) == 0) break;
+                    if (++spins > (1u << 22)) ok = false;
+                }
+                if (ok && lane == 0) dev_store32(hgen, (uint32_t)r);
+            } else if (lane == 0) {
+                while ((int)(dev_load32(hgen) - (uint32_t)r) < 0) {
+                    if (++spins > (1u << 22)) { ok = false; break; }
+                }
+            }
+            if (!ok && lane == 0) dev_store32(status, (uint32_t)kStatusTimeout);
+            if (__builtin_amdgcn_readfirstlane(ok ? 1 : 0) == 0) {
+                if (lane == 0) atomicAdd(errors, 1000000);
+                return;
+            }
+            for (int i = lane; i < nwg; i += 64)
+                if (dev_load32(vals + i) != (uint32_t)(i * 4096 + r)) ++err;
+        } else if (variant == 0) {
             uint32_t* bar = (uint32_t*)words;
             uint32_t* vals = (uint32_t*)(words + nwg) + (size_t)(r & 1) * nwg;
             if (lane == 0) vals[wg] = (uint32_t)(wg * 4096 + r);
@@ -198,6 +300,16 @@ __global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint6
 }
 
 __global__ void empty_kernel() {}
+
+// The XCD every workgroup of a grid-sized launch runs on.
+__global__ void __launch_bounds__(64, 1) xcd_map_kernel(int32_t* out) {
+    if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
+}
+
+hipError_t launch_xcd_map(int32_t* out, int grid, hipStream_t s) {
+    void* args[] = {&out};
+    return hipLaunchCooperativeKernel((const void*)xcd_map_kernel, dim3(grid), dim3(64), args, 0, s);
+}
 
 // Zero n 32-bit words (a kernel, so that a caller may capture it in a graph;
 // no hipMemsetAsync).

@@ -81,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_barrier_probe": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
         "kie_launch_probe": (c_int32, [c_int32, c_void_p, POINTER(c_float)]),
         "kie_barrier_probe_noalloc": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
+        "kie_xcd_map": (c_int32, [POINTER(c_int32), c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -344,7 +345,8 @@ def gemv_probe(A, x, variant: int = 0, stream=None):
 def barrier_probe(rounds: int, variant: int = 1, device: str = "cuda:0"):
     """Mean microseconds per exchange round across the 256-workgroup grid
     (variant 0: fenced grid barrier; 1: flagged-word all-gather of 5 words per
-    workgroup), and the count of wrong values (0 when correct)."""
+    workgroup; 2: XCD-aware barrier), and the count of wrong values (0 when
+    correct)."""
     import torch
     lib = load_library()
     scratch = torch.zeros(int(lib.kie_barrier_probe_bytes()), dtype=torch.uint8, device=device)
@@ -369,6 +371,18 @@ def barrier_probe_noalloc(rounds: int, variant: int = 1, device: str = "cuda:0")
                                            ctypes.byref(err))
     _check(rc)
     return float(us.value), int(err.value)
+
+
+def xcd_map(device: str = "cuda:0"):
+    """The XCD each of the 256 workgroups of a cooperative launch runs on."""
+    import torch
+    lib = load_library()
+    out = np.zeros(256, dtype=np.int32)
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        rc = lib.kie_xcd_map(_i32p(out), _stream_handle(torch, dev, None))
+    _check(rc)
+    return out
 
 
 def launch_probe(launches: int, device: str = "cuda:0"):

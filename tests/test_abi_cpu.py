@@ -113,11 +113,12 @@ def test_probe_argument_errors(lib):
     assert lib.kie_gemv_probe(None, ctypes.c_void_p(1), ctypes.c_void_p(1), 4, 512, 1, 0, None, None) == -1
     err = ctypes.c_int32()
     assert lib.kie_barrier_probe(None, 1, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
-    assert lib.kie_barrier_probe(ctypes.c_void_p(1), 2, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
+    assert lib.kie_barrier_probe(ctypes.c_void_p(1), 3, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
     assert lib.kie_barrier_probe(ctypes.c_void_p(1), 1, 0, None, ctypes.byref(ms), ctypes.byref(err)) == -1
     assert lib.kie_launch_probe(0, None, ctypes.byref(ms)) == -1
     # the allocation-free probe checks its arguments before any device call
-    assert lib.kie_barrier_probe_noalloc(2, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
+    assert lib.kie_barrier_probe_noalloc(3, 10, None, ctypes.byref(ms), ctypes.byref(err)) == -1
+    assert lib.kie_xcd_map(None, None) == -1
     assert lib.kie_barrier_probe_noalloc(1, 0, None, ctypes.byref(ms), ctypes.byref(err)) == -1
     assert lib.kie_barrier_probe_noalloc(1, 10, None, None, ctypes.byref(err)) == -1
 

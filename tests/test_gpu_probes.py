@@ -84,7 +84,19 @@ def test_gemv_probe_full_shapes_sampled(torch_cuda, si):
     assert ms > 0
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+def test_xcd_map(torch_cuda):
+    """Every workgroup of the 256-workgroup grid reports an XCD id; the ids
+    are 0..7 on MI355X, 32 workgroups each."""
+    from memory_bandwidth_bound_amd import kie
+    m = kie.xcd_map()
+    counts = np.bincount(m, minlength=8)
+    rr = bool(np.array_equal(m, np.arange(256) % 8))
+    say(f"xcd map: workgroups per XCD {counts.tolist()}, round robin (XCD = workgroup % 8): {rr}")
+    assert m.min() >= 0 and m.max() < 16
+    assert counts.sum() == 256
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_barrier_probe(torch_cuda, variant):
     from memory_bandwidth_bound_amd import kie
     say(f"exchange probe variant={variant} 20000 rounds")

@@ -19,7 +19,7 @@ def kie_gpu():
     return kie
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_noalloc_probe_matches_workspace_probe(kie_gpu, variant):
     kie = kie_gpu
     for rounds in (3000, 400):
@@ -41,5 +41,5 @@ def test_noalloc_probe_rejects_bad_arguments(kie_gpu):
         kie.barrier_probe_noalloc(0, 1)
     assert e.value.code == -1
     with pytest.raises(kie.KieError) as e:
-        kie.barrier_probe_noalloc(10, 2)
+        kie.barrier_probe_noalloc(10, 3)
     assert e.value.code == -1
