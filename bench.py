@@ -84,7 +84,11 @@ def describe(cfg) -> str:
          f"{cfg.n_kv_heads} KV heads x {cfg.head_dim}, SwiGLU {cfg.ffn_dim}")
     if cfg.n_experts:
         s += f" x {cfg.n_experts} experts (top-{cfg.top_k})"
-    s += f", vocab {cfg.vocab}, fp16 weights N(0,{cfg.weight_sigma}); batch 1, "
+    if getattr(cfg, "weight_format", "fp16") == "fp8":
+        s += (f", vocab {cfg.vocab}, weights N(0,{cfg.weight_sigma}) held as FP8 E4M3 with one fp32 scale per row "
+              f"(quantised at load; embedding fp16); batch 1, ")
+    else:
+        s += f", vocab {cfg.vocab}, fp16 weights N(0,{cfg.weight_sigma}); batch 1, "
     if cfg.kv_prefill:
         s += f"KV cache pre-filled with {cfg.kv_prefill} seeded positions, "
     else:
@@ -166,7 +170,8 @@ def bench_decode(cfg, args):
         "metric": "batch-1 decode tokens/sec on 1 MI355X + MBU (% of 8 TB/s HBM)",
         "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 weights, fp32 math" if getattr(cfg, "weight_format", "fp16") == "fp8" else "fp16",
         "data": "synthetic",
         "config": {"workload": describe(cfg), "global_batch": 1, "seq_len": pos0 + n,
                    "decode_tokens_per_step": n, "parallelism": "single GPU, one persistent launch per request"},
@@ -275,7 +280,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="2b",
-                    help="2b (default), 2b_32k, moe, tiny, gemv, or copy (counter calibration)")
+                    help="2b (default), 2b_32k, 2b_fp8, moe, tiny, gemv, or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")

@@ -63,6 +63,18 @@ enum {
  * 1024 experts); the longest matrix-vector input (d_model, n_heads*head_dim,
  * ffn_dim, or top_k*ffn_dim for MoE) at most 8192; 2 <= vocab <= 65536;
  * max_seq <= 65536.
+ * weight_format selects how the streamed projection weights are held:
+ *  KIE_WEIGHTS_FP16: the fp16 tensors as given (RMSNorm gains folded in).
+ *  KIE_WEIGHTS_FP8:  OCP FP8 E4M3 with one fp32 scale per row, the route to
+ *    fewer bytes per token that the agentlenshq.com article names ("Scaling to
+ *    frontier MoE models": FP8/FP4 quantisation). kie_load quantizes each
+ *    projection after folding in the RMSNorm gain that precedes it (Wq, Wk,
+ *    Wv: g_attn; Wg, Wu: g_ffn; W_lm: g_final; Wo, Wd: none): for a row v of
+ *    fp32 values (v_k = w_k * g_k), s = fp32(max_k |v_k| / 448) (1 for an
+ *    all-zero row) and q_k = E4M3 nearest to fp32(v_k / s), ties to the even
+ *    code (kie_quantize_e4m3_rows). The embedding stays fp16. Dense models
+ *    with head_dim 128 only; d_model, ffn_dim and n_heads*head_dim multiples
+ *    of 512, vocab even.
  */
 typedef struct kie_config {
     int32_t n_layers;
@@ -77,7 +89,23 @@ typedef struct kie_config {
     float rms_eps;       /* RMSNorm: x / sqrt(mean(x^2) + eps) * g */
     float rope_theta;    /* rotary base; pairs (i, i + head_dim/2) */
     int32_t max_seq;     /* KV-cache capacity in positions */
+    int32_t weight_format;   /* KIE_WEIGHTS_FP16 (0) or KIE_WEIGHTS_FP8 (1) */
 } kie_config;
+
+enum { KIE_WEIGHTS_FP16 = 0, KIE_WEIGHTS_FP8 = 1 };
+
+/*
+ * The library's FP8 quantizer, as kie_load applies it (host only, no device
+ * call): rows x K fp16 weights w (row-major, host) and an optional fp16 gain
+ * [K] (NULL = 1) -> q [rows][K] E4M3 codes and scales [rows] fp32, with
+ * s = fp32(max_k |fp32(w_k) * fp32(g_k)| / 448) (1 for an all-zero row) and
+ * q_k the E4M3 code nearest to fp32(fp32(w_k) * fp32(g_k) / s), ties to the
+ * even code, saturating at 448. E4M3 is the OCP 8-bit float with 4 exponent
+ * bits (bias 7), 3 mantissa bits, no infinities, code 0x7f/0xff = NaN.
+ * Returns KIE_OK or KIE_ERR_ARG.
+ */
+int kie_quantize_e4m3_rows(const void* w_fp16, const void* gain_fp16, int32_t rows, int32_t K, uint8_t* q,
+                           float* scales);
 
 /*
  * Optional per-call debug outputs and teacher forcing (all host memory).
@@ -292,6 +320,11 @@ int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_
  */
 int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                               int32_t* errors);
+
+/* FP8 conversion probe: out256 (host) receives the fp32 value the device's
+ * E4M3 conversion (the one the fp8 GEMVs use) gives each code 0..255. Uses the
+ * library's own 64 KiB device array (no allocation); waits for the launch. */
+int kie_e4m3_table_probe(float* out256, void* hip_stream);
 
 /* XCD placement probe: out_xcd (host, [256]) receives the XCD (0..7 on
  * MI355X) that workgroup w of a 256-workgroup cooperative launch ran on, read

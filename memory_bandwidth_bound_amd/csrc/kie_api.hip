@@ -187,8 +187,12 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
         delete m;
         return code;
     };
+    std::vector<float> scales(D.w8 ? (size_t)D.L * L.layer_scales + D.V : 0);
     for (int l = 0; l < D.L; ++l) {
-        repack_layer(*cfg, L, T, l, (uint16_t*)stage.data());
+        if (D.w8)
+            repack_layer_fp8(*cfg, L, T, l, stage.data(), scales.data() + (size_t)l * L.layer_scales);
+        else
+            repack_layer(*cfg, L, T, l, (uint16_t*)stage.data());
         if ((rc = upload(m, L.off_layers + (size_t)l * L.layer_bytes, stage.data(), L.layer_bytes)) != KIE_OK)
             return bail(rc);
         if (D.E) {
@@ -199,7 +203,12 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
             }
         }
     }
-    repack_lm(*cfg, L, T, (uint16_t*)stage.data());
+    if (D.w8) {
+        repack_lm_fp8(*cfg, L, T, stage.data(), scales.data() + (size_t)D.L * L.layer_scales);
+        if ((rc = upload(m, L.off_scales, scales.data(), scales.size() * 4)) != KIE_OK) return bail(rc);
+    } else {
+        repack_lm(*cfg, L, T, (uint16_t*)stage.data());
+    }
     if ((rc = upload(m, L.off_lm, stage.data(), L.lm_bytes)) != KIE_OK) return bail(rc);
     if ((rc = upload(m, L.off_emb, T[tidx_emb()], (size_t)D.V * D.d * 2)) != KIE_OK) return bail(rc);
     rope_table(*cfg, (float*)stage.data());
@@ -281,6 +290,8 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.plan = (const int32_t*)(m->ws + L.off_plan);
         a.idle = m->ws + L.off_idle;
         a.trace = (int64_t*)(m->ws + L.off_trace);
+        a.scales = D.w8 ? (const float*)(m->ws + L.off_scales) : nullptr;
+        a.layer_scales = (int32_t)L.layer_scales;
         a.pos0 = m->pos + s0;
         a.pending = tok;
         a.n_steps = nc;
@@ -293,7 +304,8 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
         __atomic_store_n(m->habort, 0u, __ATOMIC_SEQ_CST);
         HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
-        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, skip_lm, kGrid, m->stream));
+        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w8 != 0, skip_lm, kGrid,
+                                 m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
         // Host watchdog: poll the launch's end event against a wall-clock
         // limit. Past it, raise the host word the kernel's long waits read
@@ -443,6 +455,15 @@ int kie_state(const kie_model* m, int32_t* pos, int32_t* pending) {
 float kie_last_kernel_ms(const kie_model* m) { return m ? m->last_ms : 0.f; }
 int32_t kie_grid_size(const kie_model* m) { return m ? kGrid : 0; }
 
+int kie_quantize_e4m3_rows(const void* w_fp16, const void* gain_fp16, int32_t rows, int32_t K, uint8_t* q,
+                           float* scales) {
+    if (!w_fp16 || !q || !scales || rows < 0 || K < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    const uint16_t* w = (const uint16_t*)w_fp16;
+    for (int r = 0; r < rows; ++r)
+        quantize_row_e4m3(w + (size_t)r * K, (const uint16_t*)gain_fp16, K, q + (size_t)r * K, scales + r);
+    return KIE_OK;
+}
+
 int kie_set_limits(kie_model* m, uint32_t spin_limit, int32_t watchdog_ms) {
     if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
     m->spin_limit = spin_limit ? spin_limit : kDefaultSpin;
@@ -563,6 +584,17 @@ int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream,
     const auto t1 = std::chrono::steady_clock::now();
     HIP_TRY(nullptr, hipMemcpy(errors, err, 4, hipMemcpyDeviceToHost));
     *us_per_round = (float)(std::chrono::duration<double, std::micro>(t1 - t0).count() / rounds);
+    return KIE_OK;
+}
+
+int kie_e4m3_table_probe(float* out256, void* hip_stream) {
+    if (!out256) return fail(nullptr, KIE_ERR_ARG, "null output");
+    hipStream_t s = (hipStream_t)hip_stream;
+    void* ptr = nullptr;   // the no-alloc scratch: 256 floats of output
+    HIP_TRY(nullptr, noalloc_scratch(&ptr));
+    HIP_TRY(nullptr, launch_e4m3_table((float*)ptr, s));
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    HIP_TRY(nullptr, hipMemcpy(out256, ptr, 256 * sizeof(float), hipMemcpyDeviceToHost));
     return KIE_OK;
 }
 

@@ -6,7 +6,9 @@
 //  * how each phase's rows are split over the workgroups of the persistent
 //    grid (the same split for the output projection and the FFN down
 //    projection, so each residual element has exactly one owner),
-//  * the streaming unit: 1 KiB = one wave-wide 16-byte-per-lane load,
+//  * the streaming unit: 1 KiB = one wave-wide 16-byte-per-lane load (fp16
+//    weights: 512 columns of one row; fp8 weights: 512 columns of a pair of
+//    rows, lane l holding 8 bytes of each),
 //  * the per-workgroup weight stream: for every layer, one contiguous piece
 //    holding that workgroup's rows of every phase in phase order, then its
 //    rows of the LM head.
@@ -58,6 +60,7 @@ enum Phase : int {
 
 struct Dims {
     int L, d, H, Hkv, hd, F, V, E, topk, max_seq;
+    int w8;   // 1: fp8 (E4M3) weights with one fp32 scale per row; 0: fp16 weights
 };
 
 struct RowSplit {
@@ -82,6 +85,11 @@ KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Units of a slab of nrows rows of K fp16 each, padded to whole units.
 KIE_HD int slab_units(int nrows, int K) { return ceil_div(nrows * K, kUnitHalves); }
+// The same for the weight format of D (fp8 rows take one byte per weight and
+// come in pairs, so nrows is even and a unit holds 1024 weights).
+KIE_HD int slab_units_of(const Dims& D, int nrows, int K) {
+    return D.w8 ? ceil_div(nrows * K, 2 * kUnitHalves) : slab_units(nrows, K);
+}
 
 // Shape of a phase matrix: rows M, row length K (fp16), split granularity.
 struct PhaseShape {
@@ -100,7 +108,7 @@ KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
     case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;
     case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = 1; break;
-    case PH_LM: s.M = D.V; s.K = D.d; s.gran = 1; break;
+    case PH_LM: s.M = D.V; s.K = D.d; s.gran = D.w8 ? 2 : 1; break;   // fp8: rows in pairs
     case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;   // K per selected expert
     default: s.M = 0; s.K = 0; s.gran = 1; break;
@@ -112,7 +120,7 @@ KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
 KIE_HD int phase_units(const Dims& D, int ph, int nwg, int w) {
     PhaseShape s = phase_shape(D, ph);
     RowSplit r = split_rows(s.M, s.gran, nwg, w);
-    if (ph == PH_EDOWN) return D.topk * slab_units(r.nrows, s.K);
+    if (ph == PH_EDOWN) return D.topk * slab_units_of(D, r.nrows, s.K);
     if (ph == PH_EGU) {
         // the workgroup's virtual rows may span several experts; each expert
         // segment is padded on its own
@@ -122,12 +130,12 @@ KIE_HD int phase_units(const Dims& D, int ph, int nwg, int w) {
         while (a < end) {
             int seg_end = (a / per + 1) * per;
             if (seg_end > end) seg_end = end;
-            u += slab_units(seg_end - a, s.K);
+            u += slab_units_of(D, seg_end - a, s.K);
             a = seg_end;
         }
         return u;
     }
-    return slab_units(r.nrows, s.K);
+    return slab_units_of(D, r.nrows, s.K);
 }
 
 // Phases whose weights sit in the per-layer streaming block, in stream order.

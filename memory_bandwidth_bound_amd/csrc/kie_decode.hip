@@ -197,6 +197,7 @@ struct Smem {
         float att_o[kCompute * kMaxGroup * 128];   // attention: per compute wave, unnormalised o
     };
     float att_q[kMaxGroup * 128];               // queries of the attention group, pre-scaled (also scratch)
+    static_assert(sizeof(uint16_t) * 2 * kMaxIn == sizeof(float) * kMaxIn, "fp32 staging reuses xin and xlo");
     alignas(16) uint16_t att_k[128];            // the new position's key and value
     alignas(16) uint16_t att_v[128];
     float att_ml[kCompute * kMaxGroup * 2];     // per compute wave: (max, sum)
@@ -240,11 +241,19 @@ __device__ __forceinline__ void write_geo(const DecodeArgs& a, const WgPlan& W, 
 
 // Stage input element i in LDS as two fp16 terms: xin = fp16(v), xlo =
 // fp16(v - xin). A GEMV sums the products with both, so its input keeps about
-// 22 significant bits while every product is a v_dot2 of fp16 pairs.
+// 22 significant bits while every product is a v_dot2 of fp16 pairs. With fp8
+// weights (W8) the input is staged as fp32 over the same bytes (xf) and the
+// products are fp32 multiply-adds of converted weights.
+__device__ __forceinline__ KIE_LDS float* xf_of(KIE_LDS Smem* S) { return (KIE_LDS float*)S->xin; }
+template <bool W8>
 __device__ __forceinline__ void stage1(KIE_LDS Smem* S, int i, float v) {
-    const _Float16 hi = (_Float16)v;
-    S->xin[i] = __builtin_bit_cast(uint16_t, hi);
-    S->xlo[i] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi));
+    if constexpr (W8) {
+        xf_of(S)[i] = v;
+    } else {
+        const _Float16 hi = (_Float16)v;
+        S->xin[i] = __builtin_bit_cast(uint16_t, hi);
+        S->xlo[i] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi));
+    }
 }
 
 // Every wave of the workgroup gathers its slice of the phase's input vector
@@ -253,6 +262,7 @@ __device__ __forceinline__ void stage1(KIE_LDS Smem* S, int i, float v) {
 // norm scale is applied to the row sums afterwards, which is the same product
 // since a GEMV is linear. Returns 0, or 1 (this wave timed out) / 2 (another
 // workgroup reported a failure).
+template <bool W8>
 __device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S, int kind, int n, uint32_t id,
                                             int w) {
     const uint64_t* src = kind == K_WO ? a.ex.o : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
@@ -261,7 +271,7 @@ __device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S
     const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, a.habort, [&](int i, uint32_t v) {
         const float x = __builtin_bit_cast(float, v);
         ss += x * x;
-        stage1(S, i0 + i, x);
+        stage1<W8>(S, i0 + i, x);
     });
     ss = wave_sum(ss);
     if (lane_id() == 0) S->ssp[w] = ss;
@@ -354,7 +364,7 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
 // ------------------------------------------------------------------------
 // Communication wave.
 // ------------------------------------------------------------------------
-template <int HD>
+template <int HD, bool W8>
 struct Comm {
     const DecodeArgs& a;
     KIE_LDS Smem* S;
@@ -362,6 +372,7 @@ struct Comm {
     int wg, lane, tok;
     bool dead;
     float rq[4];   // QKV epilogue: (cos, sin) of this lane's two rotary pairs, loaded before the input gather
+    float rs[4];   // fp8 weights: scales of the rows this lane's epilogue handles, loaded before the input gather
 
     __device__ __forceinline__ Comm(const DecodeArgs& args, KIE_LDS Smem* s, const WgPlan& plan)
         : a(args), S(s), W(plan) {
@@ -394,8 +405,39 @@ struct Comm {
     __device__ __forceinline__ void input_share(int kind, uint32_t id) {
         if (dead) return;
         const int n = S->geo[kind].gin;
-        const int r = gather_input(a, S, kind, n, id, 0);
+        const int r = gather_input<W8>(a, S, kind, n, id, 0);
         if (r) fail(r);
+    }
+
+    // fp8 weights: the row scales this lane's epilogue multiplies by. Row
+    // r of lane e-th slot: QKV and gate/up 4 lane + e, Wo and down 2 lane + e,
+    // LM lane + 64 e (the epilogues' row loops below). Read before the input
+    // gather, so the trip overlaps it; rows past the phase read scale 1.
+    __device__ __forceinline__ void load_row_scales(int kind, int layer) {
+        if constexpr (W8) {
+            const Dims& D = a.D;
+            const int mq = (D.H + 2 * D.Hkv) * HD, mo = D.d, mg = 2 * D.F;
+            const KIE_GLOBAL float* b = gptr(a.scales) + (size_t)layer * a.layer_scales;
+            int r0 = 0, n = 0, step = 1, mul = 1;
+            switch (kind) {
+            case K_QKV: b += 0; r0 = W.q0; n = W.qn; mul = 4; break;
+            case K_WO: b += mq; r0 = W.wo0; n = W.won; mul = 2; break;
+            case K_GU: b += mq + mo; r0 = W.gu0; n = W.gun; mul = 4; break;
+            case K_DOWN: b += mq + mo + mg; r0 = W.wo0; n = W.won; mul = 2; break;
+            case K_LM: b = gptr(a.scales) + (size_t)D.L * a.layer_scales; r0 = W.lm0; n = W.lmn; step = 64; mul = 1;
+                break;
+            default: break;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = step == 64 ? lane + 64 * e : mul * lane + e;
+                rs[e] = (r < n && (step == 64 || e < mul)) ? b[r0 + r] : 1.0f;
+            }
+        }
+    }
+    __device__ __forceinline__ float rsc(int e) const {
+        if constexpr (W8) return rs[e];
+        return 1.0f;
     }
 
     // the first layer's input: the token's embedding row, staged whole here
@@ -405,7 +447,7 @@ struct Comm {
         for (int i = lane; i < d; i += 64) {
             const float x = h2f_bits(gptr(e)[i]);
             ss += x * x;
-            stage1(S, i, x);
+            stage1<W8>(S, i, x);
         }
         ss = wave_sum(ss);
         if (lane < kWaves) S->ssp[lane] = lane == 0 ? ss : 0.f;
@@ -432,9 +474,9 @@ struct Comm {
 
     // Add the projection to the owned residual rows and publish them.
     __device__ __forceinline__ void residual_add_publish(uint32_t id) {
-        for (int j = 2 * lane; j < W.won; j += 128) {
-            const float x0 = S->own_x[j] + rowsum(j);
-            const float x1 = S->own_x[j + 1] + rowsum(j + 1);
+        for (int j = 2 * lane; j < W.won; j += 128) {   // at most 32 rows: one trip
+            const float x0 = S->own_x[j] + rowsum(j) * rsc(0);
+            const float x1 = S->own_x[j + 1] + rowsum(j + 1) * rsc(1);
             S->own_x[j] = x0;
             S->own_x[j + 1] = x1;
             fw_store(a.ex.x + W.wo0 + j, __builtin_bit_cast(uint32_t, x0), id);
@@ -489,6 +531,7 @@ struct Comm {
         const Dims& D = a.D;
         if (dead) return;
         const int q = it.q;
+        load_row_scales(kind, it.layer);
         switch (kind) {
         case K_QKV: {
             // the epilogue's RoPE table entries, read now so that their trip
@@ -575,7 +618,7 @@ struct Comm {
                 const int vr = W.q0 + 4 * j;
                 float y[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = rowsum(4 * j + e) * sc;
+                for (int e = 0; e < 4; ++e) y[e] = rowsum(4 * j + e) * sc * rsc(e);   // one trip: qn / 4 <= 64
                 if (vr < qd + kd) {
                     // rows (4j, 4j+1) = elements (i, i+hd/2), rows (4j+2, 4j+3) = (i+1, i+1+hd/2)
                     const int i = (vr % HD) >> 1;
@@ -627,11 +670,12 @@ struct Comm {
         case K_GU: {
             // rows (4j .. 4j+3) = (g_m, u_m, g_m+1, u_m+1) with m = (gu0 + 4j) / 2
             const float sc = in_scale();
-            for (int j = lane; j < W.gun / 4; j += 64) {
+            for (int j = lane; j < W.gun / 4; j += 64) {   // one trip: gun / 4 <= 64
                 float h[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const float gv = rowsum(4 * j + 2 * e) * sc, uv = rowsum(4 * j + 2 * e + 1) * sc;
+                    const float gv = rowsum(4 * j + 2 * e) * sc * rsc(2 * e);
+                    const float uv = rowsum(4 * j + 2 * e + 1) * sc * rsc(2 * e + 1);
                     h[e] = gv / (1.0f + __expf(-gv)) * uv;
                 }
                 const int m = W.gu0 / 2 + 2 * j;
@@ -667,11 +711,15 @@ struct Comm {
             int bi = 0x7fffffff;
             const bool dbg = (a.flags & F_DBG_LOGITS) != 0;
             const float sc = in_scale();
-            for (int j = lane; j < W.lmn; j += 64) {
-                const float v = rowsum(j) * sc;
-                const int r = W.lm0 + j;
-                if (dbg) gptr(a.dbg_logits)[(size_t)(it.step % 64) * D.V + r] = v;
-                if (v > bv || (v == bv && r < bi)) { bv = v; bi = r; }
+#pragma unroll
+            for (int e = 0; e < kMaxRowsWg / 64; ++e) {   // lmn <= 256 rows
+                const int j = lane + 64 * e;
+                if (j < W.lmn) {
+                    const float v = rowsum(j) * sc * rsc(e);
+                    const int r = W.lm0 + j;
+                    if (dbg) gptr(a.dbg_logits)[(size_t)(it.step % 64) * D.V + r] = v;
+                    if (v > bv || (v == bv && r < bi)) { bv = v; bi = r; }
+                }
             }
             wave_argmax(bv, bi);
             if (lane == 0) {
@@ -867,7 +915,54 @@ struct WaveGeo {
     int upr;      // units per row segment (0: 256-wide rows, two per unit)
 };
 
-template <int HD>
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+// One fp8 unit against 8 fp32 inputs: the lane's 16 bytes are 8 E4M3 weights
+// of row a then 8 of row b (the same 8 columns); each is converted exactly to
+// fp32 (v_cvt_pk_f32_fp8, two per instruction) and multiplied-added into its
+// row's accumulator.
+__device__ __forceinline__ void dot8_fp8(uint4 w, const float (&x)[8], float& aa, float& ab) {
+    v2f_t p;
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    aa = fmaf(p.x, x[0], aa);
+    aa = fmaf(p.y, x[1], aa);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    aa = fmaf(p.x, x[2], aa);
+    aa = fmaf(p.y, x[3], aa);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    aa = fmaf(p.x, x[4], aa);
+    aa = fmaf(p.y, x[5], aa);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    aa = fmaf(p.x, x[6], aa);
+    aa = fmaf(p.y, x[7], aa);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, false);
+    ab = fmaf(p.x, x[0], ab);
+    ab = fmaf(p.y, x[1], ab);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, true);
+    ab = fmaf(p.x, x[2], ab);
+    ab = fmaf(p.y, x[3], ab);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, false);
+    ab = fmaf(p.x, x[4], ab);
+    ab = fmaf(p.y, x[5], ab);
+    p = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, true);
+    ab = fmaf(p.x, x[6], ab);
+    ab = fmaf(p.y, x[7], ab);
+}
+
+// The 8 fp32 inputs of this lane in input segment c (512 elements).
+__device__ __forceinline__ void load_xf(KIE_LDS Smem* S, int off, float (&x)[8]) {
+    const uint4 u0 = lds_ld16(xf_of(S) + off), u1 = lds_ld16(xf_of(S) + off + 4);
+    x[0] = __builtin_bit_cast(float, u0.x);
+    x[1] = __builtin_bit_cast(float, u0.y);
+    x[2] = __builtin_bit_cast(float, u0.z);
+    x[3] = __builtin_bit_cast(float, u0.w);
+    x[4] = __builtin_bit_cast(float, u1.x);
+    x[5] = __builtin_bit_cast(float, u1.y);
+    x[6] = __builtin_bit_cast(float, u1.z);
+    x[7] = __builtin_bit_cast(float, u1.w);
+}
+
+template <int HD, bool W8>
 struct Compute {
     const DecodeArgs& a;
     KIE_LDS Smem* S;
@@ -883,6 +978,7 @@ struct Compute {
     WaveGeo cg;        // geometry of the phase being consumed
     int crow, cseg, ck;   // row, unit in the row segment and segment (MoE down: expert) of the next unit
     float acc;         // running partial dot product of the current row
+    float acc2;        // fp8 weights: the second row of the current pair (crow counts pairs)
 
     __device__ __forceinline__ Compute(const DecodeArgs& args, KIE_LDS Smem* s, int wi) : a(args), S(s), w(wi) {
         lane = lane_id();
@@ -895,7 +991,7 @@ struct Compute {
         entered = false;
         cg.q = -1;
         crow = cseg = ck = 0;
-        acc = 0.f;
+        acc = acc2 = 0.f;
         ic = PIter{0, 0, 0, 0};
         seek(false);
     }
@@ -1030,7 +1126,7 @@ struct Compute {
             wg_barrier();   // the communication wave is done with the previous phases
             if (!stop) {
                 const int n = __builtin_amdgcn_readfirstlane(S->geo[kind].gin);
-                const int r = gather_input(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1);
+                const int r = gather_input<W8>(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1);
                 if (r && lane == 0) {
                     if (r == 1) dev_store32(a.status, (uint32_t)kStatusTimeout);
                     S->abort = 1u;
@@ -1141,6 +1237,51 @@ struct Compute {
         }
     }
 
+    // fp8 weights: the same with pairs of rows per unit; xf[j] holds the fp32
+    // input of segment (cseg + j) % UPR.
+    template <int UPR>
+    __device__ __forceinline__ void consume_reg_fp8(uint32_t src, const Slot& sl, float (&xf)[UPR][8]) {
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
+        uint4 wv[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; ++s)
+            if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
+        const int last = cg.hi - 1 - sl.u0;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) {
+            if (s < sl.n) {
+                dot8_fp8(wv[s], xf[s % UPR], acc, acc2);
+                const bool seg_done = cseg + 1 == UPR;
+                if (seg_done || s == last) {
+                    const float ra = wave_sum_to_lane63(acc), rb = wave_sum_to_lane63(acc2);
+                    if (lane == 63) {
+                        S->part[(2 * crow) * kCompute + w] += ra;
+                        S->part[(2 * crow + 1) * kCompute + w] += rb;
+                    }
+                    acc = acc2 = 0.f;
+                }
+                if (seg_done) {
+                    cseg = 0;
+                    ++crow;
+                } else {
+                    ++cseg;
+                }
+            }
+        }
+        constexpr int R = kNB % UPR;
+        if (R && sl.n == kNB) {
+            float t[UPR][8];
+#pragma unroll
+            for (int j = 0; j < UPR; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t[j][e] = xf[(j + R) % UPR][e];
+#pragma unroll
+            for (int j = 0; j < UPR; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[j][e] = t[j][e];
+        }
+    }
+
     // Consume every batch of the current phase at the head of the ring with
     // the input in registers (rows of UPR units, one input segment for all
     // rows), refilling each batch as it goes. On return sq[0] belongs to a
@@ -1149,6 +1290,24 @@ struct Compute {
     __device__ __forceinline__ void stream_phase(Slot (&sq)[kNS], int& head) {
         const int q = sq[0].q;
         if (cg.q != q) enter_geo(sq[0]);
+        if constexpr (W8) {
+            float xf[UPR][8];
+#pragma unroll
+            for (int j = 0; j < UPR; ++j) load_xf(S, ((cseg + j) % UPR) * kUnitHalves + lane * 8, xf[j]);
+            while (sq[0].q == q && sq[0].n > 0) {
+                const uint32_t at = ring0 + head * kBatchBytes;
+                wait_vm<(kNS - 1) * kNB>();
+                consume_reg_fp8<UPR>(at, sq[0], xf);
+                wait_lgkm0();
+                finish_if_done(sq);
+                const Slot t = fill(at);
+#pragma unroll
+                for (int i = 0; i + 1 < kNS; ++i) sq[i] = sq[i + 1];
+                sq[kNS - 1] = t;
+                head = (head + 1 == kNS) ? 0 : head + 1;
+            }
+            return;
+        }
         uint4 xh[UPR], xq[UPR];
 #pragma unroll
         for (int j = 0; j < UPR; ++j) {
@@ -1179,7 +1338,8 @@ struct Compute {
     __device__ __forceinline__ void enter_geo(const Slot& sl) {
         load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
         if (cg.upr) {
-            const int per_seg = cg.nrows * cg.upr;
+            // crow counts rows (fp8: pairs of rows, two per unit)
+            const int per_seg = (W8 ? cg.nrows / 2 : cg.nrows) * cg.upr;
             ck = cg.lo / per_seg;
             const int rem = cg.lo - ck * per_seg;
             crow = rem / cg.upr;
@@ -1187,8 +1347,47 @@ struct Compute {
         }
     }
 
+    // fp8 weights, any row length: the inputs of each unit read from LDS
+    // (dense only: one segment per row pair).
+    __device__ __forceinline__ void consume_fp8(uint32_t src, const Slot& sl) {
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
+        const int upr = cg.upr;
+        uint4 wv[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; ++s)
+            if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
+        const int last = cg.hi - 1 - sl.u0;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) {
+            if (s < sl.n) {
+                float x[8];
+                load_xf(S, cseg * kUnitHalves + lane * 8, x);
+                dot8_fp8(wv[s], x, acc, acc2);
+                const bool seg_done = cseg + 1 == upr;
+                if (seg_done || s == last) {
+                    const float ra = wave_sum_to_lane63(acc), rb = wave_sum_to_lane63(acc2);
+                    if (lane == 63) {
+                        S->part[(2 * crow) * kCompute + w] += ra;
+                        S->part[(2 * crow + 1) * kCompute + w] += rb;
+                    }
+                    acc = acc2 = 0.f;
+                }
+                if (seg_done) {
+                    cseg = 0;
+                    ++crow;
+                } else {
+                    ++cseg;
+                }
+            }
+        }
+    }
+
     __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
         if (cg.q != sl.q) enter_geo(sl);
+        if constexpr (W8) {
+            consume_fp8(src, sl);
+            return;
+        }
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
         uint4 wv[kNB], xv[kNB], xl[kNB];
         if (cg.upr) {
@@ -1429,7 +1628,7 @@ struct Compute {
     }
 };
 
-template <int HD>
+template <int HD, bool W8>
 __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WgPlan W;
@@ -1442,35 +1641,40 @@ __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S
     }
     __syncthreads();
     if (wave == 0) {
-        Comm<HD> cm(a, S, W);
+        Comm<HD, W8> cm(a, S, W);
         cm.run();
     } else {
-        Compute<HD> cp(a, S, wave - 1);
+        Compute<HD, W8> cp(a, S, wave - 1);
         cp.run();
     }
 }
 
 // Two symbols for the same code, so that profiles keep the prompt's passes
 // apart from the generation requests.
-template <int HD>
+template <int HD, bool W8>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, W8>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
-template <int HD>
+template <int HD, bool W8>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, W8>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool prefill, int grid, hipStream_t s) {
+// The fp8-weight kernels are built for head_dim 128 only (the decoders whose
+// widths fp8 needs: every projection width a multiple of 512).
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool prefill, int grid, hipStream_t s) {
     void* args[] = {&dev_args};
     const void* fn;
+    if (w8 && hd != 128) return hipErrorInvalidValue;
     if (prefill)
-        fn = hd == 64 ? (const void*)prefill_kernel<64> : (const void*)prefill_kernel<128>;
+        fn = w8 ? (const void*)prefill_kernel<128, true>
+                : (hd == 64 ? (const void*)prefill_kernel<64, false> : (const void*)prefill_kernel<128, false>);
     else
-        fn = hd == 64 ? (const void*)decode_kernel<64> : (const void*)decode_kernel<128>;
+        fn = w8 ? (const void*)decode_kernel<128, true>
+                : (hd == 64 ? (const void*)decode_kernel<64, false> : (const void*)decode_kernel<128, false>);
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 

@@ -27,6 +27,7 @@ Dims dims_of(const kie_config& c) {
     D.E = c.n_experts;
     D.topk = c.n_experts ? c.top_k : 0;
     D.max_seq = c.max_seq;
+    D.w8 = c.weight_format == KIE_WEIGHTS_FP8 ? 1 : 0;
     return D;
 }
 
@@ -71,6 +72,15 @@ int validate_config(const kie_config& c, std::string* err) {
         if (c.d_model % 512 || c.ffn_dim % 512) return fail("MoE needs d_model and ffn_dim multiples of 512");
     }
     if (c.vocab > kMaxRowsWg * kGrid) return fail("vocab must be at most 65536");
+    if (c.weight_format != KIE_WEIGHTS_FP16 && c.weight_format != KIE_WEIGHTS_FP8)
+        return fail("weight_format must be KIE_WEIGHTS_FP16 or KIE_WEIGHTS_FP8");
+    if (c.weight_format == KIE_WEIGHTS_FP8) {
+        if (c.n_experts) return fail("fp8 weights are supported for dense models only");
+        if (c.head_dim != 128) return fail("fp8 weights are supported for head_dim 128 only");
+        if (c.d_model % 512 || c.ffn_dim % 512 || (c.n_heads * c.head_dim) % 512)
+            return fail("fp8 weights need d_model, ffn_dim and n_heads*head_dim multiples of 512");
+        if (c.vocab % 2) return fail("fp8 weights need an even vocab (LM rows come in pairs)");
+    }
     Dims D = dims_of(c);
     // LDS budget: input vector, per-phase partial sums, owned residual rows
     int max_in = c.d_model;
@@ -150,6 +160,11 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_args = take(4096);
     Y.off_idle = take(16384);
     Y.off_trace = take((size_t)kTracePhases * kGrid * 4 * 8);
+    Y.layer_scales = 0;
+    if (D.w8) {
+        for (int i = 0; i < layer_block_phase_count(D); ++i) Y.layer_scales += phase_shape(D, layer_block_phase(D, i)).M;
+        Y.off_scales = take(((size_t)D.L * Y.layer_scales + D.V) * 4);
+    }
     Y.total = off;
 }
 
@@ -291,6 +306,136 @@ void repack_expert(const kie_config& c, const Layout& lay, const uint16_t* const
     for (int r = 0; r < 2 * D.F; ++r)
         put_row(dst + (size_t)r * D.d, ((r & 1) ? Wu : Wg) + (size_t)(r >> 1) * D.d, D.d, g, g1);
     std::memcpy(dst + (size_t)2 * D.F * D.d, Wd, (size_t)D.d * D.F * 2);
+}
+
+// ---------------------------------------------------------------- fp8 ------
+// E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
+// subnormal (m/8 * 2^-6), exponent 15 with mantissa 7 is NaN, so the largest
+// finite value is 1.75 * 2^8 = 448.
+float e4m3_decode(uint8_t q) {
+    const int e = (q >> 3) & 15, m = q & 7;
+    const float s = (q & 0x80) ? -1.f : 1.f;
+    if (e == 15 && m == 7) return std::nanf("");
+    if (e == 0) return s * std::ldexp((float)m, -9);
+    return s * std::ldexp(8.f + m, e - 10);
+}
+
+uint8_t e4m3_encode(float v) {
+    if (std::isnan(v)) return 0x7f;
+    uint8_t sign = std::signbit(v) ? 0x80 : 0;
+    float a = std::fabs(v);
+    if (a >= 448.f) return sign | 0x7e;                       // saturate (no infinity)
+    if (a == 0.f) return sign;                                 // (+-)0: frexp gives no binade
+    // spacing of E4M3 values around a: 2^-9 below 2^-6, else 2^(E-3) for a in [2^E, 2^(E+1))
+    int E;
+    std::frexp(a, &E);                                         // a = f * 2^E, f in [0.5, 1)
+    --E;
+    if (E < -6) E = -6;
+    const float step = std::ldexp(1.f, E - 3);
+    const float n = std::nearbyint(a / step);                  // exact division by a power of two; ties to even
+    // n counts steps: 0..8 below 2^-6 (8 = 2^-6, the smallest normal), else 8..16
+    int e = E + 7, m;
+    if (E == -6 && n < 8.f) {
+        e = 0;
+        m = (int)n;
+    } else if (n >= 16.f) {                                     // rounded up to the next binade
+        ++e;
+        m = 0;
+    } else {
+        m = (int)n - 8;
+    }
+    if (e > 15 || (e == 15 && m == 7)) return sign | 0x7e;    // beyond 448 rounds down to it
+    return sign | (uint8_t)(e << 3) | (uint8_t)m;
+}
+
+void quantize_row_e4m3(const uint16_t* w, const uint16_t* gain, int K, uint8_t* q, float* scale) {
+    float amax = 0.f;
+    for (int k = 0; k < K; ++k) {
+        const float v = f16_to_f32(w[k]) * (gain ? f16_to_f32(gain[k]) : 1.f);
+        amax = std::fmax(amax, std::fabs(v));
+    }
+    const float s = amax > 0.f ? amax / 448.f : 1.f;
+    for (int k = 0; k < K; ++k) {
+        const float v = f16_to_f32(w[k]) * (gain ? f16_to_f32(gain[k]) : 1.f);
+        q[k] = e4m3_encode(v / s);
+    }
+    *scale = s;
+}
+
+// One pair of quantized rows (qa, qb) of K columns as K/512 units: unit s,
+// lane l holds qa[512 s + 8 l .. + 8] then qb[512 s + 8 l .. + 8].
+static void put_pair_fp8(uint8_t* dst, const uint8_t* qa, const uint8_t* qb, int K) {
+    for (int s = 0; s < K / 512; ++s)
+        for (int l = 0; l < 64; ++l) {
+            std::memcpy(dst + ((size_t)s * 64 + l) * 16, qa + s * 512 + 8 * l, 8);
+            std::memcpy(dst + ((size_t)s * 64 + l) * 16 + 8, qb + s * 512 + 8 * l, 8);
+        }
+}
+
+void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int l, uint8_t* dst,
+                      float* scales) {
+    const Dims& D = lay.D;
+    const uint16_t* g_attn = t[tidx_layer(c, l, 0)];
+    const uint16_t* g_ffn = t[tidx_layer(c, l, 5)];
+    std::memset(dst, 0, lay.layer_bytes);
+    std::vector<uint8_t> qa(kMaxInput), qb(kMaxInput);
+    // source row (pointer, gain) of a phase row
+    auto source = [&](int ph, int row, const uint16_t** src, const uint16_t** g) {
+        *g = nullptr;
+        switch (ph) {
+        case PH_QKV: {
+            int mat, r;
+            qkv_row_source(D, row, &mat, &r);
+            *src = t[tidx_layer(c, l, 1 + mat)] + (size_t)r * D.d;
+            *g = g_attn;
+            break;
+        }
+        case PH_WO: *src = t[tidx_layer(c, l, 4)] + (size_t)row * D.H * D.hd; break;
+        case PH_GU:
+            *src = t[tidx_layer(c, l, (row & 1) ? 7 : 6)] + (size_t)(row >> 1) * D.d;
+            *g = g_ffn;
+            break;
+        default: *src = t[tidx_layer(c, l, 8)] + (size_t)row * D.F; break;   // PH_DOWN
+        }
+    };
+    size_t sbase = 0;   // this phase's first scale in the layer's scale block
+    for (int i = 0; i < layer_block_phase_count(D); ++i) {
+        const int ph = layer_block_phase(D, i);
+        const PhaseShape s = phase_shape(D, ph);
+        for (int w = 0; w < kGrid; ++w) {
+            size_t off = (size_t)lay.piece_off[w] * kUnitBytes;
+            for (int j = 0; j < i; ++j)
+                off += (size_t)phase_units(D, layer_block_phase(D, j), kGrid, w) * kUnitBytes;
+            const RowSplit r = split_rows(s.M, s.gran, kGrid, w);
+            for (int j = 0; j < r.nrows; j += 2) {
+                const uint16_t *sa, *sb, *ga, *gb;
+                source(ph, r.row0 + j, &sa, &ga);
+                source(ph, r.row0 + j + 1, &sb, &gb);
+                quantize_row_e4m3(sa, ga, s.K, qa.data(), &scales[sbase + r.row0 + j]);
+                quantize_row_e4m3(sb, gb, s.K, qb.data(), &scales[sbase + r.row0 + j + 1]);
+                put_pair_fp8(dst + off + (size_t)(j / 2) * s.K * 2, qa.data(), qb.data(), s.K);
+            }
+        }
+        sbase += s.M;
+    }
+}
+
+void repack_lm_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, uint8_t* dst, float* scales) {
+    const Dims& D = lay.D;
+    const uint16_t* g = t[tidx_gfinal(c)];
+    const uint16_t* W = t[tidx_lm(c)];
+    std::memset(dst, 0, lay.lm_bytes);
+    std::vector<uint8_t> qa(D.d), qb(D.d);
+    for (int w = 0; w < kGrid; ++w) {
+        const RowSplit r = split_rows(D.V, 2, kGrid, w);
+        uint8_t* p = dst + (size_t)lay.lm_off[w] * kUnitBytes;
+        for (int j = 0; j < r.nrows; j += 2) {
+            const int row = r.row0 + j;
+            quantize_row_e4m3(W + (size_t)row * D.d, g, D.d, qa.data(), &scales[row]);
+            quantize_row_e4m3(W + (size_t)(row + 1) * D.d, g, D.d, qb.data(), &scales[row + 1]);
+            put_pair_fp8(p + (size_t)(j / 2) * D.d * 2, qa.data(), qb.data(), D.d);
+        }
+    }
 }
 
 void rope_table(const kie_config& c, float* dst) {

@@ -46,6 +46,8 @@ struct Layout {
     size_t off_args;              // kernel argument block (4 KiB)
     size_t off_idle;              // 16 KiB read by weight batches that have nothing to stream
     size_t off_trace;             // i64 [kTracePhases][kGrid][4] phase timeline
+    size_t off_scales;            // fp8: f32 per layer [QKV rows][Wo rows][gate/up rows][down rows], then [V] LM
+    size_t layer_scales;          // floats per layer
     size_t total;
     int piece_off[kGrid + 1];     // units: start of workgroup w's piece in a layer block
     int lm_off[kGrid + 1];        // units: start of workgroup w's LM slab
@@ -72,6 +74,16 @@ void repack_expert(const kie_config& c, const Layout& lay, const uint16_t* const
                    int expert, uint16_t* dst);
 // cos/sin table, angles formed in double precision. dst: float [max_seq][hd/2][2].
 void rope_table(const kie_config& c, float* dst);
+
+// FP8 (E4M3) rows: the quantizer of kie_quantize_e4m3_rows.
+uint8_t e4m3_encode(float v);                 // nearest code, ties to even, saturating
+float e4m3_decode(uint8_t q);
+void quantize_row_e4m3(const uint16_t* w, const uint16_t* gain, int K, uint8_t* q, float* scale);
+// fp8 weights: one layer's streaming block (layer_bytes bytes) and its row
+// scales (layer_scales floats), and the LM head block and its V scales.
+void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, uint8_t* dst,
+                      float* scales);
+void repack_lm_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, uint8_t* dst, float* scales);
 
 // Canonical tensor index helpers (same order as kie.h documents).
 int tidx_emb();

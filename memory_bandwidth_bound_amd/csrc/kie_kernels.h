@@ -74,6 +74,8 @@ struct DecodeArgs {
     const int32_t* plan;     // piece_off[kGrid+1], lm_off[kGrid+1]
     const uint8_t* idle;     // kIdleBytes of zeros: target of loads that keep a batch slot busy
     int64_t* trace;          // [kTracePhases][kGrid][4] phase timeline (F_TRACE)
+    const float* scales;     // fp8 weights: per layer [QKV][Wo][gate/up][down] row scales, then [V] LM
+    int32_t layer_scales;    // floats per layer in scales
     int32_t pos0;
     int32_t pending;
     int32_t n_steps;
@@ -95,7 +97,7 @@ inline int phases_per_layer(const Dims& D) { return D.E ? 7 : 6; }
 inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2; }
 
 // Launchers. dev_args: the argument block already copied to device memory.
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool prefill, int grid, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool prefill, int grid, hipStream_t s);
 // Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
 // per workgroup, a contiguous range of units per wave, row sums added into y,
 // which the caller zeroes). Needs K <= kMaxInput.
@@ -108,6 +110,8 @@ hipError_t launch_gemv_direct(const GemvArgs& a, hipStream_t s);
 hipError_t launch_barrier_probe(int variant, uint64_t* words, uint32_t* status, int32_t* errors, int rounds,
                                 int grid, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);
+// out[c] = the device's fp8 (E4M3) conversion of code c, c < 256.
+hipError_t launch_e4m3_table(float* out, hipStream_t s);
 // out[w] = the XCD workgroup w of a grid-sized cooperative launch ran on.
 hipError_t launch_xcd_map(int32_t* out, int grid, hipStream_t s);
 // Zero n 32-bit words with a kernel.

@@ -301,6 +301,26 @@ __global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint6
 
 __global__ void empty_kernel() {}
 
+// Every E4M3 code converted by the device's fp8 conversion (the one the fp8
+// GEMVs use): out[c] = value of code c, one workgroup of 64 lanes, 4 codes
+// per lane.
+__global__ void __launch_bounds__(64, 1) e4m3_table_kernel(float* out) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const int l = threadIdx.x;
+    const uint32_t w = (uint32_t)(4 * l) | ((uint32_t)(4 * l + 1) << 8) | ((uint32_t)(4 * l + 2) << 16) |
+                       ((uint32_t)(4 * l + 3) << 24);
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    out[4 * l] = a.x;
+    out[4 * l + 1] = a.y;
+    out[4 * l + 2] = b.x;
+    out[4 * l + 3] = b.y;
+}
+
+hipError_t launch_e4m3_table(float* out, hipStream_t s) {
+    hipLaunchKernelGGL(e4m3_table_kernel, dim3(1), dim3(64), 0, s, out);
+    return hipGetLastError();
+}
+
 // The XCD every workgroup of a grid-sized launch runs on.
 __global__ void __launch_bounds__(64, 1) xcd_map_kernel(int32_t* out) {
     if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();

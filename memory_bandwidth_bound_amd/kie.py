@@ -28,7 +28,10 @@ class KieConfig(ctypes.Structure):
     _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_heads", c_int32),
                 ("n_kv_heads", c_int32), ("head_dim", c_int32), ("ffn_dim", c_int32),
                 ("vocab", c_int32), ("n_experts", c_int32), ("top_k", c_int32),
-                ("rms_eps", c_float), ("rope_theta", c_float), ("max_seq", c_int32)]
+                ("rms_eps", c_float), ("rope_theta", c_float), ("max_seq", c_int32),
+                ("weight_format", c_int32)]
+
+WEIGHT_FORMATS = {"fp16": 0, "fp8": 1}
 
 
 class KieDebug(ctypes.Structure):
@@ -82,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_launch_probe": (c_int32, [c_int32, c_void_p, POINTER(c_float)]),
         "kie_barrier_probe_noalloc": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
         "kie_xcd_map": (c_int32, [POINTER(c_int32), c_void_p]),
+        "kie_e4m3_table_probe": (c_int32, [POINTER(c_float), c_void_p]),
+        "kie_quantize_e4m3_rows": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -102,7 +107,8 @@ def make_config(cfg) -> KieConfig:
     """kie_config from a synth.DecoderConfig (or anything with the same fields)."""
     return KieConfig(cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                      cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k if cfg.n_experts else 0,
-                     cfg.rms_eps, cfg.rope_theta, cfg.max_seq)
+                     cfg.rms_eps, cfg.rope_theta, cfg.max_seq,
+                     WEIGHT_FORMATS[getattr(cfg, "weight_format", "fp16")])
 
 
 def expected_shapes(cfg):
@@ -371,6 +377,36 @@ def barrier_probe_noalloc(rounds: int, variant: int = 1, device: str = "cuda:0")
                                            ctypes.byref(err))
     _check(rc)
     return float(us.value), int(err.value)
+
+
+def quantize_e4m3_rows(W: np.ndarray, gain: Optional[np.ndarray] = None):
+    """The library's host FP8 quantizer (kie_quantize_e4m3_rows) on fp16 W
+    [rows][K] with an optional fp16 gain [K]: returns (codes uint8, scales f32)."""
+    lib = load_library()
+    W = np.ascontiguousarray(W, dtype=np.float16)
+    if W.ndim != 2:
+        raise KieError(-1, "W must be [rows][K]")
+    g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float16)
+    if g is not None and g.shape != (W.shape[1],):
+        raise KieError(-1, "gain must be [K]")
+    q = np.zeros(W.shape, dtype=np.uint8)
+    s = np.zeros(W.shape[0], dtype=np.float32)
+    _check(lib.kie_quantize_e4m3_rows(c_void_p(W.ctypes.data), None if g is None else c_void_p(g.ctypes.data),
+                                      W.shape[0], W.shape[1], c_void_p(q.ctypes.data),
+                                      s.ctypes.data_as(POINTER(c_float))))
+    return q, s
+
+
+def e4m3_table_probe(device: str = "cuda:0"):
+    """The fp32 values the device's E4M3 conversion gives codes 0..255."""
+    import torch
+    lib = load_library()
+    out = np.zeros(256, dtype=np.float32)
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        rc = lib.kie_e4m3_table_probe(out.ctypes.data_as(POINTER(c_float)), _stream_handle(torch, dev, None))
+    _check(rc)
+    return out
 
 
 def xcd_map(device: str = "cuda:0"):

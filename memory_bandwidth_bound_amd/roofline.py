@@ -15,11 +15,13 @@ HBM_PEAK_BYTES_PER_S = 8.0e12      # MI355X HBM3E, published peak
 
 
 def active_weight_bytes(cfg) -> int:
-    """fp16 bytes of weights read for one token.
+    """Bytes of weights read for one token.
 
     Every layer projection (Q, K, V, O), the FFN (MoE: the router plus the
     top_k selected experts), the LM head and one embedding row. RMSNorm gains
-    are folded into the following projections, so they are not read.
+    are folded into the following projections, so they are not read. fp16
+    weights take 2 bytes each; fp8 weights 1 byte each plus one fp32 scale per
+    row (the embedding row stays fp16).
     """
     d, q, kv, f = cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim
     attn = q * d + 2 * kv * d + d * q
@@ -27,6 +29,9 @@ def active_weight_bytes(cfg) -> int:
         ffn = cfg.n_experts * d + cfg.top_k * 3 * f * d
     else:
         ffn = 3 * f * d
+    if getattr(cfg, "weight_format", "fp16") == "fp8":
+        rows = cfg.n_layers * (q + 2 * kv + d + 2 * f + d) + cfg.vocab
+        return cfg.n_layers * (attn + ffn) + cfg.vocab * d + 4 * rows + 2 * d
     params = cfg.n_layers * (attn + ffn) + cfg.vocab * d + d
     return 2 * params
 

@@ -9,11 +9,13 @@ itself: closed forms, invariants, brute force on tiny inputs and the numbers
 the pages print. No function here is left unpinned.
 """
 from .decoder import (Decoder, rmsnorm, rope_angles, apply_rope, softmax, attention_decode,
-                      silu, swiglu_ffn, topk_experts, greedy_argmax, gemv_f64)
+                      silu, swiglu_ffn, topk_experts, greedy_argmax, gemv_f64, E4M3_MAX,
+                      e4m3_decode_table, e4m3_encode, quantize_rows_e4m3, dequantize_rows_e4m3)
 from .compare import zscore_error, top2_gap, compare_logits
 
 __all__ = [
     "Decoder", "rmsnorm", "rope_angles", "apply_rope", "softmax", "attention_decode",
-    "silu", "swiglu_ffn", "topk_experts", "greedy_argmax", "gemv_f64",
+    "silu", "swiglu_ffn", "topk_experts", "greedy_argmax", "gemv_f64", "E4M3_MAX",
+    "e4m3_decode_table", "e4m3_encode", "quantize_rows_e4m3", "dequantize_rows_e4m3",
     "zscore_error", "top2_gap", "compare_logits",
 ]

@@ -135,6 +135,80 @@ def gemv_f64(A: np.ndarray, x: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP8 weights. The pages name FP8/FP4 quantisation as the way to fewer bytes
+# per token (agentlenshq.com article, "Scaling to frontier MoE models") without
+# fixing a format; the one used here is the OCP 8-bit float E4M3 with one
+# scale per weight row, the scale mapping the row's largest magnitude to
+# E4M3's largest finite value.
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """float64 value of each of the 256 E4M3 codes, from the format's
+    definition: sign bit, 4 exponent bits e (bias 7), 3 mantissa bits m;
+    e = 0 is subnormal, m/8 * 2^-6; otherwise (1 + m/8) * 2^(e-7); e = 15 with
+    m = 7 is NaN (no infinities)."""
+    codes = np.arange(256)
+    e = (codes >> 3) & 15
+    m = (codes & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(codes & 0x80, -mag, mag)
+
+
+def _e4m3_encode_block(v: np.ndarray, table: np.ndarray) -> np.ndarray:
+    a = np.minimum(np.abs(v), table.dtype.type(E4M3_MAX))
+    hi = np.clip(np.searchsorted(table, a, side="left"), 1, 0x7e)   # first table value >= a
+    lo = hi - 1
+    # exact differences: a lies between two neighbouring table values
+    dlo, dhi = a - table[lo], table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == 0, 0, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    code = np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(v), np.uint8(0x7f), code).astype(np.uint8)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """The E4M3 code nearest to each value (ties to the even code), saturating
+    at +-448; NaN maps to 0x7f. Found among the sorted table of the 127
+    non-negative finite codes, not by arithmetic on exponent and mantissa.
+    float32 input is encoded in float32 (every table value and every
+    difference to a neighbouring table value is exact there), in blocks."""
+    v = np.asarray(v)
+    if v.dtype != np.float32:
+        v = v.astype(np.float64)
+    table = e4m3_decode_table()[:0x7f].astype(v.dtype)   # codes 0x00..0x7e, increasing
+    flat = v.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 18
+    for i in range(0, flat.size, step):
+        out[i:i + step] = _e4m3_encode_block(flat[i:i + step], table)
+    return out.reshape(v.shape)
+
+
+def quantize_rows_e4m3(W: np.ndarray, gain: Optional[np.ndarray] = None):
+    """Row-wise E4M3 quantisation of fp16 weights W [rows][K], each column k
+    first multiplied by gain[k] (an RMSNorm gain folded into the matrix).
+    In float32, as specified: v = w * g (exact for fp16 operands),
+    s = max|v| / 448 per row (1 for an all-zero row), q = E4M3(v / s).
+    Returns (q uint8 [rows][K], s float32 [rows])."""
+    v = np.asarray(W, dtype=np.float16).astype(np.float32)
+    if gain is not None:
+        v = v * np.asarray(gain, dtype=np.float16).astype(np.float32)[None, :]
+    amax = np.max(np.abs(v), axis=1)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = e4m3_encode((v / s[:, None]).astype(np.float32))
+    return q, s
+
+
+def dequantize_rows_e4m3(q: np.ndarray, s: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """q [rows][K] codes and s [rows] scales -> the weights they stand for."""
+    return (e4m3_decode_table()[q] * np.asarray(s, dtype=np.float64)[:, None]).astype(dtype)
+
+
+# --------------------------------------------------------------------------
 # The decoder.
 # --------------------------------------------------------------------------
 
@@ -157,6 +231,10 @@ class Decoder:
                  cache_experts: bool = False, kv_dtype=np.float16):
         self.cfg = cfg
         self.dtype = np.dtype(dtype)
+        # fp8 weights: every projection is the row-wise E4M3 quantisation of
+        # the matrix with its preceding RMSNorm gain folded in, and the norms
+        # themselves then carry no gain (the embedding stays fp16)
+        self.fp8 = getattr(cfg, "weight_format", "fp16") == "fp8"
         # The KV cache holds fp16 keys and values: each k, v is rounded to
         # fp16 when it is stored and read back exactly. kv_dtype=None keeps
         # the compute precision instead.
@@ -165,6 +243,14 @@ class Decoder:
         self._cache_experts = cache_experts
         self._conv: Dict[int, np.ndarray] = {}
         self._index = self._build_index()
+        if self.fp8:
+            # quantise every projection once, matrices in parallel (the
+            # element-wise work releases the interpreter lock)
+            from concurrent.futures import ThreadPoolExecutor
+            import os
+            names = [n for n in self._index if n != "E" and not n.split(".")[-1].startswith("g_")]
+            with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+                list(ex.map(self.w, names))
         L, S, Hkv, hd = cfg.n_layers, cfg.max_seq, cfg.n_kv_heads, cfg.head_dim
         self.K = np.zeros((L, S, Hkv, hd), dtype=self.kv_dtype)
         self.V = np.zeros((L, S, Hkv, hd), dtype=self.kv_dtype)
@@ -185,12 +271,28 @@ class Decoder:
                 raise ValueError(f"{name}: shape {t.shape} != {shape}")
         return {name: i for i, (name, _, _) in enumerate(specs)}
 
+    # the RMSNorm gain folded into each projection of an fp8 model
+    _FOLD = {"Wq": "g_attn", "Wk": "g_attn", "Wv": "g_attn", "Wg": "g_ffn", "Wu": "g_ffn", "Wo": None,
+             "Wd": None}
+
     def w(self, name: str) -> np.ndarray:
         i = self._index[name]
         hit = self._conv.get(i)
         if hit is not None:
             return hit
-        a = self._raw[i].astype(self.dtype)
+        if self.fp8 and name.split(".")[-1].startswith("g_"):   # gains live in the fp8 matrices
+            a = np.ones(self._raw[i].shape, dtype=self.dtype)
+        elif self.fp8 and name != "E":
+            if name == "W_lm":
+                g = self._raw[self._index["g_final"]]
+            else:
+                layer, mat = name.split(".")[0], name.split(".")[-1]
+                gname = self._FOLD[mat]
+                g = None if gname is None else self._raw[self._index[f"{layer}.{gname}"]]
+            q, s = quantize_rows_e4m3(self._raw[i], g)
+            a = dequantize_rows_e4m3(q, s, self.dtype)
+        else:
+            a = self._raw[i].astype(self.dtype)
         if self._cache_experts or ".e" not in name:
             self._conv[i] = a
         return a

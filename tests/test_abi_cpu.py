@@ -170,3 +170,48 @@ def test_binding_rejects_bad_kv_and_tokens():
         with pytest.raises(kie.KieError) as e:
             kie.check_tokens(t, n, "force")
         assert e.value.code == -1
+
+
+# ---- fp8 weights ------------------------------------------------------------
+def test_host_fp8_quantizer_matches_oracle(lib):
+    """The library's E4M3 quantizer (what kie_load applies) against the
+    oracle's, bit for bit: codes and scales, with and without a folded gain,
+    an all-zero row, and values exactly halfway between codes."""
+    import oracle
+    rng = np.random.default_rng(30)
+    W = (rng.standard_normal((40, 2560)) * 0.02).astype(np.float16)
+    W[3] = 0
+    W[4, :] = 0
+    W[4, 0] = np.float16(448.0)                  # scale exactly 1: the rest encode as given
+    t = oracle.e4m3_decode_table()
+    mids = ((t[1:0x7e] + t[2:0x7f]) / 2).astype(np.float16)
+    mids = mids[mids.astype(np.float64) == (t[1:0x7e] + t[2:0x7f]) / 2][:200]   # exact in fp16
+    W[4, 1:1 + len(mids)] = mids
+    W[5, :len(mids)] = -mids
+    W[5, -1] = np.float16(-448.0)
+    g = (1 + rng.standard_normal(2560) * 0.3).astype(np.float16)
+    for gain in (None, g):
+        q, s = kie.quantize_e4m3_rows(W, gain)
+        qo, so = oracle.quantize_rows_e4m3(W, gain)
+        assert np.array_equal(s.view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(q, qo)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(weight_format=2), dict(weight_format=1, n_experts=4, top_k=2, d_model=512, ffn_dim=512),
+    dict(weight_format=1, head_dim=64, d_model=512, n_heads=8, n_kv_heads=4, ffn_dim=512, vocab=1000),
+    dict(weight_format=1, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4, head_dim=128, vocab=1001),
+    dict(weight_format=1),                       # the tiny decoder: d_model 256
+])
+def test_fp8_configs_rejected(lib, bad):
+    kc = kie.make_config(synth.get_config("tiny"))
+    for k, v in bad.items():
+        setattr(kc, k, v)
+    assert lib.kie_workspace_bytes(ctypes.byref(kc)) == 0
+    assert lib.kie_last_error(None).decode()
+
+
+def test_fp8_workspace_is_about_half(lib):
+    a = kie.workspace_bytes(synth.get_config("2b"))
+    b = kie.workspace_bytes(synth.get_config("2b_fp8"))
+    assert 0.5 < b / a < 0.62          # weights halve; embedding, KV cache and buffers stay

@@ -58,6 +58,16 @@ CASES = {
     "gqa4_long_hd128": synth.DecoderConfig(name="gqa4_long_hd128", n_layers=2, d_model=512, n_heads=4,
                                            n_kv_heads=1, head_dim=128, ffn_dim=1024, vocab=2048,
                                            prompt_len=1136, decode_steps=32),
+    # fp8 (E4M3, one scale per row) weights with non-unit RMSNorm gains folded
+    # in before quantising; rows of 512 and 1024 (the per-unit input path)
+    "fp8_d512_gains": synth.DecoderConfig(name="fp8_d512_gains", n_layers=2, d_model=512, n_heads=4,
+                                          n_kv_heads=2, head_dim=128, ffn_dim=1024, vocab=2000, prompt_len=12,
+                                          decode_steps=16, gain_sigma=0.2, weight_format="fp8"),
+    # fp8 with rows of 2048 (inputs held in registers), a 1536-wide FFN and a
+    # ragged LM split (1501 row pairs over 256 workgroups)
+    "fp8_d2048": synth.DecoderConfig(name="fp8_d2048", n_layers=2, d_model=2048, n_heads=16, n_kv_heads=4,
+                                     head_dim=128, ffn_dim=1536, vocab=3002, prompt_len=40, decode_steps=12,
+                                     weight_format="fp8"),
 }
 
 

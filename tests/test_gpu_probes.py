@@ -84,6 +84,19 @@ def test_gemv_probe_full_shapes_sampled(torch_cuda, si):
     assert ms > 0
 
 
+def test_e4m3_device_conversion_table(torch_cuda):
+    """The device's fp8 conversion (what the fp8 GEMVs use) gives every E4M3
+    code exactly the oracle's value from the format's definition (NaN codes
+    NaN): the device reads OCP E4M3, bias 7."""
+    from memory_bandwidth_bound_amd import kie
+    dev = kie.e4m3_table_probe().astype(np.float64)
+    ref = oracle.e4m3_decode_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(dev), nan)
+    assert np.array_equal(dev[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(dev[~nan]), np.signbit(ref[~nan]))
+
+
 def test_xcd_map(torch_cuda):
     """Every workgroup of the 256-workgroup grid reports an XCD id; the ids
     are 0..7 on MI355X, 32 workgroups each."""

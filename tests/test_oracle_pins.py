@@ -517,3 +517,108 @@ def test_compare_non_finite_device_rows_fail(bad_value):
     assert worst == float("inf")
     # a shape mismatch is no pass either
     assert oracle.compare_logits(ref[:, :4], ref)[0] == float("inf")
+
+
+# ---------------------------------------------------------------- fp8 -------
+
+def test_e4m3_table_closed_form_points():
+    """E4M3 (OCP): largest finite 448 = 1.75 * 2^8, smallest normal 2^-6,
+    smallest subnormal 2^-9, 1.0 at exponent field 7, no infinities, NaN at
+    0x7f / 0xff, a sign bit."""
+    t = oracle.e4m3_decode_table()
+    assert t[0x7e] == 448.0 and t[0xfe] == -448.0
+    assert t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9
+    assert t[0x38] == 1.0 and t[0x39] == 1.125 and t[0x40] == 2.0 and t[0xb8] == -1.0
+    assert np.isnan(t[0x7f]) and np.isnan(t[0xff]) and np.isfinite(t[np.r_[0:0x7f, 0x80:0xff]]).all()
+    assert t[0] == 0.0 and np.signbit(t[0x80])
+    pos = t[:0x7f]
+    assert np.all(np.diff(pos) > 0)                         # codes increase with value
+    assert np.array_equal(t[0x80:0xff], -pos)
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    t = oracle.e4m3_decode_table()
+    finite = np.array([c for c in range(256) if np.isfinite(t[c])])
+    assert np.array_equal(oracle.e4m3_encode(t[finite]), finite.astype(np.uint8))
+    pos = t[:0x7f]
+    mid = (pos[:-1] + pos[1:]) / 2                          # ties: to the even code
+    want = np.where(np.arange(1, 0x7f) % 2 == 0, np.arange(1, 0x7f), np.arange(0, 0x7e))
+    assert np.array_equal(oracle.e4m3_encode(mid), want.astype(np.uint8))
+    eps = np.diff(pos) * 1e-3
+    assert np.array_equal(oracle.e4m3_encode(mid - eps), np.arange(0, 0x7e).astype(np.uint8))
+    assert np.array_equal(oracle.e4m3_encode(mid + eps), np.arange(1, 0x7f).astype(np.uint8))
+    assert oracle.e4m3_encode(np.array([500.0, -1e9, 448.5]))[:2].tolist() == [0x7e, 0xfe]
+    v = np.sort(np.random.default_rng(20).standard_normal(5000) * 100)
+    assert np.all(np.diff(t[oracle.e4m3_encode(v)]) >= 0)   # monotone
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """A library routine: torch's float32 -> float8_e4m3fn cast (nearest, ties
+    to even) on values within the finite range."""
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    rng = np.random.default_rng(21)
+    v = np.concatenate([rng.standard_normal(50000) * 60, rng.standard_normal(50000) * 1e-2,
+                        rng.uniform(-448, 448, 20000)]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(v), want)
+
+
+def test_quantize_rows_e4m3_properties():
+    rng = np.random.default_rng(22)
+    W = (rng.standard_normal((6, 1024)) * 0.02).astype(np.float16)
+    W[1] = 0                                                 # an all-zero row: scale 1, codes 0
+    W[2] = 0
+    W[2, 7] = np.float16(-0.5)                               # one non-zero: it is -448 * s
+    g = (1 + rng.standard_normal(1024) * 0.2).astype(np.float16)
+    q, s = oracle.quantize_rows_e4m3(W, g)
+    assert s.dtype == np.float32 and q.dtype == np.uint8
+    assert s[1] == 1.0 and not q[1].any()
+    assert q[2, 7] == 0xfe and (q[2, :7] == 0).all()
+    v = W.astype(np.float32) * g.astype(np.float32)
+    for r in (0, 3, 4, 5):
+        k = int(np.argmax(np.abs(v[r])))
+        assert q[r, k] & 0x7f == 0x7e                       # the row's largest magnitude maps to 448
+        assert s[r] == np.float32(np.abs(v[r]).max() / np.float32(448.0))
+    # dequantised within half a code spacing of the exact value (the wider of
+    # the two spacings next to the chosen code: 2^-4 relative for normals)
+    deq = oracle.dequantize_rows_e4m3(q, s)
+    t = oracle.e4m3_decode_table()
+    c = (q & 0x7f).astype(np.int64)
+    up = t[np.minimum(c, 0x7d) + 1] - t[np.minimum(c, 0x7d)]
+    down = t[np.maximum(c, 1)] - t[np.maximum(c, 1) - 1]
+    step = np.maximum(up, down) * s[:, None]
+    assert np.all(np.abs(deq - v) <= step / 2 * (1 + 1e-6))
+    assert np.abs(deq - v).max() > 0                        # it is a quantisation
+
+
+def test_fp8_decoder_is_the_model_on_dequantised_weights():
+    """An fp8 decoder equals the written-out definition with every projection
+    replaced by its row-wise E4M3 quantisation (gain of the preceding RMSNorm
+    folded in; norms without gain)."""
+    cfg = _tiny(d_model=16, weight_format="fp8")
+    W = make_weights(cfg)
+    names = [n for n, _, _ in tensor_specs(cfg)]
+    T = dict(zip(names, W))
+    deq = []
+    for n, t in zip(names, W):
+        if n.split(".")[-1].startswith("g_"):
+            deq.append(np.ones(t.shape))
+        elif n == "E":
+            deq.append(t.astype(np.float64))
+        else:
+            mat = n.split(".")[-1]
+            g = {"Wq": "g_attn", "Wk": "g_attn", "Wv": "g_attn", "Wg": "g_ffn", "Wu": "g_ffn"}.get(mat)
+            if n == "W_lm":
+                g = T["g_final"]
+            elif g is not None:
+                g = T[n.split(".")[0] + "." + g]
+            deq.append(oracle.dequantize_rows_e4m3(*oracle.quantize_rows_e4m3(t, g)))
+    toks = [3, 17, 0, 22, 9]
+    dec = oracle.Decoder(cfg, W, dtype=np.float64)
+    got = np.stack([dec.step(t) for t in toks])
+    np.testing.assert_allclose(got, _brute_logits(cfg, deq, toks), rtol=1e-10, atol=1e-12)
+    # and it is not the fp16 model
+    plain = oracle.Decoder(cfg.with_(weight_format="fp16"), W, dtype=np.float64)
+    assert not np.allclose(got, np.stack([plain.step(t) for t in toks]))
