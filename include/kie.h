@@ -16,8 +16,8 @@
  *    No exception crosses the ABI. kie_last_error() gives a message.
  *  - Host pointers are plain CPU memory owned by the caller. Device pointers
  *    are device memory owned by the caller (for example a torch tensor); the
- *    library never allocates or frees device memory (kie_load takes one
- *    64-byte word of pinned host memory for the watchdog, see kie_set_limits).
+ *    library never allocates or frees device memory (kie_load takes 64 bytes
+ *    of pinned host memory for the kernel's status word, see kie_set_limits).
  *  - All device work is enqueued on the HIP stream given to kie_load (NULL =
  *    the default stream). Calls that return data to host buffers synchronise
  *    that stream before returning.
@@ -241,9 +241,10 @@ float kie_last_kernel_ms(const kie_model* m);
  * workgroup's waits give up too and the kernel exits; the call returns
  * KIE_ERR_TIMEOUT. watchdog_ms: the host's wall-clock limit per launch
  * (0 = automatic: 10 s plus 20 ms per pass; < 0 = none). The host polls the
- * launch's completion; past the limit it raises a word in pinned host memory
- * (allocated by kie_load, 64 bytes) that the kernel's waits read once they
- * have polled in vain, lets the launch end and returns KIE_ERR_TIMEOUT. A
+ * launch's completion; past the limit it sets the kernel's status word (in
+ * pinned host memory allocated by kie_load, 64 bytes), which the kernel's
+ * waits read once they have polled in vain, lets the launch end and returns
+ * KIE_ERR_TIMEOUT. A
  * launch still making progress is not cut short; its overrun is reported the
  * same way. Applies to later kie_prefill / kie_decode calls. KIE_ERR_ARG for a
  * null model.

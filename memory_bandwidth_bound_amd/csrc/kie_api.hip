@@ -28,11 +28,12 @@ struct kie_model {
     float last_ms;
     uint32_t spin_limit;    // polls before a device-side wait gives up
     int32_t watchdog_ms;    // host limit per launch: 0 automatic, < 0 none
-    uint32_t* habort;       // pinned host word the kernel's long waits read
+    uint32_t* hstatus;      // pinned host word: the kernel's status (the host's watchdog writes it too)
     std::string err;
 };
 
 constexpr uint32_t kDefaultSpin = 1u << 22;
+constexpr uint32_t kStatusHostAbort = 2;   // written by the host's watchdog (kernel timeouts write 1)
 
 // Wall-clock limit of one launch of n passes: the automatic limit allows
 // 10 s plus 20 ms per pass (a pass takes about 1.3 ms on the ~2.1B decoder).
@@ -162,7 +163,7 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     m->ev0 = m->ev1 = nullptr;
     m->spin_limit = kDefaultSpin;
     m->watchdog_ms = 0;
-    m->habort = nullptr;
+    m->hstatus = nullptr;
     if (ws_bytes < m->lay.total) {
         rc = fail(nullptr, KIE_ERR_WORKSPACE, "workspace smaller than kie_workspace_bytes()");
         delete m;
@@ -224,14 +225,14 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     if ((rc = clear_state(m, true)) != KIE_OK) return bail(rc);
     hipError_t e = hipEventCreate(&m->ev0);
     if (e == hipSuccess) e = hipEventCreate(&m->ev1);
-    if (e == hipSuccess) e = hipHostMalloc((void**)&m->habort, 64, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&m->hstatus, 64, hipHostMallocDefault);
     if (e != hipSuccess) {
         hip_fail(m, e, "hipEventCreate / hipHostMalloc");
         if (m->ev0) (void)hipEventDestroy(m->ev0);
         if (m->ev1) (void)hipEventDestroy(m->ev1);
         return bail(KIE_ERR_HIP);
     }
-    __atomic_store_n(m->habort, 0u, __ATOMIC_SEQ_CST);
+    __atomic_store_n(m->hstatus, 0u, __ATOMIC_SEQ_CST);
     *out = m;
     return KIE_OK;
 }
@@ -254,7 +255,6 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
             int rc = clear_state(m, false);
             if (rc != KIE_OK) return rc;
         }
-        HIP_TRY(m, hipMemsetAsync(m->ws + L.off_status, 0, 256, m->stream));
         if (force)
             HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_force, force + s0, (size_t)nc * 4, hipMemcpyHostToDevice,
                                       m->stream));
@@ -280,8 +280,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.ex.h = (uint64_t*)(m->ws + L.off_ex_h);
         a.ex.r = (uint64_t*)(m->ws + L.off_ex_r);
         a.ex.am = (uint64_t*)(m->ws + L.off_ex_am);
-        a.status = (uint32_t*)(m->ws + L.off_status);
-        a.habort = m->habort;
+        a.status = m->hstatus;
         a.out_ids = (int32_t*)(m->ws + L.off_out);
         a.force_ids = (const int32_t*)(m->ws + L.off_force);
         a.dbg_logits = (float*)(m->ws + L.off_dbg_logits);
@@ -302,13 +301,13 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         static_assert(sizeof(DecodeArgs) <= 4096, "argument block");
         static_assert(KIE_TRACE_PHASES == kTracePhases, "trace length");
         HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
-        __atomic_store_n(m->habort, 0u, __ATOMIC_SEQ_CST);
+        __atomic_store_n(m->hstatus, 0u, __ATOMIC_SEQ_CST);   // the previous launch has ended
         HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
         HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w8 != 0, skip_lm, kGrid,
                                  m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
         // Host watchdog: poll the launch's end event against a wall-clock
-        // limit. Past it, raise the host word the kernel's long waits read
+        // limit. Past it, set the status word the kernel's long waits read
         // (workgroups that wait on each other then give up and exit), let the
         // launch end and report KIE_ERR_TIMEOUT. A kernel that still makes
         // progress runs to its end; the overrun is reported all the same.
@@ -321,15 +320,14 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
             if (q != hipErrorNotReady) return hip_fail(m, q, "hipEventQuery");
             const double el = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
             if (!fired && limit >= 0.0 && el > limit) {
-                __atomic_store_n(m->habort, 1u, __ATOMIC_SEQ_CST);
+                __atomic_store_n(m->hstatus, kStatusHostAbort, __ATOMIC_SEQ_CST);
                 fired = true;
             }
             if (el < 5.0) std::this_thread::yield();   // short launches: no sleep granularity
             else std::this_thread::sleep_for(std::chrono::microseconds(20));
         }
         HIP_TRY(m, hipEventElapsedTime(&m->last_ms, m->ev0, m->ev1));
-        uint32_t status = 0;
-        HIP_TRY(m, hipMemcpy(&status, m->ws + L.off_status, 4, hipMemcpyDeviceToHost));
+        const uint32_t status = __atomic_load_n(m->hstatus, __ATOMIC_SEQ_CST);
         if (fired) {
             m->pending = -1;
             return fail(m, KIE_ERR_TIMEOUT, "the launch exceeded the host watchdog's wall-clock limit");
@@ -475,7 +473,7 @@ void kie_free(kie_model* m) {
     if (!m) return;
     if (m->ev0) (void)hipEventDestroy(m->ev0);
     if (m->ev1) (void)hipEventDestroy(m->ev1);
-    if (m->habort) (void)hipHostFree(m->habort);
+    if (m->hstatus) (void)hipHostFree(m->hstatus);
     delete m;
 }
 

@@ -268,7 +268,7 @@ __device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S
     const uint64_t* src = kind == K_WO ? a.ex.o : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
     const int i0 = n * w / kWaves, i1 = n * (w + 1) / kWaves;
     float ss = 0.f;
-    const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, a.habort, [&](int i, uint32_t v) {
+    const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, [&](int i, uint32_t v) {
         const float x = __builtin_bit_cast(float, v);
         ss += x * x;
         stage1<W8>(S, i0 + i, x);
@@ -330,7 +330,7 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
                     const bool ok = fw_ok(w0, id) && fw_ok(w1, id) && fw_ok(w2, id) && fw_ok(w3, id);
                     if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
                     if (++spins > a.spin) return 1;
-                    if ((spins & 63) == 0 && stop_requested(a.status, a.habort)) return 2;
+                    if ((spins & 63) == 0 && stop_requested(a.status)) return 2;
 #if KIE_POLL_SLEEP > 0
                     __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
 #endif
@@ -387,7 +387,7 @@ struct Comm {
     // why: 1 = this wave's wait timed out, 2 = another workgroup reported one
     __device__ __forceinline__ void fail(int why) {
         if (!dead && lane == 0) {
-            if (why == 1) dev_store32(a.status, (uint32_t)kStatusTimeout);
+            if (why == 1) sys_store32(a.status, (uint32_t)kStatusTimeout);
             S->abort = 1u;
         }
         dead = true;
@@ -396,7 +396,7 @@ struct Comm {
     template <class F>
     __device__ __forceinline__ bool gather(const uint64_t* src, int n, uint32_t id, F f) {
         if (dead) return false;
-        const int r = fw_gather(src, n, id, a.spin, a.status, a.habort, f);
+        const int r = fw_gather(src, n, id, a.spin, a.status, f);
         if (r) fail(r);
         return r == 0;
     }
@@ -800,7 +800,7 @@ struct Comm {
                 fail(1);
                 return false;
             }
-            if ((spins & 63) == 0 && stop_requested(a.status, a.habort)) {
+            if ((spins & 63) == 0 && stop_requested(a.status)) {
                 fail(2);
                 return false;
             }
@@ -1128,7 +1128,7 @@ struct Compute {
                 const int n = __builtin_amdgcn_readfirstlane(S->geo[kind].gin);
                 const int r = gather_input<W8>(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1);
                 if (r && lane == 0) {
-                    if (r == 1) dev_store32(a.status, (uint32_t)kStatusTimeout);
+                    if (r == 1) sys_store32(a.status, (uint32_t)kStatusTimeout);
                     S->abort = 1u;
                 }
             }

@@ -205,6 +205,10 @@ __device__ __forceinline__ void dev_store64(void* p, uint64_t v) {
 __device__ __forceinline__ void dev_store32(void* p, uint32_t v) {
     __hip_atomic_store(gptr((uint32_t*)p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// System-scope store (the decode kernel's status word in pinned host memory).
+__device__ __forceinline__ void sys_store32(void* p, uint32_t v) {
+    __hip_atomic_store(gptr((uint32_t*)p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 __device__ __forceinline__ uint64_t dev_load64(const void* p) {
     return __hip_atomic_load(gptr((uint64_t*)const_cast<void*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -251,14 +255,12 @@ __device__ __forceinline__ void dev_load128x8_sync(const void* k0, const void* k
         : "memory");
 }
 
-// Should a waiting wave give up? *status is set by a workgroup that timed out;
-// *habort (host memory, may be null) by the host's watchdog. Read only by
-// waits that have already polled in vain many times, so the host round trip
-// is off every normal path.
-__device__ __forceinline__ bool stop_requested(const uint32_t* status, const uint32_t* habort) {
-    if (dev_load32(status) != 0) return true;
-    return habort &&
-           __hip_atomic_load(gptr(const_cast<uint32_t*>(habort)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0;
+// Should a waiting wave give up? *status is set non-zero by a workgroup that
+// timed out or by the host's watchdog (the decode kernel's status word lives
+// in pinned host memory). Read only by waits that have already polled in vain
+// many times, so its trip is off every normal path.
+__device__ __forceinline__ bool stop_requested(const uint32_t* status) {
+    return __hip_atomic_load(gptr(const_cast<uint32_t*>(status)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0;
 }
 
 // Wait until words [0, n) of src all carry `id`, then call f(i, payload) for
@@ -284,8 +286,7 @@ constexpr int kGatherRegs = 16;     // words per lane per block (at most)
 
 template <int R, class F>
 __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
-                                               const uint32_t* status, const uint32_t* habort, uint32_t& spins,
-                                               F& f) {
+                                               const uint32_t* status, uint32_t& spins, F& f) {
     const int lane = lane_id();
     const uint64_t* p[R];
 #pragma unroll
@@ -302,7 +303,7 @@ __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint3
         for (int c = 0; c < R; ++c) ok = fw_ok(x[c], id) && ok;
         if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
         if (++spins > spin_limit) return 1;
-        if ((spins & 63) == 0 && stop_requested(status, habort)) return 2;
+        if ((spins & 63) == 0 && stop_requested(status)) return 2;
 #if KIE_POLL_SLEEP > 0
         __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
 #endif
@@ -317,17 +318,17 @@ __device__ __forceinline__ int fw_gather_block(const uint64_t* src, int n, uint3
 
 template <class F>
 __device__ __forceinline__ int fw_gather(const uint64_t* src, int n, uint32_t id, uint32_t spin_limit,
-                                         const uint32_t* status, const uint32_t* habort, F f) {
+                                         const uint32_t* status, F f) {
     uint32_t spins = 0;
     for (int base = 0; base < n; base += 64 * kGatherRegs) {
         const int m = (n - base < 64 * kGatherRegs) ? n - base : 64 * kGatherRegs;
         const int per = (m + 63) / 64;
         auto g = [&](int i, uint32_t v) { f(base + i, v); };
         int r;
-        if (per <= 2) r = fw_gather_block<2>(src + base, m, id, spin_limit, status, habort, spins, g);
-        else if (per <= 4) r = fw_gather_block<4>(src + base, m, id, spin_limit, status, habort, spins, g);
-        else if (per <= 8) r = fw_gather_block<8>(src + base, m, id, spin_limit, status, habort, spins, g);
-        else r = fw_gather_block<16>(src + base, m, id, spin_limit, status, habort, spins, g);
+        if (per <= 2) r = fw_gather_block<2>(src + base, m, id, spin_limit, status, spins, g);
+        else if (per <= 4) r = fw_gather_block<4>(src + base, m, id, spin_limit, status, spins, g);
+        else if (per <= 8) r = fw_gather_block<8>(src + base, m, id, spin_limit, status, spins, g);
+        else r = fw_gather_block<16>(src + base, m, id, spin_limit, status, spins, g);
         if (r) return r;
     }
     return 0;

@@ -64,8 +64,7 @@ struct DecodeArgs {
     uint16_t* kc;            // [L][Hkv][max_seq][hd]
     uint16_t* vc;
     Exchange ex;
-    uint32_t* status;
-    const uint32_t* habort;  // host memory: non-zero once the host's watchdog fired (may be null)
+    uint32_t* status;        // pinned host memory: 0, kStatusTimeout from a workgroup, or set by the host's watchdog
     int32_t* out_ids;
     const int32_t* force_ids;
     float* dbg_logits;

@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint6
         if (lane == 0) fw_store(map + wg, (uint32_t)xcd, 1u);
         int mem = 0, lead = nwg;
         uint32_t mask = 0;
-        const int e = fw_gather(map, nwg, 1u, 1u << 22, status, nullptr, [&](int i, uint32_t v) {
+        const int e = fw_gather(map, nwg, 1u, 1u << 22, status, [&](int i, uint32_t v) {
             mask |= 1u << (v & 15);
             if ((int)v == xcd) {
                 ++mem;
@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(64, 1) barrier_probe_kernel(int variant, uint6
         } else {
             uint64_t* buf = words + (size_t)(r & 1) * 5 * nwg;
             if (lane < 5) fw_store(buf + 5 * wg + lane, (uint32_t)((wg * 8 + lane) ^ r), (uint32_t)r);
-            const int e = fw_gather(buf, 5 * nwg, (uint32_t)r, 1u << 22, status, nullptr, [&](int i, uint32_t v) {
+            const int e = fw_gather(buf, 5 * nwg, (uint32_t)r, 1u << 22, status, [&](int i, uint32_t v) {
                 if (v != (uint32_t)(((i / 5) * 8 + i % 5) ^ r)) ++err;
             });
             if (e) {
