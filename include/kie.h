@@ -172,15 +172,27 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
              void* dev_workspace, size_t ws_bytes, void* hip_stream, kie_model** out);
 
 /*
- * Prefill: run one forward pass per prompt token at positions 0..n-1 (cache
- * entries at those positions are overwritten) and return the greedy first
- * generated token, which becomes the pending token. The passes run in one
- * kernel launch (launches of at most 64 passes when debug logits are
- * requested); the LM head runs on the last pass only. Not part of the decode
- * metric. dbg may be NULL; dbg->logits, if set, receives [n][vocab].
+ * Prefill: process the prompt's tokens at positions 0..n-1 (cache entries at
+ * those positions are overwritten) and return the greedy first generated
+ * token, which becomes the pending token. Not part of the decode metric
+ * (paper-digest.app digest, "Core Mechanics"). Two ways, one result (up to
+ * rounding order):
+ *  - batched (dense fp16 models, the default): the prompt's projections as
+ *    GEMMs on the matrix cores in chunks of 256 tokens, with causal attention
+ *    over the cache, norms, RoPE, SwiGLU and residuals as row kernels;
+ *  - passes (other models, kie_set_prefill_mode(m, KIE_PREFILL_PASSES), or
+ *    when dbg->trace is set): one decode pass per token in one persistent
+ *    launch (launches of at most 64 passes when debug logits are requested),
+ *    the LM head on the last pass only.
+ * dbg may be NULL; dbg->logits, if set, receives [n][vocab].
  */
 int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_token,
                 const kie_debug* dbg);
+
+enum { KIE_PREFILL_AUTO = 0, KIE_PREFILL_PASSES = 1 };
+/* Choose how later kie_prefill calls run (see kie_prefill). KIE_ERR_ARG for
+ * an unknown mode or a null model. */
+int kie_set_prefill_mode(kie_model* m, int32_t mode);
 
 /*
  * Store already-rotated keys and values for positions 0..n_pos-1 directly in
@@ -321,6 +333,17 @@ int kie_barrier_probe(void* scratch, int32_t variant, int32_t rounds, void* hip_
  */
 int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream, float* us_per_round,
                               int32_t* errors);
+
+/*
+ * Matrix-core GEMM probe (the kernel of the batched prefill): Y[p][m] =
+ * sum_k A[p][k] W[m][k] for p < n, m < M, with A fp32 [n][K], W fp16 [M][K]
+ * and Y fp32 [n][M], all row-major device memory owned by the caller; A is
+ * taken as two fp16 terms (about 22 significant bits), products accumulated
+ * in fp32 on v_mfma_f32_32x32x8_f16. K a multiple of 32. *ms_out (may be
+ * NULL) receives the device time. Waits for the launch.
+ */
+int kie_gemm_probe(const float* A, const void* W, float* Y, int32_t n, int32_t M, int32_t K, void* hip_stream,
+                   float* ms_out);
 
 /* FP8 conversion probe: out256 (host) receives the fp32 value the device's
  * E4M3 conversion (the one the fp8 GEMVs use) gives each code 0..255. Uses the

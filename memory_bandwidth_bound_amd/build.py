@@ -51,7 +51,7 @@ def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BU
         raise RuntimeError("hipcc not found")
     os.makedirs(build_dir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    units = ["kie_decode", "kie_probes", "kie_api"]
+    units = ["kie_decode", "kie_prefill", "kie_probes", "kie_api"]
     dflags = ["-D" + d for d in defines]
     jobs = [[GXX, *CXX_FLAGS, *dflags, *inc, "-c", os.path.join(CSRC, "kie_host.cpp"), "-o",
              os.path.join(build_dir, "kie_host.o")]]

@@ -29,6 +29,7 @@ struct kie_model {
     uint32_t spin_limit;    // polls before a device-side wait gives up
     int32_t watchdog_ms;    // host limit per launch: 0 automatic, < 0 none
     uint32_t* hstatus;      // pinned host word: the kernel's status (the host's watchdog writes it too)
+    int32_t prefill_mode;   // KIE_PREFILL_AUTO or KIE_PREFILL_PASSES
     std::string err;
 };
 
@@ -164,6 +165,7 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     m->spin_limit = kDefaultSpin;
     m->watchdog_ms = 0;
     m->hstatus = nullptr;
+    m->prefill_mode = KIE_PREFILL_AUTO;
     if (ws_bytes < m->lay.total) {
         rc = fail(nullptr, KIE_ERR_WORKSPACE, "workspace smaller than kie_workspace_bytes()");
         delete m;
@@ -220,6 +222,20 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
         plan[kGrid + 1 + w] = L.lm_off[w];
     }
     if ((rc = upload(m, L.off_plan, plan.data(), plan.size() * 4)) != KIE_OK) return bail(rc);
+    if (batched_prefill_ok(D)) {
+        // where each workgroup's rows of QKV, Wo, gate/up and down start in a
+        // layer block, and its LM rows in the LM block (units)
+        std::vector<int32_t> slab(5 * kGrid);
+        for (int w = 0; w < kGrid; ++w) {
+            int off = L.piece_off[w];
+            for (int i = 0; i < layer_block_phase_count(D); ++i) {
+                slab[i * kGrid + w] = off;
+                off += phase_units(D, layer_block_phase(D, i), kGrid, w);
+            }
+            slab[4 * kGrid + w] = L.lm_off[w];
+        }
+        if ((rc = upload(m, L.off_pf_slab, slab.data(), slab.size() * 4)) != KIE_OK) return bail(rc);
+    }
     static_assert(kIdleBytes <= 16384, "idle region");
     if (hipMemsetAsync(m->ws + L.off_idle, 0, 16384, m->stream) != hipSuccess) return bail(KIE_ERR_HIP);
     if ((rc = clear_state(m, true)) != KIE_OK) return bail(rc);
@@ -358,6 +374,95 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
     return KIE_OK;
 }
 
+// The prompt as batched GEMMs on the matrix cores (kie_prefill.hip), in chunks
+// of kPrefillRows tokens: per layer RMSNorm, QKV GEMM, RoPE and KV append,
+// causal attention over the cache, Wo GEMM + residual, RMSNorm, gate/up GEMM,
+// SwiGLU, down GEMM + residual; then the final norm, the LM head GEMM (every
+// row when logits are asked for, else the chunk that holds the last token)
+// and the argmax of the last row. Many small launches on the model's stream:
+// prefill is not the decode metric.
+static int run_batched_prefill(kie_model* m, const int32_t* tokens, int n, int32_t* first, float* dbg_logits) {
+    const Layout& L = m->lay;
+    const Dims& D = L.D;
+    hipStream_t s = m->stream;
+    uint8_t* ws = m->ws;
+    const int32_t* slab = (const int32_t*)(ws + L.off_pf_slab);
+    const int qkvM = (D.H + 2 * D.Hkv) * D.hd, qd = D.H * D.hd;
+    PrefillRowArgs r;
+    memset(&r, 0, sizeof(r));
+    r.D = D;
+    r.eps = m->cfg.rms_eps;
+    r.emb = (const uint16_t*)(ws + L.off_emb);
+    r.tok = (const int32_t*)(ws + L.off_pf_tok);
+    r.X = (float*)(ws + L.off_pf_x);
+    r.A = (float*)(ws + L.off_pf_a);
+    r.Y = (const float*)(ws + L.off_pf_y);
+    r.Q = (float*)(ws + L.off_pf_q);
+    r.rope = (const float*)(ws + L.off_rope);
+    r.kc = (uint16_t*)(ws + L.off_k);
+    r.vc = (uint16_t*)(ws + L.off_v);
+    r.out = (int32_t*)(ws + L.off_pf_tok) + kPrefillRows;
+    float* Y = (float*)(ws + L.off_pf_y);
+    auto rows = [&](int op) -> hipError_t { return launch_prefill_rows(op, r, s); };
+    auto gemm = [&](const float* A, int lda, const uint8_t* base, const int32_t* sl, int M, int K, int gran) {
+        GemmRows R;
+        R.base = base;
+        R.slab = sl;
+        R.M = M;
+        R.K = K;
+        R.gran = gran;
+        R.dense = 0;
+        return launch_gemm_mfma(A, lda, r.n, R, Y, M, s);
+    };
+#define PF_TRY(call)                                         \
+    do {                                                     \
+        hipError_t e_ = (call);                              \
+        if (e_ != hipSuccess) return hip_fail(m, e_, #call); \
+    } while (0)
+    for (int c0 = 0; c0 < n; c0 += kPrefillRows) {
+        const int nc = (n - c0 < kPrefillRows) ? n - c0 : kPrefillRows;
+        const bool last = c0 + nc == n;
+        r.n = nc;
+        r.pos0 = c0;
+        PF_TRY(hipMemcpyAsync(ws + L.off_pf_tok, tokens + c0, (size_t)nc * 4, hipMemcpyHostToDevice, s));
+        PF_TRY(rows(PF_EMBED));
+        for (int l = 0; l < D.L; ++l) {
+            const uint8_t* blk = ws + L.off_layers + (size_t)l * L.layer_bytes;
+            r.layer = l;
+            PF_TRY(rows(PF_RMSNORM));
+            PF_TRY(gemm(r.A, D.d, blk, slab + 0 * kGrid, qkvM, D.d, 4));
+            r.ldy = qkvM;
+            PF_TRY(rows(PF_QKV));
+            PF_TRY(rows(PF_ATTN));
+            PF_TRY(gemm(r.A, qd, blk, slab + 1 * kGrid, D.d, qd, 2));
+            r.ldy = D.d;
+            PF_TRY(rows(PF_RESIDUAL));
+            PF_TRY(rows(PF_RMSNORM));
+            PF_TRY(gemm(r.A, D.d, blk, slab + 2 * kGrid, 2 * D.F, D.d, 4));
+            r.ldy = 2 * D.F;
+            PF_TRY(rows(PF_SWIGLU));
+            PF_TRY(gemm(r.A, D.F, blk, slab + 3 * kGrid, D.d, D.F, 2));
+            r.ldy = D.d;
+            PF_TRY(rows(PF_RESIDUAL));
+        }
+        if (!last && !dbg_logits) continue;
+        PF_TRY(rows(PF_RMSNORM));
+        PF_TRY(gemm(r.A, D.d, ws + L.off_lm, slab + 4 * kGrid, D.V, D.d, 1));
+        if (dbg_logits)
+            PF_TRY(hipMemcpyAsync(dbg_logits + (size_t)c0 * D.V, Y, (size_t)nc * D.V * 4, hipMemcpyDeviceToHost, s));
+        if (last) {
+            PrefillRowArgs am = r;
+            am.Y = Y + (size_t)(nc - 1) * D.V;
+            PF_TRY(launch_prefill_rows(PF_ARGMAX, am, s));
+            PF_TRY(hipMemcpyAsync(first, r.out, 4, hipMemcpyDeviceToHost, s));
+        }
+    }
+#undef PF_TRY
+    HIP_TRY(m, hipStreamSynchronize(s));
+    m->last_ms = 0.f;
+    return KIE_OK;
+}
+
 int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_token, const kie_debug* dbg) {
     if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
     if (!tokens || !first_token || n < 1) return fail(m, KIE_ERR_ARG, "need at least one prompt token");
@@ -366,6 +471,17 @@ int kie_prefill(kie_model* m, const int32_t* tokens, int32_t n, int32_t* first_t
         if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) return fail(m, KIE_ERR_ARG, "prompt token out of range");
     if (dbg && (dbg->experts || dbg->router) && m->cfg.n_experts == 0)
         return fail(m, KIE_ERR_ARG, "experts or router logits requested for a dense model");
+    if (m->prefill_mode == KIE_PREFILL_AUTO && batched_prefill_ok(m->lay.D) && !(dbg && dbg->trace)) {
+        m->pos = 0;
+        m->pending = -1;
+        int32_t first = 0;
+        int rc = run_batched_prefill(m, tokens, n, &first, dbg ? dbg->logits : nullptr);
+        if (rc != KIE_OK) return rc;
+        m->pos = n;
+        m->pending = first;
+        *first_token = first;
+        return KIE_OK;
+    }
     std::vector<int32_t> force(n);
     for (int i = 0; i + 1 < n; ++i) force[i] = tokens[i + 1];
     force[n - 1] = -1;
@@ -459,6 +575,40 @@ int kie_quantize_e4m3_rows(const void* w_fp16, const void* gain_fp16, int32_t ro
     const uint16_t* w = (const uint16_t*)w_fp16;
     for (int r = 0; r < rows; ++r)
         quantize_row_e4m3(w + (size_t)r * K, (const uint16_t*)gain_fp16, K, q + (size_t)r * K, scales + r);
+    return KIE_OK;
+}
+
+int kie_set_prefill_mode(kie_model* m, int32_t mode) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    if (mode != KIE_PREFILL_AUTO && mode != KIE_PREFILL_PASSES) return fail(m, KIE_ERR_ARG, "unknown prefill mode");
+    m->prefill_mode = mode;
+    return KIE_OK;
+}
+
+int kie_gemm_probe(const float* A, const void* W, float* Y, int32_t n, int32_t M, int32_t K, void* hip_stream,
+                   float* ms_out) {
+    if (!A || !W || !Y || n < 1 || M < 1 || K < 32 || K % 32) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    hipStream_t s = (hipStream_t)hip_stream;
+    GemmRows R;
+    R.base = (const uint8_t*)W;
+    R.slab = nullptr;
+    R.M = M;
+    R.K = K;
+    R.gran = 1;
+    R.dense = 1;
+    hipEvent_t e0, e1;
+    HIP_TRY(nullptr, hipEventCreate(&e0));
+    HIP_TRY(nullptr, hipEventCreate(&e1));
+    HIP_TRY(nullptr, hipEventRecord(e0, s));
+    hipError_t le = launch_gemm_mfma(A, K, n, R, Y, M, s);
+    if (le != hipSuccess) return hip_fail(nullptr, le, "gemm probe launch");
+    HIP_TRY(nullptr, hipEventRecord(e1, s));
+    HIP_TRY(nullptr, hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIP_TRY(nullptr, hipEventElapsedTime(&ms, e0, e1));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (ms_out) *ms_out = ms;
     return KIE_OK;
 }
 

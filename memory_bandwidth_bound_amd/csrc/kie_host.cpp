@@ -160,6 +160,21 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_args = take(4096);
     Y.off_idle = take(16384);
     Y.off_trace = take((size_t)kTracePhases * kGrid * 4 * 8);
+    if (batched_prefill_ok(D)) {
+        const size_t R = kPrefillRows;
+        size_t kmax = D.d, ymax = (size_t)(D.H + 2 * D.Hkv) * D.hd;
+        if ((size_t)D.H * D.hd > kmax) kmax = (size_t)D.H * D.hd;
+        if ((size_t)D.F > kmax) kmax = D.F;
+        if ((size_t)2 * D.F > ymax) ymax = (size_t)2 * D.F;
+        if ((size_t)D.V > ymax) ymax = D.V;
+        if ((size_t)D.d > ymax) ymax = D.d;
+        Y.off_pf_x = take(R * D.d * 4);
+        Y.off_pf_a = take(R * kmax * 4);
+        Y.off_pf_y = take(R * ymax * 4);
+        Y.off_pf_q = take(R * D.H * D.hd * 4);
+        Y.off_pf_tok = take((R + 4) * 4);
+        Y.off_pf_slab = take((size_t)5 * kGrid * 4);
+    }
     Y.layer_scales = 0;
     if (D.w8) {
         for (int i = 0; i < layer_block_phase_count(D); ++i) Y.layer_scales += phase_shape(D, layer_block_phase(D, i)).M;

@@ -13,6 +13,10 @@
 namespace kie {
 
 constexpr int kDebugRows = 64;    // logits rows buffered on the device per launch
+constexpr int kPrefillRows = 256; // prompt tokens per batched-prefill chunk
+
+// Does the batched (matrix-core) prefill support this model? Dense fp16.
+inline bool batched_prefill_ok(const Dims& D) { return D.E == 0 && !D.w8; }
 
 // Byte offsets of every region of the caller's device workspace.
 struct Layout {
@@ -47,6 +51,13 @@ struct Layout {
     size_t off_idle;              // 16 KiB read by weight batches that have nothing to stream
     size_t off_trace;             // i64 [kTracePhases][kGrid][4] phase timeline
     size_t off_scales;            // fp8: f32 per layer [QKV rows][Wo rows][gate/up rows][down rows], then [V] LM
+    // batched prefill (dense fp16 models), chunks of kPrefillRows tokens
+    size_t off_pf_x;              // f32 [R][d] residual
+    size_t off_pf_a;              // f32 [R][max(d, H hd, F)] GEMM input
+    size_t off_pf_y;              // f32 [R][max(QKV rows, 2F, V)] GEMM output
+    size_t off_pf_q;              // f32 [R][H hd] queries
+    size_t off_pf_tok;            // i32 [R] tokens, then i32 [4] argmax
+    size_t off_pf_slab;           // i32 [5][kGrid] slab offsets: QKV, Wo, gate/up, down (layer block), LM
     size_t layer_scales;          // floats per layer
     size_t total;
     int piece_off[kGrid + 1];     // units: start of workgroup w's piece in a layer block

@@ -91,6 +91,37 @@ struct GemvArgs {
     int32_t M, K, copies, accumulate;
 };
 
+// Weight rows of one GEMM: row m of M rows of K fp16 is at base +
+// slab[w] KiB + (m - row0(w)) K 2 bytes, w its owner in the even split of M
+// rows in groups of gran over the persistent grid (the decode layout), or at
+// base + m K 2 bytes when dense.
+struct GemmRows {
+    const uint8_t* base;
+    const int32_t* slab;   // [kGrid] units (device memory)
+    int32_t M, K, gran, dense;
+};
+
+// Row-wise prefill kernels (kie_prefill.hip).
+enum : int { PF_EMBED = 0, PF_RMSNORM, PF_RESIDUAL, PF_SWIGLU, PF_QKV, PF_ATTN, PF_ARGMAX };
+struct PrefillRowArgs {
+    Dims D;
+    float eps;
+    int32_t n;        // rows (tokens) of this chunk
+    int32_t pos0;     // position of row 0
+    int32_t layer;
+    int32_t ldy;      // row stride of Y
+    const uint16_t* emb;
+    const int32_t* tok;
+    float* X;         // [n][d] residual
+    float* A;         // GEMM input rows ([n][d], attention output [n][H hd], SwiGLU output [n][F])
+    const float* Y;   // GEMM output rows (PF_ARGMAX: the one row to reduce, V wide)
+    float* Q;         // [n][H hd] rotated queries
+    const float* rope;
+    uint16_t* kc;
+    uint16_t* vc;
+    int32_t* out;     // PF_ARGMAX: the index
+};
+
 // Phases per decode step (used by the host to advance phase ids).
 inline int phases_per_layer(const Dims& D) { return D.E ? 7 : 6; }
 inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2; }
@@ -109,6 +140,11 @@ hipError_t launch_gemv_direct(const GemvArgs& a, hipStream_t s);
 hipError_t launch_barrier_probe(int variant, uint64_t* words, uint32_t* status, int32_t* errors, int rounds,
                                 int grid, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);
+// Y[p][m] = sum_k A[p][k] W(m)[k] on the matrix cores, p < n, m < R.M; A fp32
+// (row stride lda, a multiple of 4), taken as two fp16 terms; R.K a multiple
+// of 32.
+hipError_t launch_gemm_mfma(const float* A, int lda, int n, const GemmRows& R, float* Y, int ldy, hipStream_t s);
+hipError_t launch_prefill_rows(int op, const PrefillRowArgs& r, hipStream_t s);
 // out[c] = the device's fp8 (E4M3) conversion of code c, c < 256.
 hipError_t launch_e4m3_table(float* out, hipStream_t s);
 // out[w] = the XCD workgroup w of a grid-sized cooperative launch ran on.

@@ -1,0 +1,289 @@
+// kie_prefill.hip - batched prefill on the matrix cores (gfx950 MFMA).
+//
+// Decode at batch 1 is a matrix-vector product; a prompt of P tokens is not:
+// its projections multiply P activation rows by every weight row, a dense
+// contraction, so they run here as tiled GEMMs on v_mfma_f32_32x32x8_f16
+// (fp16 x fp16 -> fp32). The pages measure decode, not prefill (paper-digest.app
+// digest, "Core Mechanics": time-to-first-token is outside the metric); this
+// path exists so that a prompt is not P sequential decode passes.
+//
+// The GEMMs read the decode kernel's repacked weights in place (each
+// workgroup's rows of a phase are one contiguous slab; a row map finds row r),
+// so RMSNorm gains are already folded in and QKV / gate-up rows come in the
+// decode kernel's virtual order (rotary pairs adjacent, gate/up interleaved).
+// Activations enter the GEMM as two fp16 terms (hi = fp16(a), lo =
+// fp16(a - hi)), two MFMAs per step, so inputs keep about 22 significant bits
+// as in decode. Everything else (norms, RoPE, the KV append, causal attention,
+// SwiGLU, residual adds, the argmax) is plain VALU work on [rows][width]
+// buffers, one small kernel each.
+#include <hip/hip_runtime.h>
+
+#include "kie_common.h"
+#include "kie_device.h"
+#include "kie_kernels.h"
+
+namespace kie {
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ GEMM --
+// Y[p][m] = sum_k A[p][k] * W(m)[k] for p < n rows of A (fp32, row stride
+// lda) and m < M weight rows (fp16, K each) found by the row map.
+constexpr int kTile = 64;          // rows of A and of W per workgroup
+constexpr int kTk = 32;            // K per step
+constexpr int kLdsStride = kTk + 4;   // halves per LDS row (padding spreads the banks)
+
+__device__ __forceinline__ const uint16_t* row_addr(const GemmRows& R, int m) {
+    if (R.dense) return (const uint16_t*)(R.base + (size_t)m * R.K * 2);
+    // owner workgroup of row m in the even split of M rows in groups of gran
+    const int groups = R.M / R.gran, base = groups / kGrid, rem = groups % kGrid;
+    const int g = m / R.gran;
+    int w;
+    if (g < rem * (base + 1)) w = g / (base + 1);
+    else w = rem + (g - rem * (base + 1)) / base;
+    const int row0 = (w * base + (w < rem ? w : rem)) * R.gran;
+    return (const uint16_t*)(R.base + (size_t)R.slab[w] * kUnitBytes + (size_t)(m - row0) * R.K * 2);
+}
+
+__global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict__ A, int lda, int n, GemmRows R,
+                                                        float* __restrict__ Y, int ldy) {
+    __shared__ __attribute__((aligned(16))) _Float16 ahi[kTile * kLdsStride];
+    __shared__ __attribute__((aligned(16))) _Float16 alo[kTile * kLdsStride];
+    __shared__ __attribute__((aligned(16))) _Float16 bt[kTile * kLdsStride];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = blockIdx.x * kTile, p0 = blockIdx.y * kTile;
+    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's 32 x 32 sub-tile
+    // loader: thread t fills row t / 4, 8 consecutive k at 8 (t % 4)
+    const int lr = tid >> 2, lk = (tid & 3) * 8;
+    const bool arow = p0 + lr < n, brow = m0 + lr < R.M;
+    const float* ap = A + (size_t)(p0 + lr) * lda + lk;
+    const uint16_t* bp = brow ? row_addr(R, m0 + lr) + lk : nullptr;
+    f16x_t acc = {};
+    for (int k0 = 0; k0 < R.K; k0 += kTk) {
+        float av[8];
+        if (arow) {
+            const float4 u0 = *(const float4*)(ap + k0), u1 = *(const float4*)(ap + k0 + 4);
+            av[0] = u0.x; av[1] = u0.y; av[2] = u0.z; av[3] = u0.w;
+            av[4] = u1.x; av[5] = u1.y; av[6] = u1.z; av[7] = u1.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = 0.f;
+        }
+        uint4 bv = brow ? *(const uint4*)(bp + k0) : make_uint4(0, 0, 0, 0);
+        __syncthreads();   // the previous step's reads are done
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const _Float16 h = (_Float16)av[e];
+            ahi[lr * kLdsStride + lk + e] = h;
+            alo[lr * kLdsStride + lk + e] = (_Float16)(av[e] - (float)h);
+        }
+        *(uint2*)&bt[lr * kLdsStride + lk] = make_uint2(bv.x, bv.y);
+        *(uint2*)&bt[lr * kLdsStride + lk + 4] = make_uint2(bv.z, bv.w);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kTk; kk += 8) {
+            // A[i][k]: lane i + 32 (k / 4) holds k % 4; B[k][j]: lane j + 32 (k / 4)
+            const int kq = kk + 4 * (lane >> 5);
+            const h4_t a_h = *(const h4_t*)&ahi[(wr + (lane & 31)) * kLdsStride + kq];
+            const h4_t a_l = *(const h4_t*)&alo[(wr + (lane & 31)) * kLdsStride + kq];
+            const h4_t b = *(const h4_t*)&bt[(wc + (lane & 31)) * kLdsStride + kq];
+            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, acc, 0, 0, 0);
+        }
+    }
+    // D[i][j]: lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
+        const int p = p0 + wr + i, m = m0 + wc + j;
+        if (p < n && m < R.M) Y[(size_t)p * ldy + m] = acc[v];
+    }
+}
+
+hipError_t launch_gemm_mfma(const float* A, int lda, int n, const GemmRows& R, float* Y, int ldy, hipStream_t s) {
+    if (R.K % kTk || lda % 4 || n < 1 || R.M < 1) return hipErrorInvalidValue;
+    dim3 grid((unsigned)ceil_div(R.M, kTile), (unsigned)ceil_div(n, kTile));
+    hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), 0, s, A, lda, n, R, Y, ldy);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------- row kernels --
+// X[t][:] = E[tok[t]] (fp16 -> fp32)
+__global__ void pf_embed_kernel(const uint16_t* __restrict__ E, const int32_t* __restrict__ tok, int d,
+                                float* __restrict__ X) {
+    const int t = blockIdx.x;
+    const uint16_t* e = E + (size_t)tok[t] * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) X[(size_t)t * d + i] = h2f_bits(e[i]);
+}
+
+// A[t][:] = X[t][:] / sqrt(mean(X[t]^2) + eps) (the gains are in the weights)
+__global__ void __launch_bounds__(256) pf_rmsnorm_kernel(const float* __restrict__ X, int d, float eps,
+                                                         float* __restrict__ Aout) {
+    __shared__ float part[4];
+    const int t = blockIdx.x;
+    const float* x = X + (size_t)t * d;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) ss += x[i] * x[i];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float s = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) Aout[(size_t)t * d + i] = x[i] * s;
+}
+
+// X += Y (rows of d)
+__global__ void pf_residual_kernel(float* __restrict__ X, const float* __restrict__ Y, int d, int ldy) {
+    const int t = blockIdx.x;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) X[(size_t)t * d + i] += Y[(size_t)t * ldy + i];
+}
+
+// A[t][m] = silu(Y[t][2m]) * Y[t][2m+1]: gate/up rows come interleaved
+__global__ void pf_swiglu_kernel(const float* __restrict__ Y, int F, int ldy, float* __restrict__ Aout) {
+    const int t = blockIdx.x;
+    for (int m = threadIdx.x; m < F; m += blockDim.x) {
+        const float g = Y[(size_t)t * ldy + 2 * m], u = Y[(size_t)t * ldy + 2 * m + 1];
+        Aout[(size_t)t * F + m] = g / (1.0f + __expf(-g)) * u;
+    }
+}
+
+// QKV rows of token t at position pos0 + t: rotate the rotary pairs of q and k
+// (virtual rows 2i, 2i+1 of a head are elements i, i + hd/2) with the table
+// row of that position; q to Q[t][H*hd] (natural order), k and v (fp16) to
+// the cache. One thread per pair of virtual rows.
+__global__ void pf_qkv_kernel(const float* __restrict__ Y, int ldy, int pos0, int layer, Dims D,
+                              const float* __restrict__ rope, float* __restrict__ Q, uint16_t* __restrict__ kc,
+                              uint16_t* __restrict__ vc) {
+    const int t = blockIdx.x, hd = D.hd, qd = D.H * hd, kd = D.Hkv * hd;
+    const int pos = pos0 + t;
+    const float* y = Y + (size_t)t * ldy;
+    for (int pr = threadIdx.x; pr < (qd + 2 * kd) / 2; pr += blockDim.x) {
+        const int r = 2 * pr;
+        const float y0 = y[r], y1 = y[r + 1];
+        if (r < qd + kd) {
+            const bool isq = r < qd;
+            const int rr = isq ? r : r - qd, head = rr / hd, i = (rr % hd) >> 1;
+            const float c = rope[((size_t)pos * (hd / 2) + i) * 2], s = rope[((size_t)pos * (hd / 2) + i) * 2 + 1];
+            const float a = y0 * c - y1 * s, b = y1 * c + y0 * s;
+            if (isq) {
+                Q[(size_t)t * qd + head * hd + i] = a;
+                Q[(size_t)t * qd + head * hd + i + hd / 2] = b;
+            } else {
+                uint16_t* kp = kc + (((size_t)layer * D.Hkv + head) * D.max_seq + pos) * hd;
+                kp[i] = f2h_bits(a);
+                kp[i + hd / 2] = f2h_bits(b);
+            }
+        } else {
+            const int vi = r - qd - kd, g = vi / hd, dd = vi % hd;
+            uint16_t* vp = vc + (((size_t)layer * D.Hkv + g) * D.max_seq + pos) * hd;
+            vp[dd] = f2h_bits(y0);
+            vp[dd + 1] = f2h_bits(y1);
+        }
+    }
+}
+
+// Causal attention of token t (position pos0 + t) for query head j (one wave):
+// softmax over positions u <= pos of q . K[u] / sqrt(hd), times V[u], with
+// the keys and values read back from the cache (fp16, as decode reads them).
+// Lanes take 64 positions at a time for the scores (online softmax across
+// blocks), then the head dimensions for the weighted sum.
+template <int HD>
+__global__ void __launch_bounds__(64) pf_attention_kernel(const float* __restrict__ Q, int pos0, int layer, Dims D,
+                                                          const uint16_t* __restrict__ kc,
+                                                          const uint16_t* __restrict__ vc, float* __restrict__ O) {
+    __shared__ float q[HD];
+    __shared__ float pr[64];
+    const int t = blockIdx.x, j = blockIdx.y, lane = threadIdx.x;
+    const int g = j / (D.H / D.Hkv), c = pos0 + t + 1;
+    const float scale = 1.0f / sqrtf((float)HD);
+    for (int i = lane; i < HD; i += 64) q[i] = Q[(size_t)t * D.H * HD + j * HD + i] * scale;
+    __syncthreads();
+    const uint16_t* Kb = kc + ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
+    const uint16_t* Vb = vc + ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
+    constexpr int DPL = HD / 64;   // head dimensions per lane in the weighted sum
+    float m = -3.0e38f, l = 0.f, o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+    for (int u0 = 0; u0 < c; u0 += 64) {
+        const int u = u0 + lane;
+        float sc = -3.0e38f;
+        if (u < c) {
+            const uint16_t* kr = Kb + (size_t)u * HD;
+            float acc = 0.f;
+            for (int i = 0; i < HD; i += 8) {
+                const uint4 w = *(const uint4*)(kr + i);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc += h2f_bits((uint16_t)ww[e]) * q[i + 2 * e];
+                    acc += h2f_bits((uint16_t)(ww[e] >> 16)) * q[i + 2 * e + 1];
+                }
+            }
+            sc = acc;
+        }
+        const float mx = fmaxf(m, wave_max(sc));
+        const float p = u < c ? __expf(sc - mx) : 0.f;
+        const float cr = __expf(m - mx);
+        l = l * cr + wave_sum(p);
+        __syncthreads();
+        pr[lane] = p;
+        __syncthreads();
+        const int nb = (c - u0 < 64) ? c - u0 : 64;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] *= cr;
+        for (int k = 0; k < nb; ++k) {
+            const float pk = pr[k];
+            const uint16_t* vr = Vb + (size_t)(u0 + k) * HD;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[e] += pk * h2f_bits(vr[lane + 64 * e]);
+        }
+        m = mx;
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) O[(size_t)t * D.H * HD + j * HD + lane + 64 * e] = o[e] / l;
+}
+
+// Index of the largest of n values (ties to the lowest index); one workgroup.
+__global__ void __launch_bounds__(256) pf_argmax_kernel(const float* __restrict__ y, int n, int32_t* out) {
+    __shared__ float bv[4];
+    __shared__ int bi[4];
+    float v = -3.4e38f;
+    int idx = 0x7fffffff;
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+        if (y[i] > v || (y[i] == v && i < idx)) { v = y[i]; idx = i; }
+    wave_argmax(v, idx);
+    if ((threadIdx.x & 63) == 0) { bv[threadIdx.x >> 6] = v; bi[threadIdx.x >> 6] = idx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (bv[w] > v || (bv[w] == v && bi[w] < idx)) { v = bv[w]; idx = bi[w]; }
+        out[0] = (idx >= 0 && idx < n) ? idx : 0;   // out of range only with NaN logits
+    }
+}
+
+hipError_t launch_prefill_rows(int op, const PrefillRowArgs& r, hipStream_t s) {
+    const dim3 rows((unsigned)r.n);
+    switch (op) {
+    case PF_EMBED: hipLaunchKernelGGL(pf_embed_kernel, rows, dim3(256), 0, s, r.emb, r.tok, r.D.d, r.X); break;
+    case PF_RMSNORM: hipLaunchKernelGGL(pf_rmsnorm_kernel, rows, dim3(256), 0, s, r.X, r.D.d, r.eps, r.A); break;
+    case PF_RESIDUAL: hipLaunchKernelGGL(pf_residual_kernel, rows, dim3(256), 0, s, r.X, r.Y, r.D.d, r.ldy); break;
+    case PF_SWIGLU: hipLaunchKernelGGL(pf_swiglu_kernel, rows, dim3(256), 0, s, r.Y, r.D.F, r.ldy, r.A); break;
+    case PF_QKV:
+        hipLaunchKernelGGL(pf_qkv_kernel, rows, dim3(256), 0, s, r.Y, r.ldy, r.pos0, r.layer, r.D, r.rope, r.Q,
+                           r.kc, r.vc);
+        break;
+    case PF_ATTN:
+        if (r.D.hd == 64)
+            hipLaunchKernelGGL(pf_attention_kernel<64>, dim3((unsigned)r.n, (unsigned)r.D.H), dim3(64), 0, s, r.Q,
+                               r.pos0, r.layer, r.D, r.kc, r.vc, r.A);
+        else
+            hipLaunchKernelGGL(pf_attention_kernel<128>, dim3((unsigned)r.n, (unsigned)r.D.H), dim3(64), 0, s, r.Q,
+                               r.pos0, r.layer, r.D, r.kc, r.vc, r.A);
+        break;
+    case PF_ARGMAX: hipLaunchKernelGGL(pf_argmax_kernel, dim3(1), dim3(256), 0, s, r.Y, r.D.V, r.out); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kie

@@ -85,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_launch_probe": (c_int32, [c_int32, c_void_p, POINTER(c_float)]),
         "kie_barrier_probe_noalloc": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
         "kie_xcd_map": (c_int32, [POINTER(c_int32), c_void_p]),
+        "kie_set_prefill_mode": (c_int32, [c_void_p, c_int32]),
+        "kie_gemm_probe": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                     POINTER(c_float)]),
         "kie_e4m3_table_probe": (c_int32, [POINTER(c_float), c_void_p]),
         "kie_quantize_e4m3_rows": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float)]),
     }
@@ -287,6 +290,12 @@ class Model:
                                       n_pos, int(pending))
         _check(rc, self._h)
 
+    def set_prefill_mode(self, mode: str):
+        """"auto" (batched on the matrix cores where supported) or "passes"
+        (one decode pass per prompt token in one persistent launch)."""
+        code = {"auto": 0, "passes": 1}[mode]
+        _check(self._lib.kie_set_prefill_mode(self._h, code), self._h)
+
     def set_limits(self, spin_limit: int = 0, watchdog_ms: int = 0):
         """Device wait limit (polls; 0 = default) and host watchdog per launch
         (ms; 0 = automatic, negative = none) for later calls."""
@@ -395,6 +404,27 @@ def quantize_e4m3_rows(W: np.ndarray, gain: Optional[np.ndarray] = None):
                                       W.shape[0], W.shape[1], c_void_p(q.ctypes.data),
                                       s.ctypes.data_as(POINTER(c_float))))
     return q, s
+
+
+def gemm_probe(A, W, stream=None):
+    """Y = A @ W.T on the matrix cores for device tensors A float32 [n, K] and
+    W float16 [M, K]; returns (Y float32 [n, M], device milliseconds)."""
+    import torch
+    lib = load_library()
+    assert A.dtype == torch.float32 and W.dtype == torch.float16 and A.is_cuda and W.is_cuda
+    A = A.contiguous()
+    W = W.contiguous()
+    n, K = A.shape
+    M, K2 = W.shape
+    if K2 != K:
+        raise KieError(-1, "A and W must share K")
+    Y = torch.empty((n, M), dtype=torch.float32, device=A.device)
+    ms = c_float()
+    with torch.cuda.device(A.device):
+        rc = lib.kie_gemm_probe(c_void_p(A.data_ptr()), c_void_p(W.data_ptr()), c_void_p(Y.data_ptr()), n, M, K,
+                                _stream_handle(torch, A.device, stream), ctypes.byref(ms))
+    _check(rc)
+    return Y, float(ms.value)
 
 
 def e4m3_table_probe(device: str = "cuda:0"):

@@ -341,3 +341,42 @@ def test_host_watchdog_reports_overrun_then_recovery(torch_cuda):
         assert np.array_equal(got, want)
     finally:
         m.close()
+
+
+# ---- the batched (matrix-core) prefill ---------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_gains", "gqa5_chunks_hd128", "gqa8_hd64"])
+def test_batched_prefill_rows_and_modes(torch_cuda, name):
+    """Every prompt row's logits from the batched prefill against the oracle's
+    full causal forward, element by element (the 760-token prompt spans
+    three chunks of 256); the same prompt prefilled pass by pass gives the same
+    first token wherever the gap decides it, and decoding after either
+    prefill matches the oracle."""
+    cfg = CASES[name]
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    say(f"{name}: oracle full forward over the {len(P)}-token prompt")
+    ref = oracle.Decoder(cfg, W)
+    rows = ref.forward_full(list(P))
+    first = int(np.argmax(rows[-1]))
+    dec = oracle.Decoder(cfg, W)
+    dec.prefill_batched(P)
+    ids, drows, _ = dec.decode(4, keep_logits=True)
+    m = _model(cfg, W)
+    try:
+        g_first, g_logits, _ = m.prefill(P, logits=True)
+        check_rows(g_logits, rows, label=f"{name} batched-prefill")
+        if oracle.top2_gap(rows[-1]) > 2e-2:
+            assert g_first == first
+        m.rewind(len(P), first)
+        _, g_rows, _ = m.decode(4, force=ids, logits=True)
+        check_rows(g_rows, drows, label=f"{name} after-batched")
+        m.set_prefill_mode("passes")
+        p_first, p_logits, _ = m.prefill(P, logits=True)
+        check_rows(p_logits[-1:], rows[-1:], label=f"{name} passes-prefill")
+        if oracle.top2_gap(rows[-1]) > 2e-2:
+            assert p_first == g_first
+        m.rewind(len(P), first)
+        _, p_rows, _ = m.decode(4, force=ids, logits=True)
+        check_rows(p_rows, drows, label=f"{name} after-passes")
+    finally:
+        m.close()

@@ -124,3 +124,41 @@ def test_launch_probe(torch_cuda):
     us = kie.launch_probe(2000)
     say(f"launch probe: {us:.2f} us per empty kernel launch")
     assert us > 0
+
+
+# ---- the matrix-core GEMM of the batched prefill ----------------------------------
+def _gemm(torch, A, W):
+    from memory_bandwidth_bound_amd import kie
+    Y, ms = kie.gemm_probe(torch.from_numpy(A).cuda(), torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    return Y.cpu().numpy().astype(np.float64), ms
+
+
+@pytest.mark.parametrize("shape", [(128, 3584, 2560), (1, 64, 32), (37, 100, 256), (300, 130, 1024),
+                                   (64, 2560, 8192)])
+def test_gemm_probe_matches_f64(torch_cuda, shape):
+    """Y = A W^T against float64 within the bound of fp32 accumulation plus
+    the two-term fp16 rounding of A (2^-22 relative per element)."""
+    n, M, K = shape
+    say(f"gemm probe n={n} M={M} K={K}")
+    rng = np.random.default_rng(n * 7 + M + K)
+    A = rng.standard_normal((n, K)).astype(np.float32)
+    W = (rng.standard_normal((M, K)) * 0.02).astype(np.float16)
+    Y, _ = _gemm(torch_cuda, A, W)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    bound = (K * 2.0 ** -23 + 2.0 ** -21) * (np.abs(A.astype(np.float64)) @ np.abs(W.astype(np.float64)).T) + 1e-30
+    assert np.all(np.abs(Y - ref) <= bound)
+
+
+def test_gemm_probe_integer_exact_and_unit_rows(torch_cuda):
+    rng = np.random.default_rng(8)
+    n, M, K = 70, 90, 512
+    A = rng.integers(-8, 9, size=(n, K)).astype(np.float32)
+    W = rng.integers(-8, 9, size=(M, K)).astype(np.float16)
+    Y, _ = _gemm(torch_cuda, A, W)
+    assert np.array_equal(Y, A.astype(np.float64) @ W.astype(np.float64).T)
+    E = np.zeros((n, K), dtype=np.float32)
+    E[np.arange(n), np.arange(n) % K] = 1.0                 # row p of A = e_(p mod K)
+    W2 = (rng.standard_normal((M, K)) * 0.1).astype(np.float16)
+    Y2, _ = _gemm(torch_cuda, E, W2)
+    assert np.array_equal(Y2, W2.astype(np.float64)[:, np.arange(n) % K].T)
