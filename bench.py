@@ -246,6 +246,56 @@ def bench_gemv(args):
     return line
 
 
+def bench_prefill(args):
+    """Prompt processing of the ~2.1B decoder: the 128-token prompt through the
+    batched matrix-core prefill (and, for comparison, one persistent launch
+    of 128 decode passes); roofline of the GEMM kernel on the prompt's largest
+    projection (gate/up: 128 x 16384 x 2560), timed by the library with HIP
+    events. Not the decode metric."""
+    import torch
+    from memory_bandwidth_bound_amd import kie
+    cfg = synth.get_config("2b")
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    m = kie.Model(cfg, W, device="cuda:0")
+    out = {}
+    for mode in ("auto", "passes"):
+        m.set_prefill_mode(mode)
+        for _ in range(args.warmup):
+            m.prefill(P)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            m.prefill(P)
+        torch.cuda.synchronize()
+        out[mode] = (time.perf_counter() - t0) / args.steps
+    m.close()
+    del W
+    n, M, K = len(P), 2 * cfg.ffn_dim, cfg.d_model
+    A = torch.randn((n, K), dtype=torch.float32, device="cuda:0")
+    Wg = (torch.randn((M, K), device="cuda:0") * 0.02).to(torch.float16)
+    kie.gemm_probe(A, Wg)
+    ms = float(np.mean([kie.gemm_probe(A, Wg)[1] for _ in range(max(3, args.steps))]))
+    flops = 2.0 * n * M * K                          # algorithmic: one product per (row, weight)
+    tflops = flops / (ms * 1e-3) / 1e12
+    wbytes = 2.0 * M * K + 4.0 * n * K + 4.0 * n * M  # weights once, fp32 activations in, fp32 out
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    # 128 prompt rows: 2n/2 = 128 FLOP per weight byte, below the ridge of
+    # 2.5 PFLOP/s over 8 TB/s (~312): the GEMM's roofline is HBM
+    return {"metric": "prefill tokens/sec on 1 MI355X (batched matrix-core prompt processing)",
+            "value": round(n / out["auto"], 1), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(out["auto"] * 1e3, 3), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp16 weights, fp16x2 activations, fp32 accumulate",
+            "data": "synthetic",
+            "config": {"workload": describe(cfg).replace(f", {cfg.decode_steps} greedy decode steps per request",
+                                                         "; the prompt only"),
+                       "prompt_tokens": n, "passes_ms": round(out["passes"] * 1e3, 3)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_GBS, 4), "traffic": None,
+                         "kernel": f"gemm_mfma {n}x{M}x{K}, {ms:.4f} ms, {tflops:.1f} TFLOP/s of 2500 dense fp16 "
+                                   f"(two fp16 MFMAs per step: hi and lo terms)"}}
+
+
 def bench_copy(args):
     """Counter calibration: a plain device copy of a known size (1 GiB read,
     1 GiB written per launch), timed like the other workloads."""
@@ -280,7 +330,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="2b",
-                    help="2b (default), 2b_32k, 2b_fp8, moe, tiny, gemv, or copy (counter calibration)")
+                    help="2b (default), 2b_32k, 2b_fp8, moe, tiny, gemv, prefill, or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -296,6 +346,8 @@ def main():
         sys.exit("bench.py needs a GPU")
     if args.config == "gemv":
         line = bench_gemv(args)
+    elif args.config == "prefill":
+        line = bench_prefill(args)
     elif args.config == "copy":
         line = bench_copy(args)
     else:

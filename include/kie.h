@@ -339,7 +339,7 @@ int kie_barrier_probe_noalloc(int32_t variant, int32_t rounds, void* hip_stream,
  * sum_k A[p][k] W[m][k] for p < n, m < M, with A fp32 [n][K], W fp16 [M][K]
  * and Y fp32 [n][M], all row-major device memory owned by the caller; A is
  * taken as two fp16 terms (about 22 significant bits), products accumulated
- * in fp32 on v_mfma_f32_32x32x8_f16. K a multiple of 32. *ms_out (may be
+ * in fp32 on v_mfma_f32_32x32x8_f16. K a multiple of 64. *ms_out (may be
  * NULL) receives the device time. Waits for the launch.
  */
 int kie_gemm_probe(const float* A, const void* W, float* Y, int32_t n, int32_t M, int32_t K, void* hip_stream,

@@ -587,7 +587,7 @@ int kie_set_prefill_mode(kie_model* m, int32_t mode) {
 
 int kie_gemm_probe(const float* A, const void* W, float* Y, int32_t n, int32_t M, int32_t K, void* hip_stream,
                    float* ms_out) {
-    if (!A || !W || !Y || n < 1 || M < 1 || K < 32 || K % 32) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    if (!A || !W || !Y || n < 1 || M < 1 || K < 64 || K % 64) return fail(nullptr, KIE_ERR_ARG, "bad argument");
     hipStream_t s = (hipStream_t)hip_stream;
     GemmRows R;
     R.base = (const uint8_t*)W;

@@ -142,7 +142,7 @@ hipError_t launch_barrier_probe(int variant, uint64_t* words, uint32_t* status, 
 hipError_t launch_empty(hipStream_t s);
 // Y[p][m] = sum_k A[p][k] W(m)[k] on the matrix cores, p < n, m < R.M; A fp32
 // (row stride lda, a multiple of 4), taken as two fp16 terms; R.K a multiple
-// of 32.
+// of 64.
 hipError_t launch_gemm_mfma(const float* A, int lda, int n, const GemmRows& R, float* Y, int ldy, hipStream_t s);
 hipError_t launch_prefill_rows(int op, const PrefillRowArgs& r, hipStream_t s);
 // out[c] = the device's fp8 (E4M3) conversion of code c, c < 256.

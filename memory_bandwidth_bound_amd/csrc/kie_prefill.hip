@@ -31,7 +31,7 @@ typedef float f16x_t __attribute__((ext_vector_type(16)));
 // Y[p][m] = sum_k A[p][k] * W(m)[k] for p < n rows of A (fp32, row stride
 // lda) and m < M weight rows (fp16, K each) found by the row map.
 constexpr int kTile = 64;          // rows of A and of W per workgroup
-constexpr int kTk = 32;            // K per step
+constexpr int kTk = 64;            // K per step
 constexpr int kLdsStride = kTk + 4;   // halves per LDS row (padding spreads the banks)
 
 __device__ __forceinline__ const uint16_t* row_addr(const GemmRows& R, int m) {
@@ -46,6 +46,32 @@ __device__ __forceinline__ const uint16_t* row_addr(const GemmRows& R, int m) {
     return (const uint16_t*)(R.base + (size_t)R.slab[w] * kUnitBytes + (size_t)(m - row0) * R.K * 2);
 }
 
+// One step's share of a thread: 16 consecutive k of one row of A (fp32) and
+// of one row of W (fp16). Thread t loads row t / 4 at k offset 16 (t % 4).
+struct GemmStage {
+    float a[16];
+    uint4 b[2];
+};
+
+__device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const uint16_t* bp, bool arow, bool brow,
+                                          int k0) {
+    if (arow) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 u = *(const float4*)(ap + k0 + 4 * q);
+            st.a[4 * q] = u.x;
+            st.a[4 * q + 1] = u.y;
+            st.a[4 * q + 2] = u.z;
+            st.a[4 * q + 3] = u.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) st.a[e] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) st.b[q] = brow ? *(const uint4*)(bp + k0 + 8 * q) : make_uint4(0, 0, 0, 0);
+}
+
 __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict__ A, int lda, int n, GemmRows R,
                                                         float* __restrict__ Y, int ldy) {
     __shared__ __attribute__((aligned(16))) _Float16 ahi[kTile * kLdsStride];
@@ -54,33 +80,28 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = blockIdx.x * kTile, p0 = blockIdx.y * kTile;
     const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's 32 x 32 sub-tile
-    // loader: thread t fills row t / 4, 8 consecutive k at 8 (t % 4)
-    const int lr = tid >> 2, lk = (tid & 3) * 8;
+    const int lr = tid >> 2, lk = (tid & 3) * 16;
     const bool arow = p0 + lr < n, brow = m0 + lr < R.M;
     const float* ap = A + (size_t)(p0 + lr) * lda + lk;
     const uint16_t* bp = brow ? row_addr(R, m0 + lr) + lk : nullptr;
     f16x_t acc = {};
+    GemmStage st;
+    gemm_load(st, ap, bp, arow, brow, 0);
     for (int k0 = 0; k0 < R.K; k0 += kTk) {
-        float av[8];
-        if (arow) {
-            const float4 u0 = *(const float4*)(ap + k0), u1 = *(const float4*)(ap + k0 + 4);
-            av[0] = u0.x; av[1] = u0.y; av[2] = u0.z; av[3] = u0.w;
-            av[4] = u1.x; av[5] = u1.y; av[6] = u1.z; av[7] = u1.w;
-        } else {
+        __syncthreads();   // the previous step's LDS reads are done
 #pragma unroll
-            for (int e = 0; e < 8; ++e) av[e] = 0.f;
-        }
-        uint4 bv = brow ? *(const uint4*)(bp + k0) : make_uint4(0, 0, 0, 0);
-        __syncthreads();   // the previous step's reads are done
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const _Float16 h = (_Float16)av[e];
+        for (int e = 0; e < 16; ++e) {
+            const _Float16 h = (_Float16)st.a[e];
             ahi[lr * kLdsStride + lk + e] = h;
-            alo[lr * kLdsStride + lk + e] = (_Float16)(av[e] - (float)h);
+            alo[lr * kLdsStride + lk + e] = (_Float16)(st.a[e] - (float)h);
         }
-        *(uint2*)&bt[lr * kLdsStride + lk] = make_uint2(bv.x, bv.y);
-        *(uint2*)&bt[lr * kLdsStride + lk + 4] = make_uint2(bv.z, bv.w);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            *(uint2*)&bt[lr * kLdsStride + lk + 8 * q] = make_uint2(st.b[q].x, st.b[q].y);
+            *(uint2*)&bt[lr * kLdsStride + lk + 8 * q + 4] = make_uint2(st.b[q].z, st.b[q].w);
+        }
         __syncthreads();
+        if (k0 + kTk < R.K) gemm_load(st, ap, bp, arow, brow, k0 + kTk);   // next step's loads fly meanwhile
 #pragma unroll
         for (int kk = 0; kk < kTk; kk += 8) {
             // A[i][k]: lane i + 32 (k / 4) holds k % 4; B[k][j]: lane j + 32 (k / 4)

@@ -134,7 +134,7 @@ def _gemm(torch, A, W):
     return Y.cpu().numpy().astype(np.float64), ms
 
 
-@pytest.mark.parametrize("shape", [(128, 3584, 2560), (1, 64, 32), (37, 100, 256), (300, 130, 1024),
+@pytest.mark.parametrize("shape", [(128, 3584, 2560), (1, 64, 64), (37, 100, 256), (300, 130, 1024),
                                    (64, 2560, 8192)])
 def test_gemm_probe_matches_f64(torch_cuda, shape):
     """Y = A W^T against float64 within the bound of fp32 accumulation plus
