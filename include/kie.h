@@ -72,9 +72,10 @@ enum {
  *    Wv: g_attn; Wg, Wu: g_ffn; W_lm: g_final; Wo, Wd: none): for a row v of
  *    fp32 values (v_k = w_k * g_k), s = fp32(max_k |v_k| / 448) (1 for an
  *    all-zero row) and q_k = E4M3 nearest to fp32(v_k / s), ties to the even
- *    code (kie_quantize_e4m3_rows). The embedding stays fp16. Dense models
- *    with head_dim 128 only; d_model, ffn_dim and n_heads*head_dim multiples
- *    of 512, vocab even.
+ *    code (kie_quantize_e4m3_rows). The embedding stays fp16. MoE: the router
+ *    (g_ffn folded) and every expert's Wg, Wu (g_ffn folded) and Wd the same
+ *    way. head_dim 128 only; d_model, ffn_dim and n_heads*head_dim multiples
+ *    of 512, vocab and n_experts even.
  */
 typedef struct kie_config {
     int32_t n_layers;

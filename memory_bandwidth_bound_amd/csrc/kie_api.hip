@@ -199,8 +199,15 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
         if ((rc = upload(m, L.off_layers + (size_t)l * L.layer_bytes, stage.data(), L.layer_bytes)) != KIE_OK)
             return bail(rc);
         if (D.E) {
+            std::vector<float> esc(D.w8 ? (size_t)(2 * D.F + D.d) : 0);
             for (int e = 0; e < D.E; ++e) {
-                repack_expert(*cfg, L, T, l, e, (uint16_t*)stage.data());
+                if (D.w8) {
+                    repack_expert_fp8(*cfg, L, T, l, e, stage.data(), esc.data());
+                    size_t so = L.off_escales + ((size_t)l * D.E + e) * esc.size() * 4;
+                    if ((rc = upload(m, so, esc.data(), esc.size() * 4)) != KIE_OK) return bail(rc);
+                } else {
+                    repack_expert(*cfg, L, T, l, e, (uint16_t*)stage.data());
+                }
                 size_t off = L.off_experts + ((size_t)l * D.E + e) * L.expert_bytes;
                 if ((rc = upload(m, off, stage.data(), L.expert_bytes)) != KIE_OK) return bail(rc);
             }
@@ -306,6 +313,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.idle = m->ws + L.off_idle;
         a.trace = (int64_t*)(m->ws + L.off_trace);
         a.scales = D.w8 ? (const float*)(m->ws + L.off_scales) : nullptr;
+        a.escales = (D.w8 && D.E) ? (const float*)(m->ws + L.off_escales) : nullptr;
         a.layer_scales = (int32_t)L.layer_scales;
         a.pos0 = m->pos + s0;
         a.pending = tok;

@@ -107,7 +107,7 @@ KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
     case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = 2; break;
     case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;
-    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = 1; break;
+    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = D.w8 ? 2 : 1; break;   // fp8: rows in pairs
     case PH_LM: s.M = D.V; s.K = D.d; s.gran = D.w8 ? 2 : 1; break;   // fp8: rows in pairs
     case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;   // K per selected expert

@@ -204,6 +204,7 @@ struct Smem {
     float own_x[kMaxOwnRows];                   // this workgroup's residual rows (fp32)
     uint32_t sel[16];                           // MoE: experts selected for the current layer
     float pi[16];                               //      and their router probabilities
+    float esc[16 * kMaxOwnRows];                // fp8 MoE: down-row scales [selected expert][own row]
     Geo geo[K_COUNT];
     float ssp[kWaves];                          // per wave: sum of squares of its share of the input
     uint32_t abort;                             // set when the communication wave gave up
@@ -373,6 +374,7 @@ struct Comm {
     bool dead;
     float rq[4];   // QKV epilogue: (cos, sin) of this lane's two rotary pairs, loaded before the input gather
     float rs[4];   // fp8 weights: scales of the rows this lane's epilogue handles, loaded before the input gather
+    float esr[8];  // fp8 MoE: down-row scales of the selected experts (entry lane + 64 j), loaded after routing
 
     __device__ __forceinline__ Comm(const DecodeArgs& args, KIE_LDS Smem* s, const WgPlan& plan)
         : a(args), S(s), W(plan) {
@@ -424,6 +426,7 @@ struct Comm {
             case K_WO: b += mq; r0 = W.wo0; n = W.won; mul = 2; break;
             case K_GU: b += mq + mo; r0 = W.gu0; n = W.gun; mul = 4; break;
             case K_DOWN: b += mq + mo + mg; r0 = W.wo0; n = W.won; mul = 2; break;
+            case K_ROUTER: b += mq + mo; r0 = W.r0; n = W.rn; step = 64; break;
             case K_LM: b = gptr(a.scales) + (size_t)D.L * a.layer_scales; r0 = W.lm0; n = W.lmn; step = 64; mul = 1;
                 break;
             default: break;
@@ -435,6 +438,42 @@ struct Comm {
             }
         }
     }
+    // fp8 MoE, right after routing: the gate/up row scales of this lane's
+    // epilogue rows (4 lane + e of the workgroup's virtual rows) and the
+    // down-row scales of every selected expert (staged in LDS before the down
+    // phase, for the compute waves).
+    __device__ __forceinline__ void load_expert_scales(int layer) {
+        if constexpr (W8) {
+            const Dims& D = a.D;
+            const int per = 2 * D.F + D.d;
+            const KIE_GLOBAL float* b = gptr(a.escales) + (size_t)layer * D.E * per;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lane + e;
+                rs[e] = 1.0f;
+                if (r < W.egun) {
+                    const int vr = W.egu0 + r, k = vr / (2 * D.F);
+                    rs[e] = b[(size_t)S->sel[k] * per + (vr - k * 2 * D.F)];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = lane + 64 * j, k = W.won ? i / W.won : 0;
+                esr[j] = 1.0f;
+                if (i < D.topk * W.won) esr[j] = b[(size_t)S->sel[k] * per + 2 * D.F + W.wo0 + (i - k * W.won)];
+            }
+        }
+    }
+    __device__ __forceinline__ void stage_expert_scales() {
+        if constexpr (W8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = lane + 64 * j;
+                if (i < a.D.topk * W.won) S->esc[i] = esr[j];
+            }
+        }
+    }
+
     __device__ __forceinline__ float rsc(int e) const {
         if constexpr (W8) return rs[e];
         return 1.0f;
@@ -589,10 +628,14 @@ struct Comm {
             break;
         case K_EGU:
             zero_part(W.egun);
-            if (W.negu || W.ned) route(q, it);   // xin and ssp still hold the router's input
+            if (W.negu || W.ned) {
+                route(q, it);   // xin and ssp still hold the router's input
+                if (!dead) load_expert_scales(it.layer);
+            }
             break;
         case K_EDOWN:
             zero_part(W.won);
+            stage_expert_scales();
             if (W.ned) input_share(kind, id_of(q - 1));
             break;
         case K_LM:
@@ -686,8 +729,8 @@ struct Comm {
         }
         case K_ROUTER: {
             const float sc = in_scale();
-            for (int j = lane; j < W.rn; j += 64)
-                fw_store(a.ex.r + W.r0 + j, __builtin_bit_cast(uint32_t, rowsum(j) * sc), id);
+            for (int j = lane; j < W.rn; j += 64)   // one trip: rn <= 4
+                fw_store(a.ex.r + W.r0 + j, __builtin_bit_cast(uint32_t, rowsum(j) * sc * rsc(0)), id);
             break;
         }
         case K_EGU: {
@@ -697,8 +740,9 @@ struct Comm {
                 const int k = vr / (2 * D.F), m = (vr % (2 * D.F)) >> 1;
                 float h[2];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const float gv = rowsum(4 * j + 2 * e) * sc, uv = rowsum(4 * j + 2 * e + 1) * sc;
+                for (int e = 0; e < 2; ++e) {   // one trip of j: egun / 4 <= 64
+                    const float gv = rowsum(4 * j + 2 * e) * sc * rsc(2 * e);
+                    const float uv = rowsum(4 * j + 2 * e + 1) * sc * rsc(2 * e + 1);
                     h[e] = S->pi[k] * (gv / (1.0f + __expf(-gv))) * uv;
                 }
                 fw_store(a.ex.h + k * D.F + m, __builtin_bit_cast(uint32_t, h[0]), id);
@@ -1048,22 +1092,26 @@ struct Compute {
                         const int u = iu + s;
                         size_t off;
                         int k;
+                        // fp8: units hold pairs of rows (one byte per weight), so
+                        // unit counts run over pairs and byte offsets halve
+                        constexpr int rpu = W8 ? 2 : 1;   // rows per unit column
+                        constexpr int wb = W8 ? 1 : 2;    // bytes per weight
                         if (kind == K_EGU) {
                             // virtual rows k * 2F + r: row r of the gate/up block of expert k
-                            const int vr = ig.row0 + u / upr, c = u - (u / upr) * upr;
+                            const int vr = ig.row0 + rpu * (u / upr), c = u - (u / upr) * upr;
                             k = vr / (2 * D.F);
                             const int rr = vr - k * 2 * D.F;
                             int vend = (k + 1) * 2 * D.F;
                             if (vend > ig.row0 + ig.nrows) vend = ig.row0 + ig.nrows;
-                            run = (vend - vr) * upr - c;
-                            off = ((size_t)rr * D.d + (size_t)c * kUnitHalves) * 2;
+                            run = ((vend - vr) / rpu) * upr - c;
+                            off = (size_t)rr * D.d * wb + (size_t)c * kUnitBytes;
                         } else {
                             // expert-major: the workgroup's down rows of expert 0, then 1, ...
-                            const int per = ig.nrows * upr;
+                            const int per = (ig.nrows / rpu) * upr;
                             k = u / per;
                             const int rem = u - k * per;
                             run = per - rem;
-                            off = (size_t)2 * D.F * D.d * 2 + (size_t)ig.row0 * D.F * 2 + (size_t)rem * kUnitBytes;
+                            off = (size_t)2 * D.F * D.d * wb + (size_t)ig.row0 * D.F * wb + (size_t)rem * kUnitBytes;
                         }
                         const int e = __builtin_amdgcn_readfirstlane(S->sel[k]);
                         p = lb + (size_t)e * a.expert_bytes + off;
@@ -1347,11 +1395,14 @@ struct Compute {
         }
     }
 
-    // fp8 weights, any row length: the inputs of each unit read from LDS
-    // (dense only: one segment per row pair).
+    // fp8 weights, any row length: the inputs of each unit read from LDS.
+    // MoE down (ck = selected expert, its input segment ck of xf): each
+    // expert's row partial sum is scaled by that expert's row scale before
+    // it joins the row's sum over experts.
     __device__ __forceinline__ void consume_fp8(uint32_t src, const Slot& sl) {
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
-        const int upr = cg.upr;
+        const int upr = cg.upr, npair = cg.nrows / 2;
+        const bool edown = cg.kind == K_EDOWN;
         uint4 wv[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; ++s)
@@ -1361,11 +1412,15 @@ struct Compute {
         for (int s = 0; s < kNB; ++s) {
             if (s < sl.n) {
                 float x[8];
-                load_xf(S, cseg * kUnitHalves + lane * 8, x);
+                load_xf(S, ck * cg.K + cseg * kUnitHalves + lane * 8, x);
                 dot8_fp8(wv[s], x, acc, acc2);
                 const bool seg_done = cseg + 1 == upr;
                 if (seg_done || s == last) {
-                    const float ra = wave_sum_to_lane63(acc), rb = wave_sum_to_lane63(acc2);
+                    float ra = wave_sum_to_lane63(acc), rb = wave_sum_to_lane63(acc2);
+                    if (edown) {
+                        ra *= S->esc[ck * cg.nrows + 2 * crow];
+                        rb *= S->esc[ck * cg.nrows + 2 * crow + 1];
+                    }
                     if (lane == 63) {
                         S->part[(2 * crow) * kCompute + w] += ra;
                         S->part[(2 * crow + 1) * kCompute + w] += rb;
@@ -1374,7 +1429,10 @@ struct Compute {
                 }
                 if (seg_done) {
                     cseg = 0;
-                    ++crow;
+                    if (++crow == npair) {
+                        crow = 0;
+                        ++ck;
+                    }
                 } else {
                     ++cseg;
                 }

@@ -75,7 +75,7 @@ int validate_config(const kie_config& c, std::string* err) {
     if (c.weight_format != KIE_WEIGHTS_FP16 && c.weight_format != KIE_WEIGHTS_FP8)
         return fail("weight_format must be KIE_WEIGHTS_FP16 or KIE_WEIGHTS_FP8");
     if (c.weight_format == KIE_WEIGHTS_FP8) {
-        if (c.n_experts) return fail("fp8 weights are supported for dense models only");
+        if (c.n_experts % 2) return fail("fp8 weights need an even number of experts (router rows come in pairs)");
         if (c.head_dim != 128) return fail("fp8 weights are supported for head_dim 128 only");
         if (c.d_model % 512 || c.ffn_dim % 512 || (c.n_heads * c.head_dim) % 512)
             return fail("fp8 weights need d_model, ffn_dim and n_heads*head_dim multiples of 512");
@@ -135,7 +135,7 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_layers = take(Y.layer_bytes * D.L);
     Y.off_lm = take(Y.lm_bytes);
     Y.off_emb = take((size_t)D.V * D.d * 2);
-    Y.expert_bytes = D.E ? (size_t)(2 * D.F * D.d + D.d * D.F) * 2 : 0;
+    Y.expert_bytes = D.E ? (size_t)(2 * D.F * D.d + D.d * D.F) * (D.w8 ? 1 : 2) : 0;
     Y.off_experts = take(Y.expert_bytes * D.E * D.L);
     Y.off_rope = take((size_t)D.max_seq * (D.hd / 2) * 8);
     Y.kv_bytes = (size_t)D.L * D.Hkv * D.max_seq * D.hd * 2;
@@ -179,6 +179,7 @@ void make_layout(const kie_config& c, Layout* lay) {
     if (D.w8) {
         for (int i = 0; i < layer_block_phase_count(D); ++i) Y.layer_scales += phase_shape(D, layer_block_phase(D, i)).M;
         Y.off_scales = take(((size_t)D.L * Y.layer_scales + D.V) * 4);
+        if (D.E) Y.off_escales = take((size_t)D.L * D.E * (2 * D.F + D.d) * 4);
     }
     Y.total = off;
 }
@@ -410,6 +411,10 @@ void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* co
             *src = t[tidx_layer(c, l, (row & 1) ? 7 : 6)] + (size_t)(row >> 1) * D.d;
             *g = g_ffn;
             break;
+        case PH_ROUTER:
+            *src = t[tidx_layer(c, l, 6)] + (size_t)row * D.d;
+            *g = g_ffn;
+            break;
         default: *src = t[tidx_layer(c, l, 8)] + (size_t)row * D.F; break;   // PH_DOWN
         }
     };
@@ -432,6 +437,28 @@ void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* co
             }
         }
         sbase += s.M;
+    }
+}
+
+void repack_expert_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int l, int e, uint8_t* dst,
+                       float* scales) {
+    const Dims& D = lay.D;
+    const uint16_t* g = t[tidx_layer(c, l, 5)];
+    const uint16_t* Wg = t[tidx_expert(c, l, e, 0)];
+    const uint16_t* Wu = t[tidx_expert(c, l, e, 1)];
+    const uint16_t* Wd = t[tidx_expert(c, l, e, 2)];
+    std::vector<uint8_t> qa(kMaxInput), qb(kMaxInput);
+    // gate/up rows interleaved (g_p, u_p): pair p is units p * d / 512 ..
+    for (int p = 0; p < D.F; ++p) {
+        quantize_row_e4m3(Wg + (size_t)p * D.d, g, D.d, qa.data(), &scales[2 * p]);
+        quantize_row_e4m3(Wu + (size_t)p * D.d, g, D.d, qb.data(), &scales[2 * p + 1]);
+        put_pair_fp8(dst + (size_t)p * D.d * 2, qa.data(), qb.data(), D.d);
+    }
+    uint8_t* down = dst + (size_t)2 * D.F * D.d;
+    for (int r = 0; r < D.d; r += 2) {
+        quantize_row_e4m3(Wd + (size_t)r * D.F, nullptr, D.F, qa.data(), &scales[2 * D.F + r]);
+        quantize_row_e4m3(Wd + (size_t)(r + 1) * D.F, nullptr, D.F, qb.data(), &scales[2 * D.F + r + 1]);
+        put_pair_fp8(down + (size_t)(r / 2) * D.F * 2, qa.data(), qb.data(), D.F);
     }
 }
 

@@ -59,6 +59,7 @@ struct Layout {
     size_t off_pf_tok;            // i32 [R] tokens, then i32 [4] argmax
     size_t off_pf_slab;           // i32 [5][kGrid] slab offsets: QKV, Wo, gate/up, down (layer block), LM
     size_t layer_scales;          // floats per layer
+    size_t off_escales;           // fp8 MoE: f32 per (layer, expert) [2F gate/up rows][d down rows]
     size_t total;
     int piece_off[kGrid + 1];     // units: start of workgroup w's piece in a layer block
     int lm_off[kGrid + 1];        // units: start of workgroup w's LM slab
@@ -95,6 +96,10 @@ void quantize_row_e4m3(const uint16_t* w, const uint16_t* gain, int K, uint8_t* 
 void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, uint8_t* dst,
                       float* scales);
 void repack_lm_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, uint8_t* dst, float* scales);
+// fp8 MoE: one expert block (gate/up row pairs (g_p, u_p), then down row
+// pairs; expert_bytes) and its 2F + d row scales.
+void repack_expert_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, int expert,
+                       uint8_t* dst, float* scales);
 
 // Canonical tensor index helpers (same order as kie.h documents).
 int tidx_emb();

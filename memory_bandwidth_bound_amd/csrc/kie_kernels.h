@@ -75,6 +75,7 @@ struct DecodeArgs {
     int64_t* trace;          // [kTracePhases][kGrid][4] phase timeline (F_TRACE)
     const float* scales;     // fp8 weights: per layer [QKV][Wo][gate/up][down] row scales, then [V] LM
     int32_t layer_scales;    // floats per layer in scales
+    const float* escales;    // fp8 MoE: per (layer, expert) [2F gate/up rows][d down rows] row scales
     int32_t pos0;
     int32_t pending;
     int32_t n_steps;

@@ -30,7 +30,8 @@ def active_weight_bytes(cfg) -> int:
     else:
         ffn = 3 * f * d
     if getattr(cfg, "weight_format", "fp16") == "fp8":
-        rows = cfg.n_layers * (q + 2 * kv + d + 2 * f + d) + cfg.vocab
+        ffn_rows = (cfg.n_experts + cfg.top_k * (2 * f + d)) if cfg.n_experts else 2 * f + d
+        rows = cfg.n_layers * (q + 2 * kv + d + ffn_rows) + cfg.vocab
         return cfg.n_layers * (attn + ffn) + cfg.vocab * d + 4 * rows + 2 * d
     params = cfg.n_layers * (attn + ffn) + cfg.vocab * d + d
     return 2 * params

@@ -245,10 +245,12 @@ class Decoder:
         self._index = self._build_index()
         if self.fp8:
             # quantise every projection once, matrices in parallel (the
-            # element-wise work releases the interpreter lock)
+            # element-wise work releases the interpreter lock); MoE experts
+            # only when they are cached anyway
             from concurrent.futures import ThreadPoolExecutor
             import os
-            names = [n for n in self._index if n != "E" and not n.split(".")[-1].startswith("g_")]
+            names = [n for n in self._index if n != "E" and not n.split(".")[-1].startswith("g_")
+                     and (cache_experts or ".e" not in n)]
             with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
                 list(ex.map(self.w, names))
         L, S, Hkv, hd = cfg.n_layers, cfg.max_seq, cfg.n_kv_heads, cfg.head_dim
@@ -273,7 +275,7 @@ class Decoder:
 
     # the RMSNorm gain folded into each projection of an fp8 model
     _FOLD = {"Wq": "g_attn", "Wk": "g_attn", "Wv": "g_attn", "Wg": "g_ffn", "Wu": "g_ffn", "Wo": None,
-             "Wd": None}
+             "Wd": None, "Wr": "g_ffn"}
 
     def w(self, name: str) -> np.ndarray:
         i = self._index[name]

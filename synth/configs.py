@@ -82,6 +82,11 @@ CONFIGS: Dict[str, object] = {
     "2b_fp8": DecoderConfig(
         name="2b_fp8", n_layers=25, d_model=2560, n_heads=20, n_kv_heads=4, head_dim=128,
         ffn_dim=8192, vocab=32768, prompt_len=128, decode_steps=1024, weight_format="fp8"),
+    # The MoE decoder with router and experts in row-scaled FP8 (E4M3).
+    "moe_fp8": DecoderConfig(
+        name="moe_fp8", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
+        ffn_dim=1024, vocab=32768, n_experts=64, top_k=8, prompt_len=128,
+        decode_steps=512, weight_format="fp8"),
     # Top-8 of 64 experts MoE decoder: only the selected experts are streamed.
     "moe": DecoderConfig(
         name="moe", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,

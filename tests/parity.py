@@ -176,7 +176,10 @@ def moe_request_parity(m, cfg, W, P, n, trials, label, deep=32):
     import synth
     k = cfg.top_k
     compared, ties = 0, 0
-    ref = oracle.Decoder(cfg, W)
+    fp8 = getattr(cfg, "weight_format", "fp16") == "fp8"
+    # fp8: one decoder for everything, its quantised experts cached (quantising
+    # them again for a second decoder would cost minutes)
+    ref = oracle.Decoder(cfg, W, cache_experts=fp8)
     g_first, g_logits, g_exp = m.prefill(P, logits=True, experts=True, router=True)
     device_topk_exact(g_exp, m.last_router, k, label=f"{label} prompt")
     say(f"{label}: oracle batched prefill of {len(P)} tokens with the device's expert sets")
@@ -193,10 +196,13 @@ def moe_request_parity(m, cfg, W, P, n, trials, label, deep=32):
         last64 = oracle.Decoder(cfg, W, dtype=np.float64).prefill_batched(P, expert_overrides=g_exp)[1]
         conditioned_check(g_logits[-1], last, last64, f"{label} prefill")
     compared += 1
-    del ref
+    if fp8:
+        dec = ref
+    else:
+        del ref
+        dec = oracle.Decoder(cfg, W, cache_experts=True)
     K, V = synth.make_kv_prefill(cfg, n_pos=len(P))
     F = synth.make_forced_tokens(cfg, n + 1)
-    dec = oracle.Decoder(cfg, W, cache_experts=True)
     for t in range(trials):
         dec.set_kv(K, V, int(F[t]))
         m.set_kv(K, V, int(F[t]))

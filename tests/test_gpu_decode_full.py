@@ -232,3 +232,18 @@ def test_moe_prompt_routing_and_forced_request(torch_cuda):
     finally:
         m.close()
     assert done >= 8 + 32
+
+
+def test_moe_fp8_prompt_routing_and_forced_request(torch_cuda):
+    """The MoE decoder with router and experts in row-scaled E4M3 (the oracle
+    quantises the fp16 experts itself): the prompt, 4 two-pass trials, 16
+    passes deep in the cache and the 512-pass request, as for fp16."""
+    cfg = synth.get_config("moe_fp8")
+    W = _weights("moe")          # the same fp16 tensors as the moe workload
+    P = synth.make_prompt(cfg)
+    m = _model(cfg, W)
+    try:
+        done, ties = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 4, "moe_fp8", deep=16)
+    finally:
+        m.close()
+    assert done >= 8 + 16

@@ -206,6 +206,18 @@ MOE_CASES = {
 }
 
 
+MOE_CASES.update({
+    # fp8 router and experts: 8 experts, top-2, the router's 8 rows in pairs
+    "moe_fp8_e8k2": synth.DecoderConfig(name="moe_fp8_e8k2", n_layers=2, d_model=512, n_heads=4, n_kv_heads=2,
+                                        head_dim=128, ffn_dim=512, vocab=3000, n_experts=8, top_k=2,
+                                        prompt_len=10, decode_steps=16, gain_sigma=0.2, weight_format="fp8"),
+    # fp8, 64 experts, top-8: the gathered down input is 8192 wide, rows of 1024
+    "moe_fp8_e64k8": synth.DecoderConfig(name="moe_fp8_e64k8", n_layers=2, d_model=1024, n_heads=8,
+                                         n_kv_heads=2, head_dim=128, ffn_dim=1024, vocab=5000, n_experts=64,
+                                         top_k=8, prompt_len=8, decode_steps=12, weight_format="fp8"),
+})
+
+
 @pytest.mark.parametrize("name", list(MOE_CASES))
 def test_moe_teacher_forced_parity(torch_cuda, name):
     cfg = MOE_CASES[name]
