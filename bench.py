@@ -39,12 +39,12 @@ from memory_bandwidth_bound_amd import roofline  # noqa: E402
 PEAK_GBS = roofline.HBM_PEAK_BYTES_PER_S / 1e9
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the decode kernel and its launch are built from
-    (every csrc file but the measurement probes)."""
+def kernel_source_hash(probes: bool = False) -> str:
+    """Hash of the sources a kernel and its launch are built from: every csrc
+    file but the measurement probes, or (probes=True) every csrc file."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "memory_bandwidth_bound_amd", "csrc", "*"))):
-        if os.path.basename(p) == "kie_probes.hip":
+        if os.path.basename(p) == "kie_probes.hip" and not probes:
             continue
         with open(p, "rb") as f:
             h.update(f.read())
@@ -62,7 +62,7 @@ def counters_traffic(name: str):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_source_sha256") != kernel_source_hash(probes=name.endswith("_probe")):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -330,14 +330,14 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="2b",
-                    help="2b (default), 2b_32k, 2b_fp8, moe, tiny, gemv, prefill, or copy (counter calibration)")
+                    help="2b (default), 2b_32k, 2b_fp8, moe, moe_fp8, tiny, gemv, prefill, or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the decoder runs on a single GPU and has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:
         sys.exit("--steps must be >= 1")

@@ -174,6 +174,53 @@ def test_long_context_split_attention(torch_cuda):
     m.close()
 
 
+SPLIT_CASES = {
+    # one query head per KV head, head_dim 128: attention is always split over
+    # positions (matrix-core rounds of 16), here from the first position on,
+    # the prompt run as decode passes
+    "mha_hd128_passes": synth.DecoderConfig(name="mha_hd128_passes", n_layers=2, d_model=512, n_heads=4,
+                                            n_kv_heads=4, head_dim=128, ffn_dim=1024, vocab=2048,
+                                            prompt_len=7, decode_steps=40),
+    # 8 query heads per KV head, head_dim 128, 1147..1160 attended positions:
+    # head mode, then from 1153 on the split over positions with all eight
+    # heads in one matrix-core pass
+    "gqa8_split_hd128": synth.DecoderConfig(name="gqa8_split_hd128", n_layers=2, d_model=1024, n_heads=8,
+                                            n_kv_heads=1, head_dim=128, ffn_dim=1024, vocab=2048,
+                                            prompt_len=1146, decode_steps=14),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_attention_parity(torch_cuda, name):
+    cfg = SPLIT_CASES[name]
+    say(f"case {name}: {cfg}")
+    W = synth.make_weights(cfg)
+    P = synth.make_prompt(cfg)
+    n = cfg.decode_steps
+    first, last, ids, rows = _oracle_run(cfg, W, P, n)
+    m = _model(cfg, W)
+    say(f"{name}: prefill {len(P)} tokens")
+    if name.endswith("_passes"):
+        # every prompt pass, from the first position on, against the oracle's
+        m.set_prefill_mode("passes")
+        dec = oracle.Decoder(cfg, W)
+        prompt_rows = np.stack([dec.step(int(t)) for t in P])
+        g_first, g_logits, _ = m.prefill(P, logits=True)
+        assert g_logits.shape[0] == len(P)
+        check_rows(g_logits, prompt_rows, label=f"{name} prompt passes")
+    else:
+        g_first, g_logits, _ = m.prefill(P, logits=True)
+    check_rows(g_logits[-1:], last[None], label=f"{name} prefill")
+    if oracle.top2_gap(last) > 2e-2:
+        assert g_first == first
+    say(f"{name}: decode {n} teacher-forced")
+    m.rewind(len(P), first)
+    g_ids, g_rows, _ = m.decode(n, force=ids, logits=True)
+    check_rows(g_rows, rows, label=f"{name} decode")
+    m.close()
+    report_worst(name)
+
+
 def test_capacity_and_state_errors(torch_cuda):
     from memory_bandwidth_bound_amd import kie
     cfg = TINY.with_(decode_steps=4)
