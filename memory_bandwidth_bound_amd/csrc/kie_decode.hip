@@ -28,7 +28,9 @@
 // Up to kAttnHeadModeMax attended positions, ATTN runs per query head: its
 // positions in chunks of at most kAttnHeadChunk, one workgroup each, and the
 // first chunk's workgroup folds in the others' states and publishes o itself;
-// COMB then has no work.
+// COMB then has no work. Beyond that, every workgroup takes a chunk of a KV
+// group's positions for all the group's query heads (on the matrix cores for
+// head_dim 128) and COMB merges the chunk states.
 // There is no grid-wide barrier: a phase waits only for the words it reads.
 // A workgroup reads a phase's input only when it has work in that phase; then
 // every overwrite of a buffer it reads depends, through the words the
@@ -103,6 +105,12 @@ __device__ __forceinline__ int attn_split(int c, int items, int* CH) {
 __device__ __forceinline__ bool head_mode(const Dims& D, int c) {
     const int Gq = D.H / D.Hkv;
     return Gq >= 2 && Gq <= kMaxGroup && D.H <= kGrid && c <= kAttnHeadModeMax;
+}
+
+// Split attention on the matrix cores: head_dim 128 outside head mode (the
+// group's at most kMaxGroup query heads fit the 16 columns of an MFMA tile).
+__device__ __forceinline__ bool mfma_attention(const Dims& D, int c) {
+    return D.hd == 128 && !head_mode(D, c);
 }
 
 // Chunks per head in head mode.
@@ -194,7 +202,11 @@ struct Smem {
             alignas(16) uint16_t xlo[kMaxIn];   // lo = fp16(v - hi)
             float part[kMaxRowsWg * kCompute];  // per (row, compute wave) partial dot products
         };
-        float att_o[kCompute * kMaxGroup * 128];   // attention: per compute wave, unnormalised o
+        struct {
+            float att_o[kCompute * kMaxGroup * 128];   // attention: per compute wave, unnormalised o
+            alignas(16) uint16_t att_qh[kMaxGroup * 128];   // matrix-core attention: the queries as
+            alignas(16) uint16_t att_ql[kMaxGroup * 128];   // two fp16 terms (hi, lo = fp16(q - hi))
+        };
     };
     float att_q[kMaxGroup * 128];               // queries of the attention group, pre-scaled (also scratch)
     static_assert(sizeof(uint16_t) * 2 * kMaxIn == sizeof(float) * kMaxIn, "fp32 staging reuses xin and xlo");
@@ -318,17 +330,29 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
         }
         const int head = g * Gq + j;
         if (hm && chunk == 0 && nch > 1) {
-            // head mode: fold in the other chunks' states of this head, then publish o
-            for (int k = 1; k < nch; ++k) {
-                const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + k) * (HD + 2);
-                uint64_t w0, w1, w2, w3;
+            // fold in the other chunks' states of this head, up to four chunks
+            // per trip (all their words polled at once), then publish o
+            for (int k0 = 1; k0 < nch; k0 += 4) {
+                const int kn = nch - k0 < 4 ? nch - k0 : 4;
+                uint64_t wv[4][4];
                 uint32_t spins = 0;
                 while (true) {
-                    w0 = fw_load(pp);
-                    w1 = fw_load(pp + 1);
-                    w2 = fw_load(pp + 2 + dd);
-                    w3 = fw_load(pp + 3 + dd);
-                    const bool ok = fw_ok(w0, id) && fw_ok(w1, id) && fw_ok(w2, id) && fw_ok(w3, id);
+                    bool ok = true;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (u < kn) {
+                            const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + k0 + u) * (HD + 2);
+                            wv[u][0] = fw_load(pp);
+                            wv[u][1] = fw_load(pp + 1);
+                            wv[u][2] = fw_load(pp + 2 + dd);
+                            wv[u][3] = fw_load(pp + 3 + dd);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (u < kn)
+                            ok = ok && fw_ok(wv[u][0], id) && fw_ok(wv[u][1], id) && fw_ok(wv[u][2], id) &&
+                                 fw_ok(wv[u][3], id);
                     if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
                     if (++spins > a.spin) return 1;
                     if ((spins & 63) == 0 && stop_requested(a.status)) return 2;
@@ -336,13 +360,19 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
                     __builtin_amdgcn_s_sleep(KIE_POLL_SLEEP);
 #endif
                 }
-                const float m2 = __builtin_bit_cast(float, fw_val(w0)), l2 = __builtin_bit_cast(float, fw_val(w1));
-                const float Mn = fmaxf(M, m2);
-                const float f1 = __builtin_amdgcn_exp2f(M - Mn), f2 = __builtin_amdgcn_exp2f(m2 - Mn);
-                L = L * f1 + l2 * f2;
-                O0 = O0 * f1 + __builtin_bit_cast(float, fw_val(w2)) * f2;
-                O1 = O1 * f1 + __builtin_bit_cast(float, fw_val(w3)) * f2;
-                M = Mn;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (u < kn) {
+                        const float m2 = __builtin_bit_cast(float, fw_val(wv[u][0]));
+                        const float l2 = __builtin_bit_cast(float, fw_val(wv[u][1]));
+                        const float Mn = fmaxf(M, m2);
+                        const float f1 = __builtin_amdgcn_exp2f(M - Mn), f2 = __builtin_amdgcn_exp2f(m2 - Mn);
+                        L = L * f1 + l2 * f2;
+                        O0 = O0 * f1 + __builtin_bit_cast(float, fw_val(wv[u][2])) * f2;
+                        O1 = O1 * f1 + __builtin_bit_cast(float, fw_val(wv[u][3])) * f2;
+                        M = Mn;
+                    }
+                }
             }
         }
         if (nper == 1 || (hm && chunk == 0)) {
@@ -595,9 +625,17 @@ struct Comm {
         case K_ATTN: {
             const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = wg % D.Hkv;
             const float qs = kLog2e / sqrtf((float)HD);
+            const bool q16 = mfma_attention(D, a.pos0 + it.step + 1);
             gather(a.ex.qkv + (size_t)g * GW, GW, id_of(q - 1), [&](int i, uint32_t v) {
                 if (i < Gq * HD) {
-                    S->att_q[i] = __builtin_bit_cast(float, v) * qs;
+                    const float x = __builtin_bit_cast(float, v) * qs;
+                    if (q16) {
+                        const _Float16 h = (_Float16)x;
+                        S->att_qh[i] = __builtin_bit_cast(uint16_t, h);
+                        S->att_ql[i] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)h));
+                    } else {
+                        S->att_q[i] = x;
+                    }
                 } else if (i < Gq * HD + HD / 2) {
                     const int k = i - Gq * HD;
                     S->att_k[k] = (uint16_t)v;
@@ -865,7 +903,7 @@ struct Comm {
     // Split attention: the workgroup of chunk c of KV group g combines the
     // nper partial states of its slice of the group's output pairs. Every
     // (pair, chunk) state is read in one trip (lanes over pairs x chunks),
-    // staged in LDS, then one lane per pair merges its chunks.
+    // staged in LDS, then a group of lanes per pair merges its chunks.
     __device__ __forceinline__ void combine(int q, int pos) {
         const Dims& D = a.D;
         int CH;
@@ -886,20 +924,39 @@ struct Comm {
             else ok = combine_trip<8>(t0, T, p0, nper, g, Gq, ida, st);
             if (!ok) return;
         }
-        for (int j = lane; j < np; j += 64) {
+        // LP lanes per pair (a power of two, LP * np <= 64 where np allows):
+        // each merges every LP-th chunk, then the LP lanes merge pairwise
+        int LP = 64;
+        while (LP > 1 && LP * np > 64) LP >>= 1;
+        const int sl = lane % LP, PPR = 64 / LP;
+        for (int j0 = 0; j0 < np; j0 += PPR) {
+            const int j = j0 + lane / LP;
             float m = -3.0e38f, l = 0.f, o0 = 0.f, o1 = 0.f;
-            for (int ch = 0; ch < nper; ++ch) {
-                const KIE_LDS float* e = st + (j * nper + ch) * 4;
-                const float M = fmaxf(m, e[0]);
-                const float fo = __builtin_amdgcn_exp2f(m - M), fn = __builtin_amdgcn_exp2f(e[0] - M);
-                l = l * fo + e[1] * fn;
-                o0 = o0 * fo + e[2] * fn;
-                o1 = o1 * fo + e[3] * fn;
+            if (j < np)
+                for (int ch = sl; ch < nper; ch += LP) {
+                    const KIE_LDS float* e = st + (j * nper + ch) * 4;
+                    const float M = fmaxf(m, e[0]);
+                    const float fo = __builtin_amdgcn_exp2f(m - M), fn = __builtin_amdgcn_exp2f(e[0] - M);
+                    l = l * fo + e[1] * fn;
+                    o0 = o0 * fo + e[2] * fn;
+                    o1 = o1 * fo + e[3] * fn;
+                    m = M;
+                }
+            for (int off = 1; off < LP; off <<= 1) {
+                const float m2 = shfl_xor_f(m, off), l2 = shfl_xor_f(l, off);
+                const float a0 = shfl_xor_f(o0, off), a1 = shfl_xor_f(o1, off);
+                const float M = fmaxf(m, m2);
+                const float fo = __builtin_amdgcn_exp2f(m - M), fn = __builtin_amdgcn_exp2f(m2 - M);
+                l = l * fo + l2 * fn;
+                o0 = o0 * fo + a0 * fn;
+                o1 = o1 * fo + a1 * fn;
                 m = M;
             }
-            const int idx = 2 * (p0 + j), head = g * Gq + idx / HD, dd = idx % HD;
-            fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, o0 / l), id_of(q));
-            fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, o1 / l), id_of(q));
+            if (j < np && sl == 0) {
+                const int idx = 2 * (p0 + j), head = g * Gq + idx / HD, dd = idx % HD;
+                fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, o0 / l), id_of(q));
+                fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, o1 / l), id_of(q));
+            }
         }
     }
 
@@ -960,6 +1017,33 @@ struct WaveGeo {
 };
 
 typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource over one KV head's cache rows of one layer: loads past
+// `bytes` return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const uint16_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset off, device scope (sc1: rows appended by other
+// workgroups earlier in the launch are seen); the compiler tracks the load.
+__device__ __forceinline__ uint4 kv_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+// Half t (0..7) of four 16-byte value rows, packed as the eight fp16 k slots of
+// an MFMA operand: rows 0..3, then the same four again.
+__device__ __forceinline__ h8_t v_col(const uint4 (&v)[4], int t) {
+    uint32_t d[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t x = (t >> 1) == 0 ? v[r].x : (t >> 1) == 1 ? v[r].y : (t >> 1) == 2 ? v[r].z : v[r].w;
+        d[r] = (t & 1) ? (x >> 16) : (x & 0xffffu);
+    }
+    const uint32_t lo = d[0] | (d[1] << 16), hi = d[2] | (d[3] << 16);
+    typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+    const u4_t u = {lo, hi, lo, hi};
+    return __builtin_bit_cast(h8_t, u);
+}
 
 // One fp8 unit against 8 fp32 inputs: the lane's 16 bytes are 8 E4M3 weights
 // of row a then 8 of row b (the same 8 columns); each is converted exactly to
@@ -1194,8 +1278,10 @@ struct Compute {
         } else if (kind == K_ATTN && !stop) {
             const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
             // register arrays sized for the group (1, 2, 4 or 5 heads; 6 to 8
-            // heads in two passes over the positions)
-            if (G == 1) attention<1>(l, pos);
+            // heads in two passes over the positions); head_dim 128 on the
+            // matrix cores
+            if constexpr (HD == 128) attention_mfma(l, pos);   // mfma_attention() holds here
+            else if (G == 1) attention<1>(l, pos);
             else if (G == 2) attention<2>(l, pos);
             else if (G <= 4) attention<4>(l, pos);
             else if (G == 5) attention<5>(l, pos);
@@ -1549,6 +1635,141 @@ struct Compute {
                 gptr(a.trace)[((size_t)(kTracePhases - 8 + w) * kGrid + wg) * 4 + i] = (int64_t)tacc[i];
 #endif
 #undef KIE_T
+    }
+
+    // Split attention on the matrix cores (head_dim 128, at most 8 query heads
+    // per KV head, so they fit the 16 columns): this workgroup's chunk of a KV
+    // group's positions. Each compute wave takes every 7th round of 16
+    // positions of the chunk. The scores come out transposed,
+    // S^T = K Q^T on v_mfma_f32_16x16x32_f16: the keys are the A operand,
+    // 16 contiguous bytes of a cache row per lane and step, the queries the B
+    // operand as two fp16 terms (hi, lo) in two products, read from LDS. Lane l then holds
+    // the scores of head l%16 at positions 4(l/16) .. 4(l/16)+3, which is the
+    // B operand of O^T = V^T P^T with P as two fp16 terms (k slots: the four
+    // positions' hi terms, then their lo terms, against the same four values
+    // twice). Row i of output block t (t = 0..7) is dimension 8i + t, so the
+    // A operand reads 16 contiguous bytes of each value row too. Each lane
+    // keeps the online-softmax state of its head (the maximum, equal on the
+    // four lanes of a head, and a partial sum) and O^T block t, whose rows
+    // 4(l/16)+r are dimensions 8(4(l/16)+r) + t. The next round's keys and
+    // values are loaded while a round is computed.
+    __device__ __forceinline__ void attention_mfma(int layer, int pos) {
+        static_assert(HD == 128, "the operand layouts are for head_dim 128");
+        const Dims& D = a.D;
+        int CH;
+        const int c = pos + 1;
+        attn_split(c, a.items_per_head, &CH);
+        const int Gq = D.H / D.Hkv;
+        const int g = wg % D.Hkv, chunk = wg / D.Hkv;
+        const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
+        const int li = lane & 15, lg = lane >> 4;
+        // B operands of the scores: the queries' two fp16 terms, staged in LDS
+        // by the communication wave (columns past the group read zeros)
+        const int qrow = (li < Gq ? li : 0) * HD + 8 * lg;
+        const bool qon = li < Gq;
+        auto qop = [&](const KIE_LDS uint16_t* base, int s) {
+            // read in every round, not held across rounds: the opaque copy of
+            // the row offset keeps the compiler from hoisting the reads (32
+            // registers) out of the loop
+            int r = qrow;
+            asm volatile("" : "+v"(r));
+            const uint4 u = lds_ld16(base + r + 32 * s);
+            return __builtin_bit_cast(h8_t, qon ? u : make_uint4(0u, 0u, 0u, 0u));
+        };
+        const size_t kvoff = ((size_t)layer * D.Hkv + g) * D.max_seq * HD;
+        const uint32_t kvbytes = (uint32_t)D.max_seq * HD * 2u;
+        const __amdgpu_buffer_rsrc_t kr = kv_rsrc(a.kc + kvoff, kvbytes), vr = kv_rsrc(a.vc + kvoff, kvbytes);
+        float m = -3.0e38f, ls = 0.f;
+        f4_t o[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+        constexpr int kStep = 16 * kCompute;
+        // rows past the chunk (padding, and every row of a round past its end)
+        // and at or past pos (the new position, whose row may not be visible
+        // yet) are read from row 0 and replaced or masked below
+        auto issue = [&](int bb, uint4 (&kx)[4], uint4 (&vx)[4]) {
+            const int pk = bb + li, sk = (pk < pos && pk < p1) ? pk : 0;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kx[s] = kv_load(kr, (uint32_t)(sk * HD + 32 * s + 8 * lg) * 2u);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pv = bb + 4 * lg + r, sv = (pv < pos && pv < p1) ? pv : 0;
+                vx[r] = kv_load(vr, (uint32_t)(sv * HD + 8 * li) * 2u);
+            }
+        };
+        auto round = [&](int b, uint4 (&kw)[4], uint4 (&vw)[4]) {
+            if (b + 16 > pos) {
+                // this round holds the new position: its key and value from LDS
+                // (and every padding row too, so that all values are finite)
+                if (b + li >= pos)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) kw[s] = lds_ld16(S->att_k + 32 * s + 8 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (b + 4 * lg + r >= pos) vw[r] = lds_ld16(S->att_v + 8 * li);
+            }
+            f4_t sc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const h8_t kh = __builtin_bit_cast(h8_t, kw[s]);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop(S->att_qh, s), sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop(S->att_ql, s), sc, 0, 0, 0);
+            }
+            float sr[4], mx = m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sr[r] = (b + 4 * lg + r < p1) ? sc[r] : -3.0e38f;
+                mx = fmaxf(mx, sr[r]);
+            }
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const float cr = __builtin_amdgcn_exp2f(m - mx);
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = sr[r] > -1.0e38f ? __builtin_amdgcn_exp2f(sr[r] - mx) : 0.f;
+            ls = ls * cr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            m = mx;
+            if (__builtin_amdgcn_ballot_w64(cr != 1.f) != 0)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) o[t] *= cr;
+            h8_t pb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const _Float16 h = (_Float16)pr[r];
+                pb[r] = h;
+                pb[4 + r] = (_Float16)(pr[r] - (float)h);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_col(vw, t), pb, o[t], 0, 0, 0);
+        };
+        // two rounds of keys and values in flight per wave: the round being
+        // computed and the next one (issued unconditionally, past the chunk
+        // from row 0, so every wait the compiler places is vmcnt(8))
+        uint4 ka[4], va[4], kb[4], vb[4];
+        int b = p0 + 16 * w;
+        issue(b, ka, va);
+        while (b < p1) {
+            issue(b + kStep, kb, vb);
+            round(b, ka, va);
+            b += kStep;
+            if (b >= p1) break;
+            issue(b + kStep, ka, va);
+            round(b, kb, vb);
+            b += kStep;
+        }
+        ls += shfl_xor_f(ls, 16);
+        ls += shfl_xor_f(ls, 32);
+        if (li < Gq) {
+            KIE_LDS float* ob = S->att_o + (w * kMaxGroup + li) * HD;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) ob[8 * (4 * lg + r) + t] = o[t][r];
+            if (lg == 0) {
+                S->att_ml[(w * kMaxGroup + li) * 2] = m;
+                S->att_ml[(w * kMaxGroup + li) * 2 + 1] = ls;
+            }
+        }
     }
 
     // Attention of this workgroup's chunk: each compute wave takes every 7th

@@ -54,7 +54,8 @@ CASES = {
                                              prompt_len=760, decode_steps=16),
     # 4 query heads per KV head, 1137..1168 attended positions: three chunks per
     # query head, then the launch crosses the 1152-position limit of work items
-    # per query head and goes on with the split over positions and its combine
+    # per query head and goes on with the split over positions (matrix cores)
+    # and its combine
     "gqa4_long_hd128": synth.DecoderConfig(name="gqa4_long_hd128", n_layers=2, d_model=512, n_heads=4,
                                            n_kv_heads=1, head_dim=128, ffn_dim=1024, vocab=2048,
                                            prompt_len=1136, decode_steps=32),
