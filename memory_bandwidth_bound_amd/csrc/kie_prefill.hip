@@ -2,7 +2,7 @@
 //
 // Decode at batch 1 is a matrix-vector product; a prompt of P tokens is not:
 // its projections multiply P activation rows by every weight row, a dense
-// contraction, so they run here as tiled GEMMs on v_mfma_f32_32x32x8_f16
+// contraction, so they run here as tiled GEMMs on v_mfma_f32_32x32x16_f16
 // (fp16 x fp16 -> fp32). The pages measure decode, not prefill (paper-digest.app
 // digest, "Core Mechanics": time-to-first-token is outside the metric); this
 // path exists so that a prompt is not P sequential decode passes.
@@ -24,7 +24,7 @@
 
 namespace kie {
 
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------------ GEMM --
@@ -32,7 +32,7 @@ typedef float f16x_t __attribute__((ext_vector_type(16)));
 // lda) and m < M weight rows (fp16, K each) found by the row map.
 constexpr int kTile = 64;          // rows of A and of W per workgroup
 constexpr int kTk = 64;            // K per step
-constexpr int kLdsStride = kTk + 4;   // halves per LDS row (padding spreads the banks)
+constexpr int kLdsStride = kTk + 8;   // halves per LDS row (16-byte rows; padding spreads the banks)
 
 __device__ __forceinline__ const uint16_t* row_addr(const GemmRows& R, int m) {
     if (R.dense) return (const uint16_t*)(R.base + (size_t)m * R.K * 2);
@@ -48,30 +48,32 @@ __device__ __forceinline__ const uint16_t* row_addr(const GemmRows& R, int m) {
 
 // One step's share of a thread: 16 consecutive k of one row of A (fp32) and
 // of one row of W (fp16). Thread t loads row t / 4 at k offset 16 (t % 4).
+// Rows past n (A) or M (W) load the last valid row instead: they only feed
+// outputs that are not stored, and the loads need no branch, which keeps the
+// compiler's waits exact across the pipelined steps.
 struct GemmStage {
     float a[16];
     uint4 b[2];
 };
 
-__device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const uint16_t* bp, bool arow, bool brow,
-                                          int k0) {
-    if (arow) {
+__device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const uint16_t* bp, int k0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 u = *(const float4*)(ap + k0 + 4 * q);
-            st.a[4 * q] = u.x;
-            st.a[4 * q + 1] = u.y;
-            st.a[4 * q + 2] = u.z;
-            st.a[4 * q + 3] = u.w;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st.a[e] = 0.f;
+    for (int q = 0; q < 4; ++q) {
+        const float4 u = *(const float4*)(ap + k0 + 4 * q);
+        st.a[4 * q] = u.x;
+        st.a[4 * q + 1] = u.y;
+        st.a[4 * q + 2] = u.z;
+        st.a[4 * q + 3] = u.w;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) st.b[q] = brow ? *(const uint4*)(bp + k0 + 8 * q) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 2; ++q) st.b[q] = *(const uint4*)(bp + k0 + 8 * q);
 }
 
+// Three K steps are in flight per thread (registers) while a fourth is
+// multiplied from LDS: a step's 24 KiB per workgroup take about one memory
+// latency to arrive, so one step in flight left the matrix cores idle most
+// of the time. Loads past the last step re-read the last step (in bounds,
+// unused), so every wait the compiler places covers exactly the step needed.
 __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict__ A, int lda, int n, GemmRows R,
                                                         float* __restrict__ Y, int ldy) {
     __shared__ __attribute__((aligned(16))) _Float16 ahi[kTile * kLdsStride];
@@ -81,37 +83,58 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict_
     const int m0 = blockIdx.x * kTile, p0 = blockIdx.y * kTile;
     const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's 32 x 32 sub-tile
     const int lr = tid >> 2, lk = (tid & 3) * 16;
-    const bool arow = p0 + lr < n, brow = m0 + lr < R.M;
-    const float* ap = A + (size_t)(p0 + lr) * lda + lk;
-    const uint16_t* bp = brow ? row_addr(R, m0 + lr) + lk : nullptr;
+    const int pa = p0 + lr < n ? p0 + lr : n - 1, mb = m0 + lr < R.M ? m0 + lr : R.M - 1;
+    const float* ap = A + (size_t)pa * lda + lk;
+    const uint16_t* bp = row_addr(R, mb) + lk;
+    const int klast = R.K - kTk;
     f16x_t acc = {};
-    GemmStage st;
-    gemm_load(st, ap, bp, arow, brow, 0);
-    for (int k0 = 0; k0 < R.K; k0 += kTk) {
+    auto stage_in = [&](const GemmStage& st) {
         __syncthreads();   // the previous step's LDS reads are done
+        h8_t h[2], l[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const _Float16 h = (_Float16)st.a[e];
-            ahi[lr * kLdsStride + lk + e] = h;
-            alo[lr * kLdsStride + lk + e] = (_Float16)(st.a[e] - (float)h);
+            const _Float16 x = (_Float16)st.a[e];
+            h[e >> 3][e & 7] = x;
+            l[e >> 3][e & 7] = (_Float16)(st.a[e] - (float)x);
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            *(uint2*)&bt[lr * kLdsStride + lk + 8 * q] = make_uint2(st.b[q].x, st.b[q].y);
-            *(uint2*)&bt[lr * kLdsStride + lk + 8 * q + 4] = make_uint2(st.b[q].z, st.b[q].w);
+            *(h8_t*)&ahi[lr * kLdsStride + lk + 8 * q] = h[q];
+            *(h8_t*)&alo[lr * kLdsStride + lk + 8 * q] = l[q];
+            *(uint4*)&bt[lr * kLdsStride + lk + 8 * q] = st.b[q];
         }
         __syncthreads();
-        if (k0 + kTk < R.K) gemm_load(st, ap, bp, arow, brow, k0 + kTk);   // next step's loads fly meanwhile
+    };
+    auto multiply = [&]() {
 #pragma unroll
-        for (int kk = 0; kk < kTk; kk += 8) {
-            // A[i][k]: lane i + 32 (k / 4) holds k % 4; B[k][j]: lane j + 32 (k / 4)
-            const int kq = kk + 4 * (lane >> 5);
-            const h4_t a_h = *(const h4_t*)&ahi[(wr + (lane & 31)) * kLdsStride + kq];
-            const h4_t a_l = *(const h4_t*)&alo[(wr + (lane & 31)) * kLdsStride + kq];
-            const h4_t b = *(const h4_t*)&bt[(wc + (lane & 31)) * kLdsStride + kq];
-            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_h, b, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(a_l, b, acc, 0, 0, 0);
+        for (int kk = 0; kk < kTk; kk += 16) {
+            // v_mfma_f32_32x32x16_f16: A[i][k] lane i + 32 (k / 8) holds k % 8;
+            // B[k][j] lane j + 32 (k / 8)
+            const int kq = kk + 8 * (lane >> 5);
+            const h8_t a_h = *(const h8_t*)&ahi[(wr + (lane & 31)) * kLdsStride + kq];
+            const h8_t a_l = *(const h8_t*)&alo[(wr + (lane & 31)) * kLdsStride + kq];
+            const h8_t b = *(const h8_t*)&bt[(wc + (lane & 31)) * kLdsStride + kq];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b, acc, 0, 0, 0);
         }
+    };
+    auto kat = [&](int k) { return k < klast ? k : klast; };
+    GemmStage s0, s1, s2;
+    gemm_load(s0, ap, bp, 0);
+    gemm_load(s1, ap, bp, kat(kTk));
+    gemm_load(s2, ap, bp, kat(2 * kTk));
+    for (int k0 = 0; k0 < R.K; k0 += 3 * kTk) {
+        stage_in(s0);
+        gemm_load(s0, ap, bp, kat(k0 + 3 * kTk));
+        multiply();
+        if (k0 + kTk >= R.K) break;
+        stage_in(s1);
+        gemm_load(s1, ap, bp, kat(k0 + 4 * kTk));
+        multiply();
+        if (k0 + 2 * kTk >= R.K) break;
+        stage_in(s2);
+        gemm_load(s2, ap, bp, kat(k0 + 5 * kTk));
+        multiply();
     }
     // D[i][j]: lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8)
 #pragma unroll
