@@ -327,7 +327,10 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         HIP_TRY(m, hipMemcpyAsync(m->ws + L.off_args, &a, sizeof(a), hipMemcpyHostToDevice, m->stream));
         __atomic_store_n(m->hstatus, 0u, __ATOMIC_SEQ_CST);   // the previous launch has ended
         HIP_TRY(m, hipEventRecord(m->ev0, m->stream));
-        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w8 != 0, skip_lm, kGrid,
+        // the variant with the matrix-core split attention only where a pass
+        // of this launch (the last attends pos0 + nc positions) leaves head mode
+        const bool ms = D.hd == 128 && !head_mode_at(D, a.pos0 + nc);
+        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w8 != 0, ms, skip_lm, kGrid,
                                  m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
         // Host watchdog: poll the launch's end event against a wall-clock

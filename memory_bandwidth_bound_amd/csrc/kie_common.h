@@ -83,6 +83,14 @@ KIE_HD RowSplit split_rows(int M, int gran, int nwg, int w) {
 
 KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Head mode of attention at c attended positions (2 to 8 query heads per KV
+// head, at most kAttnHeadModeMax positions): one work item per (query head,
+// chunk). Beyond it, the split over positions.
+KIE_HD bool head_mode_at(const Dims& D, int c) {
+    const int Gq = D.H / D.Hkv;
+    return Gq >= 2 && Gq <= kMaxGroup && D.H <= kGrid && c <= kAttnHeadModeMax;
+}
+
 // Units of a slab of nrows rows of K fp16 each, padded to whole units.
 KIE_HD int slab_units(int nrows, int K) { return ceil_div(nrows * K, kUnitHalves); }
 // The same for the weight format of D (fp8 rows take one byte per weight and

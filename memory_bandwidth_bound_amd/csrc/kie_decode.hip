@@ -102,15 +102,14 @@ __device__ __forceinline__ int attn_split(int c, int items, int* CH) {
 // itself: no combine phase over the grid. (Configurations hold at most 128
 // query heads, since n_heads * head_dim is at most 8192 and head_dim at least
 // 64, so the items fit the grid.)
-__device__ __forceinline__ bool head_mode(const Dims& D, int c) {
-    const int Gq = D.H / D.Hkv;
-    return Gq >= 2 && Gq <= kMaxGroup && D.H <= kGrid && c <= kAttnHeadModeMax;
-}
+__device__ __forceinline__ bool head_mode(const Dims& D, int c) { return head_mode_at(D, c); }
 
 // Split attention on the matrix cores: head_dim 128 outside head mode (the
-// group's at most kMaxGroup query heads fit the 16 columns of an MFMA tile).
+// group's at most kMaxGroup query heads fit the 16 columns of an MFMA tile),
+// in the kernel variant built with it (MS; see launch_decode).
+template <bool MS>
 __device__ __forceinline__ bool mfma_attention(const Dims& D, int c) {
-    return D.hd == 128 && !head_mode(D, c);
+    return MS && D.hd == 128 && !head_mode(D, c);
 }
 
 // Chunks per head in head mode.
@@ -395,7 +394,7 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
 // ------------------------------------------------------------------------
 // Communication wave.
 // ------------------------------------------------------------------------
-template <int HD, bool W8>
+template <int HD, bool W8, bool MS>
 struct Comm {
     const DecodeArgs& a;
     KIE_LDS Smem* S;
@@ -625,7 +624,7 @@ struct Comm {
         case K_ATTN: {
             const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = wg % D.Hkv;
             const float qs = kLog2e / sqrtf((float)HD);
-            const bool q16 = mfma_attention(D, a.pos0 + it.step + 1);
+            const bool q16 = mfma_attention<MS>(D, a.pos0 + it.step + 1);
             gather(a.ex.qkv + (size_t)g * GW, GW, id_of(q - 1), [&](int i, uint32_t v) {
                 if (i < Gq * HD) {
                     const float x = __builtin_bit_cast(float, v) * qs;
@@ -1090,7 +1089,7 @@ __device__ __forceinline__ void load_xf(KIE_LDS Smem* S, int off, float (&x)[8])
     x[7] = __builtin_bit_cast(float, u1.w);
 }
 
-template <int HD, bool W8>
+template <int HD, bool W8, bool MS>
 struct Compute {
     const DecodeArgs& a;
     KIE_LDS Smem* S;
@@ -1280,7 +1279,7 @@ struct Compute {
             // register arrays sized for the group (1, 2, 4 or 5 heads; 6 to 8
             // heads in two passes over the positions); head_dim 128 on the
             // matrix cores
-            if constexpr (HD == 128) attention_mfma(l, pos);   // mfma_attention() holds here
+            if constexpr (HD == 128 && MS) attention_mfma(l, pos);   // mfma_attention() holds here
             else if (G == 1) attention<1>(l, pos);
             else if (G == 2) attention<2>(l, pos);
             else if (G <= 4) attention<4>(l, pos);
@@ -1907,7 +1906,7 @@ struct Compute {
     }
 };
 
-template <int HD, bool W8>
+template <int HD, bool W8, bool MS>
 __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WgPlan W;
@@ -1920,40 +1919,45 @@ __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S
     }
     __syncthreads();
     if (wave == 0) {
-        Comm<HD, W8> cm(a, S, W);
+        Comm<HD, W8, MS> cm(a, S, W);
         cm.run();
     } else {
-        Compute<HD, W8> cp(a, S, wave - 1);
+        Compute<HD, W8, MS> cp(a, S, wave - 1);
         cp.run();
     }
 }
 
 // Two symbols for the same code, so that profiles keep the prompt's passes
 // apart from the generation requests.
-template <int HD, bool W8>
+template <int HD, bool W8, bool MS>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD, W8>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, W8, MS>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
-template <int HD, bool W8>
+template <int HD, bool W8, bool MS>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD, W8>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, W8, MS>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
 // The fp8-weight kernels are built for head_dim 128 only (the decoders whose
 // widths fp8 needs: every projection width a multiple of 512).
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool prefill, int grid, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool ms, bool prefill, int grid,
+                         hipStream_t s) {
     void* args[] = {&dev_args};
+    if ((w8 || ms) && hd != 128) return hipErrorInvalidValue;
+    // [prefill][hd 128][w8][ms]; hd 64 has neither FP8 nor the matrix-core split
     const void* fn;
-    if (w8 && hd != 128) return hipErrorInvalidValue;
-    if (prefill)
-        fn = w8 ? (const void*)prefill_kernel<128, true>
-                : (hd == 64 ? (const void*)prefill_kernel<64, false> : (const void*)prefill_kernel<128, false>);
-    else
-        fn = w8 ? (const void*)decode_kernel<128, true>
-                : (hd == 64 ? (const void*)decode_kernel<64, false> : (const void*)decode_kernel<128, false>);
+    if (hd == 64) {
+        fn = prefill ? (const void*)prefill_kernel<64, false, false> : (const void*)decode_kernel<64, false, false>;
+    } else if (prefill) {
+        fn = w8 ? (ms ? (const void*)prefill_kernel<128, true, true> : (const void*)prefill_kernel<128, true, false>)
+                : (ms ? (const void*)prefill_kernel<128, false, true> : (const void*)prefill_kernel<128, false, false>);
+    } else {
+        fn = w8 ? (ms ? (const void*)decode_kernel<128, true, true> : (const void*)decode_kernel<128, true, false>)
+                : (ms ? (const void*)decode_kernel<128, false, true> : (const void*)decode_kernel<128, false, false>);
+    }
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 

@@ -128,7 +128,13 @@ inline int phases_per_layer(const Dims& D) { return D.E ? 7 : 6; }
 inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2; }
 
 // Launchers. dev_args: the argument block already copied to device memory.
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool prefill, int grid, hipStream_t s);
+// The persistent kernel comes in variants: hd 64 or 128, fp16 or FP8 weights
+// (w8), and, for hd 128, with the matrix-core split attention (ms) or
+// without: the host takes ms only for launches with a pass beyond head mode
+// (head_mode_at), since carrying that code costs the short-context passes
+// about 1%.
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool ms, bool prefill, int grid,
+                         hipStream_t s);
 // Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
 // per workgroup, a contiguous range of units per wave, row sums added into y,
 // which the caller zeroes). Needs K <= kMaxInput.
