@@ -40,11 +40,12 @@ PEAK_GBS = roofline.HBM_PEAK_BYTES_PER_S / 1e9
 
 
 def kernel_source_hash(probes: bool = False) -> str:
-    """Hash of the sources a kernel and its launch are built from: every csrc
-    file but the measurement probes, or (probes=True) every csrc file."""
+    """Hash of the sources a kernel and its launch are built from: for the
+    decode kernel every csrc file but the measurement probes and the batched
+    prefill; with probes=True every csrc file."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "memory_bandwidth_bound_amd", "csrc", "*"))):
-        if os.path.basename(p) == "kie_probes.hip" and not probes:
+        if os.path.basename(p) in ("kie_probes.hip", "kie_prefill.hip") and not probes:
             continue
         with open(p, "rb") as f:
             h.update(f.read())
@@ -120,7 +121,9 @@ def cpu_baseline_decode(cfg, W, prompt, target_s: float):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{n} greedy decode passes of the {cfg.name} decoder at positions "
-                      f"{start}..{start + n - 1} (numpy fp32 on fp16 weights), after one untimed pass; "
+                      f"{start}..{start + n - 1} (numpy fp32 on the "
+                      f"{'E4M3 weights (dequantised)' if getattr(cfg, 'weight_format', 'fp16') == 'fp8' else 'fp16 weights'}"
+                      f"), after one untimed pass; "
                       f"host os.cpu_count()={os.cpu_count()}"}
 
 
