@@ -80,13 +80,19 @@ def blas_threads() -> int:
         return os.cpu_count() or 1
 
 
+WEIGHT_DESC = {"fp16": "fp16 weights", "fp8": "E4M3 weights (dequantised)", "fp4": "E2M1 weights (dequantised)"}
+DTYPE = {"fp16": "fp16", "fp8": "fp8-e4m3 weights, fp32 math", "fp4": "fp4-e2m1 weights, fp32 math"}
+
+
 def describe(cfg) -> str:
     s = (f"{cfg.name} decoder: {cfg.n_layers} layers, d_model {cfg.d_model}, {cfg.n_heads} query / "
          f"{cfg.n_kv_heads} KV heads x {cfg.head_dim}, SwiGLU {cfg.ffn_dim}")
     if cfg.n_experts:
         s += f" x {cfg.n_experts} experts (top-{cfg.top_k})"
-    if getattr(cfg, "weight_format", "fp16") == "fp8":
-        s += (f", vocab {cfg.vocab}, weights N(0,{cfg.weight_sigma}) held as FP8 E4M3 with one fp32 scale per row "
+    wf = getattr(cfg, "weight_format", "fp16")
+    if wf in ("fp8", "fp4"):
+        name = "FP8 E4M3" if wf == "fp8" else "FP4 E2M1"
+        s += (f", vocab {cfg.vocab}, weights N(0,{cfg.weight_sigma}) held as {name} with one fp32 scale per row "
               f"(quantised at load; embedding fp16); batch 1, ")
     else:
         s += f", vocab {cfg.vocab}, fp16 weights N(0,{cfg.weight_sigma}); batch 1, "
@@ -122,7 +128,7 @@ def cpu_baseline_decode(cfg, W, prompt, target_s: float):
     return {"value": n / dt, "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{n} greedy decode passes of the {cfg.name} decoder at positions "
                       f"{start}..{start + n - 1} (numpy fp32 on the "
-                      f"{'E4M3 weights (dequantised)' if getattr(cfg, 'weight_format', 'fp16') == 'fp8' else 'fp16 weights'}"
+                      f"{WEIGHT_DESC.get(getattr(cfg, 'weight_format', 'fp16'), 'fp16 weights')}"
                       f"), after one untimed pass; "
                       f"host os.cpu_count()={os.cpu_count()}"}
 
@@ -174,7 +180,7 @@ def bench_decode(cfg, args):
         "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8-e4m3 weights, fp32 math" if getattr(cfg, "weight_format", "fp16") == "fp8" else "fp16",
+        "dtype": DTYPE[getattr(cfg, "weight_format", "fp16")],
         "data": "synthetic",
         "config": {"workload": describe(cfg), "global_batch": 1, "seq_len": pos0 + n,
                    "decode_tokens_per_step": n, "parallelism": "single GPU, one persistent launch per request"},
@@ -333,7 +339,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="2b",
-                    help="2b (default), 2b_32k, 2b_fp8, moe, moe_fp8, tiny, gemv, prefill, or copy (counter calibration)")
+                    help="2b (default), 2b_32k, 2b_fp8, 2b_fp4, moe, moe_fp8, tiny, gemv, prefill, "
+                         "or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")

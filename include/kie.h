@@ -76,6 +76,14 @@ enum {
  *    (g_ffn folded) and every expert's Wg, Wu (g_ffn folded) and Wd the same
  *    way. head_dim 128 only; d_model, ffn_dim and n_heads*head_dim multiples
  *    of 512, vocab and n_experts even.
+ *  KIE_WEIGHTS_FP4:  OCP FP4 E2M1 (the element type of the OCP microscaling
+ *    formats: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one fp32 scale per
+ *    row, the FP4 of the same passage, quantized like FP8 with 6 in place of
+ *    448: s = fp32(max_k |v_k| / 6) (1 for an all-zero row), q_k = E2M1
+ *    nearest to fp32(v_k / s), ties to the even code, saturating at 6
+ *    (kie_quantize_e2m1_rows). Dense models only (no MoE); head_dim 128;
+ *    d_model, ffn_dim and n_heads*head_dim multiples of 512; vocab a multiple
+ *    of 4.
  */
 typedef struct kie_config {
     int32_t n_layers;
@@ -90,10 +98,10 @@ typedef struct kie_config {
     float rms_eps;       /* RMSNorm: x / sqrt(mean(x^2) + eps) * g */
     float rope_theta;    /* rotary base; pairs (i, i + head_dim/2) */
     int32_t max_seq;     /* KV-cache capacity in positions */
-    int32_t weight_format;   /* KIE_WEIGHTS_FP16 (0) or KIE_WEIGHTS_FP8 (1) */
+    int32_t weight_format;   /* KIE_WEIGHTS_FP16 (0), KIE_WEIGHTS_FP8 (1) or KIE_WEIGHTS_FP4 (2) */
 } kie_config;
 
-enum { KIE_WEIGHTS_FP16 = 0, KIE_WEIGHTS_FP8 = 1 };
+enum { KIE_WEIGHTS_FP16 = 0, KIE_WEIGHTS_FP8 = 1, KIE_WEIGHTS_FP4 = 2 };
 
 /*
  * The library's FP8 quantizer, as kie_load applies it (host only, no device
@@ -106,6 +114,18 @@ enum { KIE_WEIGHTS_FP16 = 0, KIE_WEIGHTS_FP8 = 1 };
  * Returns KIE_OK or KIE_ERR_ARG.
  */
 int kie_quantize_e4m3_rows(const void* w_fp16, const void* gain_fp16, int32_t rows, int32_t K, uint8_t* q,
+                           float* scales);
+
+/*
+ * The library's FP4 quantizer, as kie_load applies it (host only, no device
+ * call): rows x K fp16 weights w and an optional fp16 gain [K] (NULL = 1) ->
+ * q [rows][K] E2M1 codes (0..15, one per byte; bit 3 is the sign) and scales
+ * [rows] fp32, with s = fp32(max_k |fp32(w_k) * fp32(g_k)| / 6) (1 for an
+ * all-zero row) and q_k the E2M1 code nearest to fp32(fp32(w_k) * fp32(g_k) /
+ * s), ties to the even code, saturating at 6; a negative value that rounds to
+ * zero keeps its sign (code 8). Returns KIE_OK or KIE_ERR_ARG.
+ */
+int kie_quantize_e2m1_rows(const void* w_fp16, const void* gain_fp16, int32_t rows, int32_t K, uint8_t* q,
                            float* scales);
 
 /*
@@ -350,6 +370,14 @@ int kie_gemm_probe(const float* A, const void* W, float* Y, int32_t n, int32_t M
  * E4M3 conversion (the one the fp8 GEMVs use) gives each code 0..255. Uses the
  * library's own 64 KiB device array (no allocation); waits for the launch. */
 int kie_e4m3_table_probe(float* out256, void* hip_stream);
+
+/* FP4 conversion probe: out64 (host) receives what the device's E2M1
+ * conversion (the one the fp4 GEMVs use, scale 1) gives for eight 32-bit
+ * words: word l (l < 8) holds in byte b the codes (2l + b) % 16 (low nibble)
+ * and (2l + b + 8) % 16 (high nibble); out64[8 l + 2 b] and [8 l + 2 b + 1]
+ * are byte b's low- and high-nibble values. Uses the library's own 64 KiB
+ * device array (no allocation); waits for the launch. */
+int kie_e2m1_table_probe(float* out64, void* hip_stream);
 
 /* XCD placement probe: out_xcd (host, [256]) receives the XCD (0..7 on
  * MI355X) that workgroup w of a 256-workgroup cooperative launch ran on, read

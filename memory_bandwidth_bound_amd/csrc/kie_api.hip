@@ -330,8 +330,8 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         // the variant with the matrix-core split attention only where a pass
         // of this launch (the last attends pos0 + nc positions) leaves head mode
         const bool ms = D.hd == 128 && !head_mode_at(D, a.pos0 + nc);
-        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w8 != 0, ms, skip_lm, kGrid,
-                                 m->stream));
+        HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w4 ? 2 : D.w8 ? 1 : 0, ms,
+                                 skip_lm, kGrid, m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
         // Host watchdog: poll the launch's end event against a wall-clock
         // limit. Past it, set the status word the kernel's long waits read
@@ -589,6 +589,15 @@ int kie_quantize_e4m3_rows(const void* w_fp16, const void* gain_fp16, int32_t ro
     return KIE_OK;
 }
 
+int kie_quantize_e2m1_rows(const void* w_fp16, const void* gain_fp16, int32_t rows, int32_t K, uint8_t* q,
+                           float* scales) {
+    if (!w_fp16 || !q || !scales || rows < 0 || K < 1) return fail(nullptr, KIE_ERR_ARG, "bad argument");
+    const uint16_t* w = (const uint16_t*)w_fp16;
+    for (int r = 0; r < rows; ++r)
+        quantize_row_e2m1(w + (size_t)r * K, (const uint16_t*)gain_fp16, K, q + (size_t)r * K, scales + r);
+    return KIE_OK;
+}
+
 int kie_set_prefill_mode(kie_model* m, int32_t mode) {
     if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
     if (mode != KIE_PREFILL_AUTO && mode != KIE_PREFILL_PASSES) return fail(m, KIE_ERR_ARG, "unknown prefill mode");
@@ -754,6 +763,17 @@ int kie_e4m3_table_probe(float* out256, void* hip_stream) {
     HIP_TRY(nullptr, launch_e4m3_table((float*)ptr, s));
     HIP_TRY(nullptr, hipStreamSynchronize(s));
     HIP_TRY(nullptr, hipMemcpy(out256, ptr, 256 * sizeof(float), hipMemcpyDeviceToHost));
+    return KIE_OK;
+}
+
+int kie_e2m1_table_probe(float* out64, void* hip_stream) {
+    if (!out64) return fail(nullptr, KIE_ERR_ARG, "null output");
+    hipStream_t s = (hipStream_t)hip_stream;
+    void* ptr = nullptr;   // the no-alloc scratch: 64 floats of output
+    HIP_TRY(nullptr, noalloc_scratch(&ptr));
+    HIP_TRY(nullptr, launch_e2m1_table((float*)ptr, s));
+    HIP_TRY(nullptr, hipStreamSynchronize(s));
+    HIP_TRY(nullptr, hipMemcpy(out64, ptr, 64 * sizeof(float), hipMemcpyDeviceToHost));
     return KIE_OK;
 }
 

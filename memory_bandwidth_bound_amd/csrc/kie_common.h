@@ -60,7 +60,8 @@ enum Phase : int {
 
 struct Dims {
     int L, d, H, Hkv, hd, F, V, E, topk, max_seq;
-    int w8;   // 1: fp8 (E4M3) weights with one fp32 scale per row; 0: fp16 weights
+    int w8;   // 1: quantised weights (fp8 E4M3 or fp4 E2M1) with one fp32 scale per row; 0: fp16
+    int w4;   // 1: the quantised weights are fp4 (E2M1), four rows per unit; 0: fp8, two rows per unit
 };
 
 struct RowSplit {
@@ -94,8 +95,10 @@ KIE_HD bool head_mode_at(const Dims& D, int c) {
 // Units of a slab of nrows rows of K fp16 each, padded to whole units.
 KIE_HD int slab_units(int nrows, int K) { return ceil_div(nrows * K, kUnitHalves); }
 // The same for the weight format of D (fp8 rows take one byte per weight and
-// come in pairs, so nrows is even and a unit holds 1024 weights).
+// come in pairs, a unit holding 1024 weights; fp4 rows half a byte and come
+// in fours, a unit holding 2048 weights).
 KIE_HD int slab_units_of(const Dims& D, int nrows, int K) {
+    if (D.w4) return ceil_div(nrows * K, 4 * kUnitHalves);
     return D.w8 ? ceil_div(nrows * K, 2 * kUnitHalves) : slab_units(nrows, K);
 }
 
@@ -112,11 +115,11 @@ KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
     // in groups of 4 (two (gate, up) pairs -> one fp16 pair of h), residual
     // rows (Wo, down) in pairs (one fp16 pair of x per exchanged word).
     case PH_QKV: s.M = (D.H + 2 * D.Hkv) * D.hd; s.K = D.d; s.gran = 4; break;
-    case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = 2; break;
+    case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = D.w4 ? 4 : 2; break;   // fp4: rows in fours
     case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 4; break;
-    case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;
-    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = D.w8 ? 2 : 1; break;   // fp8: rows in pairs
-    case PH_LM: s.M = D.V; s.K = D.d; s.gran = D.w8 ? 2 : 1; break;   // fp8: rows in pairs
+    case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = D.w4 ? 4 : 2; break;
+    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: rows in pairs
+    case PH_LM: s.M = D.V; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: pairs, fp4: fours
     case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;   // K per selected expert
     default: s.M = 0; s.K = 0; s.gran = 1; break;

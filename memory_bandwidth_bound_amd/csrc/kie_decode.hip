@@ -394,8 +394,9 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
 // ------------------------------------------------------------------------
 // Communication wave.
 // ------------------------------------------------------------------------
-template <int HD, bool W8, bool MS>
+template <int HD, int WF, bool MS>
 struct Comm {
+    static constexpr bool W8 = WF != 0;   // quantised weights (fp8 or fp4): fp32 inputs, row scales
     const DecodeArgs& a;
     KIE_LDS Smem* S;
     WgPlan W;
@@ -1076,6 +1077,33 @@ __device__ __forceinline__ void dot8_fp8(uint4 w, const float (&x)[8], float& aa
     ab = fmaf(p.y, x[7], ab);
 }
 
+// One fp4 unit against 8 fp32 inputs: the lane's 16 bytes are 4 bytes of
+// each of 4 rows (the same 8 columns; byte b holds columns 2b (low nibble)
+// and 2b+1); each E2M1 code converts exactly to fp32
+// (v_cvt_scalef32_pk_f32_fp4 with scale 1, two per instruction) and is
+// multiplied-added into its row's accumulator.
+__device__ __forceinline__ void dot8_fp4(uint4 w, const float (&x)[8], float& a0, float& a1, float& a2, float& a3) {
+    v2f_t p;
+#define KIE_FP4_ROW(word, acc)                                     \
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((word), 1.0f, 0); \
+    acc = fmaf(p.x, x[0], acc);                                    \
+    acc = fmaf(p.y, x[1], acc);                                    \
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((word), 1.0f, 1); \
+    acc = fmaf(p.x, x[2], acc);                                    \
+    acc = fmaf(p.y, x[3], acc);                                    \
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((word), 1.0f, 2); \
+    acc = fmaf(p.x, x[4], acc);                                    \
+    acc = fmaf(p.y, x[5], acc);                                    \
+    p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((word), 1.0f, 3); \
+    acc = fmaf(p.x, x[6], acc);                                    \
+    acc = fmaf(p.y, x[7], acc);
+    KIE_FP4_ROW(w.x, a0)
+    KIE_FP4_ROW(w.y, a1)
+    KIE_FP4_ROW(w.z, a2)
+    KIE_FP4_ROW(w.w, a3)
+#undef KIE_FP4_ROW
+}
+
 // The 8 fp32 inputs of this lane in input segment c (512 elements).
 __device__ __forceinline__ void load_xf(KIE_LDS Smem* S, int off, float (&x)[8]) {
     const uint4 u0 = lds_ld16(xf_of(S) + off), u1 = lds_ld16(xf_of(S) + off + 4);
@@ -1089,8 +1117,10 @@ __device__ __forceinline__ void load_xf(KIE_LDS Smem* S, int off, float (&x)[8])
     x[7] = __builtin_bit_cast(float, u1.w);
 }
 
-template <int HD, bool W8, bool MS>
+template <int HD, int WF, bool MS>
 struct Compute {
+    static constexpr bool W8 = WF != 0;   // quantised weights (fp8 or fp4)
+    static constexpr bool W4 = WF == 2;   // fp4: four rows per unit
     const DecodeArgs& a;
     KIE_LDS Smem* S;
     int w, lane, wg, Q;
@@ -1106,6 +1136,7 @@ struct Compute {
     int crow, cseg, ck;   // row, unit in the row segment and segment (MoE down: expert) of the next unit
     float acc;         // running partial dot product of the current row
     float acc2;        // fp8 weights: the second row of the current pair (crow counts pairs)
+    float acc3, acc4;  // fp4 weights: the third and fourth rows of the current four (crow counts fours)
 
     __device__ __forceinline__ Compute(const DecodeArgs& args, KIE_LDS Smem* s, int wi) : a(args), S(s), w(wi) {
         lane = lane_id();
@@ -1118,7 +1149,7 @@ struct Compute {
         entered = false;
         cg.q = -1;
         crow = cseg = ck = 0;
-        acc = acc2 = 0.f;
+        acc = acc2 = acc3 = acc4 = 0.f;
         ic = PIter{0, 0, 0, 0};
         seek(false);
     }
@@ -1415,6 +1446,53 @@ struct Compute {
         }
     }
 
+    // fp4 weights: the same with fours of rows per unit (crow counts fours).
+    template <int UPR>
+    __device__ __forceinline__ void consume_reg_fp4(uint32_t src, const Slot& sl, float (&xf)[UPR][8]) {
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
+        uint4 wv[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; ++s)
+            if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
+        const int last = cg.hi - 1 - sl.u0;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) {
+            if (s < sl.n) {
+                dot8_fp4(wv[s], xf[s % UPR], acc, acc2, acc3, acc4);
+                const bool seg_done = cseg + 1 == UPR;
+                if (seg_done || s == last) {
+                    const float r0 = wave_sum_to_lane63(acc), r1 = wave_sum_to_lane63(acc2);
+                    const float r2 = wave_sum_to_lane63(acc3), r3 = wave_sum_to_lane63(acc4);
+                    if (lane == 63) {
+                        S->part[(4 * crow) * kCompute + w] += r0;
+                        S->part[(4 * crow + 1) * kCompute + w] += r1;
+                        S->part[(4 * crow + 2) * kCompute + w] += r2;
+                        S->part[(4 * crow + 3) * kCompute + w] += r3;
+                    }
+                    acc = acc2 = acc3 = acc4 = 0.f;
+                }
+                if (seg_done) {
+                    cseg = 0;
+                    ++crow;
+                } else {
+                    ++cseg;
+                }
+            }
+        }
+        constexpr int R = kNB % UPR;
+        if (R && sl.n == kNB) {
+            float t[UPR][8];
+#pragma unroll
+            for (int j = 0; j < UPR; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t[j][e] = xf[(j + R) % UPR][e];
+#pragma unroll
+            for (int j = 0; j < UPR; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[j][e] = t[j][e];
+        }
+    }
+
     // Consume every batch of the current phase at the head of the ring with
     // the input in registers (rows of UPR units, one input segment for all
     // rows), refilling each batch as it goes. On return sq[0] belongs to a
@@ -1430,7 +1508,8 @@ struct Compute {
             while (sq[0].q == q && sq[0].n > 0) {
                 const uint32_t at = ring0 + head * kBatchBytes;
                 wait_vm<(kNS - 1) * kNB>();
-                consume_reg_fp8<UPR>(at, sq[0], xf);
+                if constexpr (W4) consume_reg_fp4<UPR>(at, sq[0], xf);
+                else consume_reg_fp8<UPR>(at, sq[0], xf);
                 wait_lgkm0();
                 finish_if_done(sq);
                 const Slot t = fill(at);
@@ -1472,7 +1551,7 @@ struct Compute {
         load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
         if (cg.upr) {
             // crow counts rows (fp8: pairs of rows, two per unit)
-            const int per_seg = (W8 ? cg.nrows / 2 : cg.nrows) * cg.upr;
+            const int per_seg = (W4 ? cg.nrows / 4 : W8 ? cg.nrows / 2 : cg.nrows) * cg.upr;
             ck = cg.lo / per_seg;
             const int rem = cg.lo - ck * per_seg;
             crow = rem / cg.upr;
@@ -1525,9 +1604,50 @@ struct Compute {
         }
     }
 
+    // fp4 weights, any row length (dense models): the inputs of each unit read
+    // from LDS, fours of rows per unit.
+    __device__ __forceinline__ void consume_fp4(uint32_t src, const Slot& sl) {
+        const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
+        const int upr = cg.upr;
+        uint4 wv[kNB];
+#pragma unroll
+        for (int s = 0; s < kNB; ++s)
+            if (s < sl.n) wv[s] = lds_ld16(wb + s * kUnitBytes);
+        const int last = cg.hi - 1 - sl.u0;
+#pragma unroll
+        for (int s = 0; s < kNB; ++s) {
+            if (s < sl.n) {
+                float x[8];
+                load_xf(S, cseg * kUnitHalves + lane * 8, x);
+                dot8_fp4(wv[s], x, acc, acc2, acc3, acc4);
+                const bool seg_done = cseg + 1 == upr;
+                if (seg_done || s == last) {
+                    const float r0 = wave_sum_to_lane63(acc), r1 = wave_sum_to_lane63(acc2);
+                    const float r2 = wave_sum_to_lane63(acc3), r3 = wave_sum_to_lane63(acc4);
+                    if (lane == 63) {
+                        S->part[(4 * crow) * kCompute + w] += r0;
+                        S->part[(4 * crow + 1) * kCompute + w] += r1;
+                        S->part[(4 * crow + 2) * kCompute + w] += r2;
+                        S->part[(4 * crow + 3) * kCompute + w] += r3;
+                    }
+                    acc = acc2 = acc3 = acc4 = 0.f;
+                }
+                if (seg_done) {
+                    cseg = 0;
+                    ++crow;
+                } else {
+                    ++cseg;
+                }
+            }
+        }
+    }
+
     __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
         if (cg.q != sl.q) enter_geo(sl);
-        if constexpr (W8) {
+        if constexpr (W4) {
+            consume_fp4(src, sl);
+            return;
+        } else if constexpr (W8) {
             consume_fp8(src, sl);
             return;
         }
@@ -1906,7 +2026,7 @@ struct Compute {
     }
 };
 
-template <int HD, bool W8, bool MS>
+template <int HD, int WF, bool MS>
 __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WgPlan W;
@@ -1919,44 +2039,49 @@ __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S
     }
     __syncthreads();
     if (wave == 0) {
-        Comm<HD, W8, MS> cm(a, S, W);
+        Comm<HD, WF, MS> cm(a, S, W);
         cm.run();
     } else {
-        Compute<HD, W8, MS> cp(a, S, wave - 1);
+        Compute<HD, WF, MS> cp(a, S, wave - 1);
         cp.run();
     }
 }
 
 // Two symbols for the same code, so that profiles keep the prompt's passes
 // apart from the generation requests.
-template <int HD, bool W8, bool MS>
+template <int HD, int WF, bool MS>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD, W8, MS>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, WF, MS>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
-template <int HD, bool W8, bool MS>
+template <int HD, int WF, bool MS>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD, W8, MS>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, WF, MS>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
 // The fp8-weight kernels are built for head_dim 128 only (the decoders whose
 // widths fp8 needs: every projection width a multiple of 512).
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool ms, bool prefill, int grid,
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bool prefill, int grid,
                          hipStream_t s) {
     void* args[] = {&dev_args};
-    if ((w8 || ms) && hd != 128) return hipErrorInvalidValue;
-    // [prefill][hd 128][w8][ms]; hd 64 has neither FP8 nor the matrix-core split
+    if ((wf != 0 || ms) && hd != 128) return hipErrorInvalidValue;
+    if (wf < 0 || wf > 2) return hipErrorInvalidValue;
+    // hd 64: fp16 without the matrix-core split; hd 128: [weight format][ms]
     const void* fn;
     if (hd == 64) {
-        fn = prefill ? (const void*)prefill_kernel<64, false, false> : (const void*)decode_kernel<64, false, false>;
+        fn = prefill ? (const void*)prefill_kernel<64, 0, false> : (const void*)decode_kernel<64, 0, false>;
     } else if (prefill) {
-        fn = w8 ? (ms ? (const void*)prefill_kernel<128, true, true> : (const void*)prefill_kernel<128, true, false>)
-                : (ms ? (const void*)prefill_kernel<128, false, true> : (const void*)prefill_kernel<128, false, false>);
+        const void* t[3][2] = {{(const void*)prefill_kernel<128, 0, false>, (const void*)prefill_kernel<128, 0, true>},
+                               {(const void*)prefill_kernel<128, 1, false>, (const void*)prefill_kernel<128, 1, true>},
+                               {(const void*)prefill_kernel<128, 2, false>, (const void*)prefill_kernel<128, 2, true>}};
+        fn = t[wf][ms ? 1 : 0];
     } else {
-        fn = w8 ? (ms ? (const void*)decode_kernel<128, true, true> : (const void*)decode_kernel<128, true, false>)
-                : (ms ? (const void*)decode_kernel<128, false, true> : (const void*)decode_kernel<128, false, false>);
+        const void* t[3][2] = {{(const void*)decode_kernel<128, 0, false>, (const void*)decode_kernel<128, 0, true>},
+                               {(const void*)decode_kernel<128, 1, false>, (const void*)decode_kernel<128, 1, true>},
+                               {(const void*)decode_kernel<128, 2, false>, (const void*)decode_kernel<128, 2, true>}};
+        fn = t[wf][ms ? 1 : 0];
     }
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }

@@ -27,7 +27,8 @@ Dims dims_of(const kie_config& c) {
     D.E = c.n_experts;
     D.topk = c.n_experts ? c.top_k : 0;
     D.max_seq = c.max_seq;
-    D.w8 = c.weight_format == KIE_WEIGHTS_FP8 ? 1 : 0;
+    D.w8 = (c.weight_format == KIE_WEIGHTS_FP8 || c.weight_format == KIE_WEIGHTS_FP4) ? 1 : 0;
+    D.w4 = c.weight_format == KIE_WEIGHTS_FP4 ? 1 : 0;
     return D;
 }
 
@@ -72,8 +73,16 @@ int validate_config(const kie_config& c, std::string* err) {
         if (c.d_model % 512 || c.ffn_dim % 512) return fail("MoE needs d_model and ffn_dim multiples of 512");
     }
     if (c.vocab > kMaxRowsWg * kGrid) return fail("vocab must be at most 65536");
-    if (c.weight_format != KIE_WEIGHTS_FP16 && c.weight_format != KIE_WEIGHTS_FP8)
-        return fail("weight_format must be KIE_WEIGHTS_FP16 or KIE_WEIGHTS_FP8");
+    if (c.weight_format != KIE_WEIGHTS_FP16 && c.weight_format != KIE_WEIGHTS_FP8 &&
+        c.weight_format != KIE_WEIGHTS_FP4)
+        return fail("weight_format must be KIE_WEIGHTS_FP16, KIE_WEIGHTS_FP8 or KIE_WEIGHTS_FP4");
+    if (c.weight_format == KIE_WEIGHTS_FP4) {
+        if (c.n_experts) return fail("fp4 weights are supported for dense models only");
+        if (c.head_dim != 128) return fail("fp4 weights are supported for head_dim 128 only");
+        if (c.d_model % 512 || c.ffn_dim % 512 || (c.n_heads * c.head_dim) % 512)
+            return fail("fp4 weights need d_model, ffn_dim and n_heads*head_dim multiples of 512");
+        if (c.vocab % 4) return fail("fp4 weights need a vocab that is a multiple of 4 (LM rows come in fours)");
+    }
     if (c.weight_format == KIE_WEIGHTS_FP8) {
         if (c.n_experts % 2) return fail("fp8 weights need an even number of experts (router rows come in pairs)");
         if (c.head_dim != 128) return fail("fp8 weights are supported for head_dim 128 only");
@@ -378,6 +387,54 @@ void quantize_row_e4m3(const uint16_t* w, const uint16_t* gain, int K, uint8_t* 
     *scale = s;
 }
 
+// ---------------------------------------------------------------- fp4 ------
+// E2M1: sign bit 3, 2 exponent bits e (bias 1), 1 mantissa bit m; e = 0 is
+// subnormal (m/2), otherwise (1 + m/2) * 2^(e-1): magnitudes 0, 0.5, 1, 1.5,
+// 2, 3, 4, 6, no infinity or NaN.
+float e2m1_decode(uint8_t q) {
+    const int e = (q >> 1) & 3, m = q & 1;
+    const float mag = e == 0 ? 0.5f * m : std::ldexp(1.f + 0.5f * m, e - 1);
+    return (q & 8) ? -mag : mag;
+}
+
+uint8_t e2m1_encode(float v) {
+    const uint8_t sign = std::signbit(v) ? 8 : 0;
+    const float a = std::isnan(v) ? 0.f : std::fabs(v);
+    if (a >= 6.f) return sign | 7;                               // saturate
+    // spacing 0.5 below 2, 1 in [2, 4), 2 in [4, 6); codes step with the
+    // values, so rounding the count of steps to even rounds the code to even
+    if (a < 2.f) return sign | (uint8_t)std::nearbyint(a * 2.f);          // codes 0..4
+    if (a < 4.f) return sign | (uint8_t)(std::nearbyint(a) + 2.f);        // codes 4..6
+    return sign | (uint8_t)(std::nearbyint(a * 0.5f) + 4.f);              // codes 6..7
+}
+
+void quantize_row_e2m1(const uint16_t* w, const uint16_t* gain, int K, uint8_t* q, float* scale) {
+    float amax = 0.f;
+    for (int k = 0; k < K; ++k) {
+        const float v = f16_to_f32(w[k]) * (gain ? f16_to_f32(gain[k]) : 1.f);
+        amax = std::fmax(amax, std::fabs(v));
+    }
+    const float s = amax > 0.f ? amax / 6.f : 1.f;
+    for (int k = 0; k < K; ++k) {
+        const float v = f16_to_f32(w[k]) * (gain ? f16_to_f32(gain[k]) : 1.f);
+        q[k] = e2m1_encode(v / s);
+    }
+    *scale = s;
+}
+
+// Four quantized rows q[0..3] of K columns as K/512 units: unit s, lane l
+// holds 4 bytes per row r (rows in order), byte b of row r holding the codes
+// of columns 512 s + 8 l + 2 b (low nibble) and + 1 (high nibble).
+static void put_quad_fp4(uint8_t* dst, const uint8_t* const* q, int K) {
+    for (int s = 0; s < K / 512; ++s)
+        for (int l = 0; l < 64; ++l)
+            for (int r = 0; r < 4; ++r)
+                for (int b = 0; b < 4; ++b) {
+                    const int c = s * 512 + 8 * l + 2 * b;
+                    dst[((size_t)s * 64 + l) * 16 + 4 * r + b] = (uint8_t)(q[r][c] | (q[r][c + 1] << 4));
+                }
+}
+
 // One pair of quantized rows (qa, qb) of K columns as K/512 units: unit s,
 // lane l holds qa[512 s + 8 l .. + 8] then qb[512 s + 8 l .. + 8].
 static void put_pair_fp8(uint8_t* dst, const uint8_t* qa, const uint8_t* qb, int K) {
@@ -395,6 +452,8 @@ void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* co
     const uint16_t* g_ffn = t[tidx_layer(c, l, 5)];
     std::memset(dst, 0, lay.layer_bytes);
     std::vector<uint8_t> qa(kMaxInput), qb(kMaxInput);
+    std::vector<uint8_t> q4[4] = {std::vector<uint8_t>(kMaxInput), std::vector<uint8_t>(kMaxInput),
+                                  std::vector<uint8_t>(kMaxInput), std::vector<uint8_t>(kMaxInput)};
     // source row (pointer, gain) of a phase row
     auto source = [&](int ph, int row, const uint16_t** src, const uint16_t** g) {
         *g = nullptr;
@@ -427,6 +486,19 @@ void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* co
             for (int j = 0; j < i; ++j)
                 off += (size_t)phase_units(D, layer_block_phase(D, j), kGrid, w) * kUnitBytes;
             const RowSplit r = split_rows(s.M, s.gran, kGrid, w);
+            if (D.w4) {
+                // fp4: rows in fours, one unit column per 512 columns of the four
+                for (int j = 0; j < r.nrows; j += 4) {
+                    const uint8_t* qr[4] = {q4[0].data(), q4[1].data(), q4[2].data(), q4[3].data()};
+                    for (int i2 = 0; i2 < 4; ++i2) {
+                        const uint16_t *sr, *gr;
+                        source(ph, r.row0 + j + i2, &sr, &gr);
+                        quantize_row_e2m1(sr, gr, s.K, q4[i2].data(), &scales[sbase + r.row0 + j + i2]);
+                    }
+                    put_quad_fp4(dst + off + (size_t)(j / 4) * s.K * 2, qr, s.K);
+                }
+                continue;
+            }
             for (int j = 0; j < r.nrows; j += 2) {
                 const uint16_t *sa, *sb, *ga, *gb;
                 source(ph, r.row0 + j, &sa, &ga);
@@ -469,8 +541,20 @@ void repack_lm_fp8(const kie_config& c, const Layout& lay, const uint16_t* const
     std::memset(dst, 0, lay.lm_bytes);
     std::vector<uint8_t> qa(D.d), qb(D.d);
     for (int w = 0; w < kGrid; ++w) {
-        const RowSplit r = split_rows(D.V, 2, kGrid, w);
+        const RowSplit r = split_rows(D.V, D.w4 ? 4 : 2, kGrid, w);
         uint8_t* p = dst + (size_t)lay.lm_off[w] * kUnitBytes;
+        if (D.w4) {
+            std::vector<uint8_t> q4[4] = {std::vector<uint8_t>(D.d), std::vector<uint8_t>(D.d),
+                                          std::vector<uint8_t>(D.d), std::vector<uint8_t>(D.d)};
+            const uint8_t* qr[4] = {q4[0].data(), q4[1].data(), q4[2].data(), q4[3].data()};
+            for (int j = 0; j < r.nrows; j += 4) {
+                for (int i2 = 0; i2 < 4; ++i2)
+                    quantize_row_e2m1(W + (size_t)(r.row0 + j + i2) * D.d, g, D.d, q4[i2].data(),
+                                      &scales[r.row0 + j + i2]);
+                put_quad_fp4(p + (size_t)(j / 4) * D.d * 2, qr, D.d);
+            }
+            continue;
+        }
         for (int j = 0; j < r.nrows; j += 2) {
             const int row = r.row0 + j;
             quantize_row_e4m3(W + (size_t)row * D.d, g, D.d, qa.data(), &scales[row]);

@@ -87,11 +87,15 @@ void repack_expert(const kie_config& c, const Layout& lay, const uint16_t* const
 // cos/sin table, angles formed in double precision. dst: float [max_seq][hd/2][2].
 void rope_table(const kie_config& c, float* dst);
 
+// FP4 (E2M1) rows: the quantizer of kie_quantize_e2m1_rows (codes 0..15).
+uint8_t e2m1_encode(float v);                 // nearest code, ties to even, saturating at 6
+float e2m1_decode(uint8_t q);
+void quantize_row_e2m1(const uint16_t* w, const uint16_t* gain, int K, uint8_t* q, float* scale);
 // FP8 (E4M3) rows: the quantizer of kie_quantize_e4m3_rows.
 uint8_t e4m3_encode(float v);                 // nearest code, ties to even, saturating
 float e4m3_decode(uint8_t q);
 void quantize_row_e4m3(const uint16_t* w, const uint16_t* gain, int K, uint8_t* q, float* scale);
-// fp8 weights: one layer's streaming block (layer_bytes bytes) and its row
+// fp8 / fp4 weights (D.w4 picks fp4): one layer's streaming block (layer_bytes bytes) and its row
 // scales (layer_scales floats), and the LM head block and its V scales.
 void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, uint8_t* dst,
                       float* scales);

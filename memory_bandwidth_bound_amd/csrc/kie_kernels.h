@@ -128,12 +128,12 @@ inline int phases_per_layer(const Dims& D) { return D.E ? 7 : 6; }
 inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2; }
 
 // Launchers. dev_args: the argument block already copied to device memory.
-// The persistent kernel comes in variants: hd 64 or 128, fp16 or FP8 weights
-// (w8), and, for hd 128, with the matrix-core split attention (ms) or
-// without: the host takes ms only for launches with a pass beyond head mode
-// (head_mode_at), since carrying that code costs the short-context passes
-// about 1%.
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, bool w8, bool ms, bool prefill, int grid,
+// The persistent kernel comes in variants: hd 64 or 128, the weight format
+// wf (0 fp16, 1 FP8, 2 FP4; quantised formats with hd 128 only), and, for hd
+// 128, with the matrix-core split attention (ms) or without: the host takes
+// ms only for launches with a pass beyond head mode (head_mode_at), since
+// carrying that code costs the short-context passes about 1%.
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bool prefill, int grid,
                          hipStream_t s);
 // Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
 // per workgroup, a contiguous range of units per wave, row sums added into y,
@@ -154,6 +154,7 @@ hipError_t launch_gemm_mfma(const float* A, int lda, int n, const GemmRows& R, f
 hipError_t launch_prefill_rows(int op, const PrefillRowArgs& r, hipStream_t s);
 // out[c] = the device's fp8 (E4M3) conversion of code c, c < 256.
 hipError_t launch_e4m3_table(float* out, hipStream_t s);
+hipError_t launch_e2m1_table(float* out64, hipStream_t s);
 // out[w] = the XCD workgroup w of a grid-sized cooperative launch ran on.
 hipError_t launch_xcd_map(int32_t* out, int grid, hipStream_t s);
 // Zero n 32-bit words with a kernel.

@@ -321,6 +321,35 @@ hipError_t launch_e4m3_table(float* out, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The device's E2M1 conversion (v_cvt_scalef32_pk_f32_fp4, scale 1) of
+// eight words; word l holds in byte b the codes (2l + b) % 16 (low nibble)
+// and (2l + b + 8) % 16 (high nibble).
+__global__ void __launch_bounds__(64, 1) e2m1_table_kernel(float* out) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const int l = threadIdx.x;
+    if (l >= 8) return;
+    uint32_t w = 0;
+    for (int b = 0; b < 4; ++b) w |= (uint32_t)(((2 * l + b) % 16) | (((2 * l + b + 8) % 16) << 4)) << (8 * b);
+    const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    float* o = out + 8 * l;
+    o[0] = p0.x;
+    o[1] = p0.y;
+    o[2] = p1.x;
+    o[3] = p1.y;
+    o[4] = p2.x;
+    o[5] = p2.y;
+    o[6] = p3.x;
+    o[7] = p3.y;
+}
+
+hipError_t launch_e2m1_table(float* out, hipStream_t s) {
+    hipLaunchKernelGGL(e2m1_table_kernel, dim3(1), dim3(64), 0, s, out);
+    return hipGetLastError();
+}
+
 // The XCD every workgroup of a grid-sized launch runs on.
 __global__ void __launch_bounds__(64, 1) xcd_map_kernel(int32_t* out) {
     if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();

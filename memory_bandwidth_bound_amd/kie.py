@@ -31,7 +31,7 @@ class KieConfig(ctypes.Structure):
                 ("rms_eps", c_float), ("rope_theta", c_float), ("max_seq", c_int32),
                 ("weight_format", c_int32)]
 
-WEIGHT_FORMATS = {"fp16": 0, "fp8": 1}
+WEIGHT_FORMATS = {"fp16": 0, "fp8": 1, "fp4": 2}
 
 
 class KieDebug(ctypes.Structure):
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      POINTER(c_float)]),
         "kie_e4m3_table_probe": (c_int32, [POINTER(c_float), c_void_p]),
         "kie_quantize_e4m3_rows": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float)]),
+        "kie_quantize_e2m1_rows": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, POINTER(c_float)]),
+        "kie_e2m1_table_probe": (c_int32, [POINTER(c_float), c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -406,6 +408,24 @@ def quantize_e4m3_rows(W: np.ndarray, gain: Optional[np.ndarray] = None):
     return q, s
 
 
+def quantize_e2m1_rows(W: np.ndarray, gain: Optional[np.ndarray] = None):
+    """The library's host FP4 quantizer (kie_quantize_e2m1_rows) on fp16 W
+    [rows][K] with an optional fp16 gain [K]: returns (codes uint8 0..15, scales f32)."""
+    lib = load_library()
+    W = np.ascontiguousarray(W, dtype=np.float16)
+    if W.ndim != 2:
+        raise KieError(-1, "W must be [rows][K]")
+    g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float16)
+    if g is not None and g.shape != (W.shape[1],):
+        raise KieError(-1, "gain must be [K]")
+    q = np.zeros(W.shape, dtype=np.uint8)
+    s = np.zeros(W.shape[0], dtype=np.float32)
+    _check(lib.kie_quantize_e2m1_rows(c_void_p(W.ctypes.data), None if g is None else c_void_p(g.ctypes.data),
+                                      W.shape[0], W.shape[1], c_void_p(q.ctypes.data),
+                                      s.ctypes.data_as(POINTER(c_float))))
+    return q, s
+
+
 def gemm_probe(A, W, stream=None):
     """Y = A @ W.T on the matrix cores for device tensors A float32 [n, K] and
     W float16 [M, K]; returns (Y float32 [n, M], device milliseconds)."""
@@ -437,6 +457,20 @@ def e4m3_table_probe(device: str = "cuda:0"):
         rc = lib.kie_e4m3_table_probe(out.ctypes.data_as(POINTER(c_float)), _stream_handle(torch, dev, None))
     _check(rc)
     return out
+
+
+def e2m1_table_probe(device: str = "cuda:0"):
+    """What the device's E2M1 conversion gives for eight words: [8][4][2]
+    values, word l's byte b holding the codes (2l + b) % 16 (low nibble) and
+    (2l + b + 8) % 16 (high nibble)."""
+    import torch
+    lib = load_library()
+    out = np.zeros(64, dtype=np.float32)
+    dev = torch.device(device)
+    with torch.cuda.device(dev):
+        rc = lib.kie_e2m1_table_probe(out.ctypes.data_as(POINTER(c_float)), _stream_handle(torch, dev, None))
+    _check(rc)
+    return out.reshape(8, 4, 2)
 
 
 def xcd_map(device: str = "cuda:0"):

@@ -20,8 +20,8 @@ def active_weight_bytes(cfg) -> int:
     Every layer projection (Q, K, V, O), the FFN (MoE: the router plus the
     top_k selected experts), the LM head and one embedding row. RMSNorm gains
     are folded into the following projections, so they are not read. fp16
-    weights take 2 bytes each; fp8 weights 1 byte each plus one fp32 scale per
-    row (the embedding row stays fp16).
+    weights take 2 bytes each; fp8 weights 1 byte each and fp4 weights half a
+    byte each, plus one fp32 scale per row (the embedding row stays fp16).
     """
     d, q, kv, f = cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim
     attn = q * d + 2 * kv * d + d * q
@@ -29,10 +29,12 @@ def active_weight_bytes(cfg) -> int:
         ffn = cfg.n_experts * d + cfg.top_k * 3 * f * d
     else:
         ffn = 3 * f * d
-    if getattr(cfg, "weight_format", "fp16") == "fp8":
+    wf = getattr(cfg, "weight_format", "fp16")
+    if wf in ("fp8", "fp4"):
         ffn_rows = (cfg.n_experts + cfg.top_k * (2 * f + d)) if cfg.n_experts else 2 * f + d
         rows = cfg.n_layers * (q + 2 * kv + d + ffn_rows) + cfg.vocab
-        return cfg.n_layers * (attn + ffn) + cfg.vocab * d + 4 * rows + 2 * d
+        weights = cfg.n_layers * (attn + ffn) + cfg.vocab * d
+        return (weights if wf == "fp8" else weights // 2) + 4 * rows + 2 * d
     params = cfg.n_layers * (attn + ffn) + cfg.vocab * d + d
     return 2 * params
 

@@ -10,12 +10,14 @@ the pages print. No function here is left unpinned.
 """
 from .decoder import (Decoder, rmsnorm, rope_angles, apply_rope, softmax, attention_decode,
                       silu, swiglu_ffn, topk_experts, greedy_argmax, gemv_f64, E4M3_MAX,
-                      e4m3_decode_table, e4m3_encode, quantize_rows_e4m3, dequantize_rows_e4m3)
+                      e4m3_decode_table, e4m3_encode, quantize_rows_e4m3, dequantize_rows_e4m3,
+                      E2M1_MAX, e2m1_decode_table, e2m1_encode, quantize_rows_e2m1, dequantize_rows_e2m1)
 from .compare import zscore_error, top2_gap, compare_logits
 
 __all__ = [
     "Decoder", "rmsnorm", "rope_angles", "apply_rope", "softmax", "attention_decode",
     "silu", "swiglu_ffn", "topk_experts", "greedy_argmax", "gemv_f64", "E4M3_MAX",
     "e4m3_decode_table", "e4m3_encode", "quantize_rows_e4m3", "dequantize_rows_e4m3",
+    "E2M1_MAX", "e2m1_decode_table", "e2m1_encode", "quantize_rows_e2m1", "dequantize_rows_e2m1",
     "zscore_error", "top2_gap", "compare_logits",
 ]

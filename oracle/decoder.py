@@ -209,6 +209,64 @@ def dequantize_rows_e4m3(q: np.ndarray, s: np.ndarray, dtype=np.float64) -> np.n
 
 
 # --------------------------------------------------------------------------
+# FP4 weights: the OCP 4-bit float E2M1 (the element type of the OCP
+# microscaling formats) with, as for FP8 here, one fp32 scale per weight row
+# mapping the row's largest magnitude to E2M1's largest value, 6.
+# --------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+
+
+def e2m1_decode_table() -> np.ndarray:
+    """float64 value of each of the 16 E2M1 codes, from the format's
+    definition: sign bit 3, 2 exponent bits e (bias 1), 1 mantissa bit m;
+    e = 0 is subnormal, m/2; otherwise (1 + m/2) * 2^(e-1). The magnitudes are
+    0, 0.5, 1, 1.5, 2, 3, 4, 6; there is no infinity or NaN."""
+    codes = np.arange(16)
+    e = (codes >> 1) & 3
+    m = (codes & 1).astype(np.float64)
+    mag = np.where(e == 0, m / 2.0, (1.0 + m / 2.0) * 2.0 ** (e - 1.0))
+    return np.where(codes & 8, -mag, mag)
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """The E2M1 code nearest to each value (ties to the even code), saturating
+    at +-6; the sign bit follows the input's (a negative value that rounds to
+    zero gives code 8). Found among the 8 non-negative table values; every
+    table value and every difference to a neighbour is exact in float32."""
+    v = np.asarray(v)
+    if v.dtype != np.float32:
+        v = v.astype(np.float64)
+    table = e2m1_decode_table()[:8].astype(v.dtype)   # codes 0..7, increasing
+    a = np.minimum(np.abs(v), v.dtype.type(E2M1_MAX))
+    hi = np.clip(np.searchsorted(table, a, side="left"), 1, 7)
+    lo = hi - 1
+    dlo, dhi = a - table[lo], table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == 0, 0, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return np.where(np.signbit(v), code | 8, code).astype(np.uint8)
+
+
+def quantize_rows_e2m1(W: np.ndarray, gain: Optional[np.ndarray] = None):
+    """Row-wise E2M1 quantisation of fp16 weights W [rows][K], each column k
+    first multiplied by gain[k]. In float32: v = w * g, s = max|v| / 6 per row
+    (1 for an all-zero row), q = E2M1(v / s). Returns (q uint8 codes 0..15
+    [rows][K], s float32 [rows])."""
+    v = np.asarray(W, dtype=np.float16).astype(np.float32)
+    if gain is not None:
+        v = v * np.asarray(gain, dtype=np.float16).astype(np.float32)[None, :]
+    amax = np.max(np.abs(v), axis=1)
+    s = np.where(amax > 0, amax / np.float32(E2M1_MAX), np.float32(1.0)).astype(np.float32)
+    q = e2m1_encode((v / s[:, None]).astype(np.float32))
+    return q, s
+
+
+def dequantize_rows_e2m1(q: np.ndarray, s: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """q [rows][K] codes and s [rows] scales -> the weights they stand for."""
+    return (e2m1_decode_table()[q] * np.asarray(s, dtype=np.float64)[:, None]).astype(dtype)
+
+
+# --------------------------------------------------------------------------
 # The decoder.
 # --------------------------------------------------------------------------
 
@@ -231,10 +289,12 @@ class Decoder:
                  cache_experts: bool = False, kv_dtype=np.float16):
         self.cfg = cfg
         self.dtype = np.dtype(dtype)
-        # fp8 weights: every projection is the row-wise E4M3 quantisation of
-        # the matrix with its preceding RMSNorm gain folded in, and the norms
-        # themselves then carry no gain (the embedding stays fp16)
-        self.fp8 = getattr(cfg, "weight_format", "fp16") == "fp8"
+        # fp8 / fp4 weights: every projection is the row-wise E4M3 / E2M1
+        # quantisation of the matrix with its preceding RMSNorm gain folded
+        # in, and the norms themselves then carry no gain (the embedding
+        # stays fp16)
+        self.wfmt = getattr(cfg, "weight_format", "fp16")
+        self.fp8 = self.wfmt in ("fp8", "fp4")   # a quantised model (either format)
         # The KV cache holds fp16 keys and values: each k, v is rounded to
         # fp16 when it is stored and read back exactly. kv_dtype=None keeps
         # the compute precision instead.
@@ -273,7 +333,7 @@ class Decoder:
                 raise ValueError(f"{name}: shape {t.shape} != {shape}")
         return {name: i for i, (name, _, _) in enumerate(specs)}
 
-    # the RMSNorm gain folded into each projection of an fp8 model
+    # the RMSNorm gain folded into each projection of a quantised model
     _FOLD = {"Wq": "g_attn", "Wk": "g_attn", "Wv": "g_attn", "Wg": "g_ffn", "Wu": "g_ffn", "Wo": None,
              "Wd": None, "Wr": "g_ffn"}
 
@@ -291,8 +351,12 @@ class Decoder:
                 layer, mat = name.split(".")[0], name.split(".")[-1]
                 gname = self._FOLD[mat]
                 g = None if gname is None else self._raw[self._index[f"{layer}.{gname}"]]
-            q, s = quantize_rows_e4m3(self._raw[i], g)
-            a = dequantize_rows_e4m3(q, s, self.dtype)
+            if self.wfmt == "fp4":
+                q, s = quantize_rows_e2m1(self._raw[i], g)
+                a = dequantize_rows_e2m1(q, s, self.dtype)
+            else:
+                q, s = quantize_rows_e4m3(self._raw[i], g)
+                a = dequantize_rows_e4m3(q, s, self.dtype)
         else:
             a = self._raw[i].astype(self.dtype)
         if self._cache_experts or ".e" not in name:

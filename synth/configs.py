@@ -33,7 +33,7 @@ class DecoderConfig:
     router_sigma: float = 0.1
     gain_sigma: float = 0.0     # 0 -> every RMSNorm gain is exactly 1
     seed: int = 0
-    weight_format: str = "fp16"   # "fp8": projections held as row-scaled E4M3 (quantized at load)
+    weight_format: str = "fp16"   # "fp8" / "fp4": projections held as row-scaled E4M3 / E2M1 (quantized at load)
 
     @property
     def max_seq(self) -> int:
@@ -82,6 +82,10 @@ CONFIGS: Dict[str, object] = {
     "2b_fp8": DecoderConfig(
         name="2b_fp8", n_layers=25, d_model=2560, n_heads=20, n_kv_heads=4, head_dim=128,
         ffn_dim=8192, vocab=32768, prompt_len=128, decode_steps=1024, weight_format="fp8"),
+    # The same ~2.1B decoder with every projection in row-scaled FP4 (E2M1).
+    "2b_fp4": DecoderConfig(
+        name="2b_fp4", n_layers=25, d_model=2560, n_heads=20, n_kv_heads=4, head_dim=128,
+        ffn_dim=8192, vocab=32768, prompt_len=128, decode_steps=1024, weight_format="fp4"),
     # The MoE decoder with router and experts in row-scaled FP8 (E4M3).
     "moe_fp8": DecoderConfig(
         name="moe_fp8", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,

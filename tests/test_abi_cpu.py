@@ -198,7 +198,8 @@ def test_host_fp8_quantizer_matches_oracle(lib):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(weight_format=2), dict(weight_format=1, n_experts=4, top_k=2, d_model=512, ffn_dim=512),
+    dict(weight_format=3), dict(weight_format=-1),
+    dict(weight_format=1, n_experts=4, top_k=2, d_model=512, ffn_dim=512),
     dict(weight_format=1, head_dim=64, d_model=512, n_heads=8, n_kv_heads=4, ffn_dim=512, vocab=1000),
     dict(weight_format=1, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4, head_dim=128, vocab=1001),
     dict(weight_format=1),                       # the tiny decoder: d_model 256
@@ -215,3 +216,56 @@ def test_fp8_workspace_is_about_half(lib):
     a = kie.workspace_bytes(synth.get_config("2b"))
     b = kie.workspace_bytes(synth.get_config("2b_fp8"))
     assert 0.5 < b / a < 0.62          # weights halve; embedding, KV cache and buffers stay
+
+
+# ---- fp4 weights ------------------------------------------------------------
+def test_host_fp4_quantizer_matches_oracle(lib):
+    """The library's E2M1 quantizer (what kie_load applies) against the
+    oracle's, bit for bit: codes and scales, with and without a folded gain,
+    an all-zero row, values exactly halfway between codes (ties to the even
+    code), negatives that round to zero (code 8) and saturation."""
+    import oracle
+    rng = np.random.default_rng(31)
+    W = (rng.standard_normal((40, 2560)) * 0.02).astype(np.float16)
+    W[3] = 0
+    W[4, :] = 0
+    W[4, 0] = np.float16(6.0)                    # scale exactly 1: the rest encode as given
+    t = oracle.e2m1_decode_table()[:8]
+    mids = ((t[:-1] + t[1:]) / 2).astype(np.float16)   # 0.25 .. 5: all exact in fp16
+    W[4, 1:8] = mids
+    W[4, 8:15] = -mids
+    W[4, 15:19] = np.float16([-0.2, 0.2, -0.0, 5.5])
+    W[5, :] = np.float16(0.001)
+    W[5, 0] = np.float16(-1.0)
+    g = (1 + rng.standard_normal(2560) * 0.3).astype(np.float16)
+    for gain in (None, g):
+        q, s = kie.quantize_e2m1_rows(W, gain)
+        qo, so = oracle.quantize_rows_e2m1(W, gain)
+        assert np.array_equal(s.view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(q, qo)
+    q, _ = kie.quantize_e2m1_rows(W[4:5])
+    assert q[0, 1:8].tolist() == [0, 2, 2, 4, 4, 6, 6]          # ties to the even code
+    assert q[0, 15:19].tolist() == [8, 0, 8, 7]
+
+
+@pytest.mark.parametrize("bad", [
+    dict(weight_format=2, n_experts=4, top_k=2, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4,
+         head_dim=128),                          # MoE
+    dict(weight_format=2, head_dim=64, d_model=512, n_heads=8, n_kv_heads=4, ffn_dim=512, vocab=1000),
+    dict(weight_format=2, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4, head_dim=128, vocab=1002),
+    dict(weight_format=2),                       # the tiny decoder: d_model 256
+])
+def test_fp4_configs_rejected(lib, bad):
+    kc = kie.make_config(synth.get_config("tiny"))
+    for k, v in bad.items():
+        setattr(kc, k, v)
+    assert lib.kie_workspace_bytes(ctypes.byref(kc)) == 0
+    assert lib.kie_last_error(None).decode()
+
+
+def test_fp4_workspace_is_about_a_quarter(lib):
+    a = kie.workspace_bytes(synth.get_config("2b"))
+    b = kie.workspace_bytes(synth.get_config("2b_fp4"))
+    c = kie.workspace_bytes(synth.get_config("2b_fp4").with_(d_model=2560))   # same shape
+    assert b == c
+    assert 0.26 < b / a < 0.4          # weights quarter; embedding, KV cache and buffers stay

@@ -175,6 +175,58 @@ def test_2b_fp8_prompt_deep_and_request(torch_cuda):
     report_worst("2b_fp8")
 
 
+# ---- the same decoder with fp4 (E2M1, one scale per row) weights -------------------
+def test_2b_fp4_prompt_deep_and_request(torch_cuda):
+    """The ~2.1B decoder with every projection quantised to row-scaled E2M1 at
+    load (the oracle quantises the fp16 weights itself): the prompt's last
+    logits, 4 greedy passes, 4 passes from a seeded 1100-position cache, and
+    one 1024-pass teacher-forced launch checked row by row against the
+    oracle's full causal forward."""
+    cfg = synth.get_config("2b_fp4")
+    n = cfg.decode_steps
+    W = _weights("2b")          # the same fp16 tensors as the 2b workload
+    P = synth.make_prompt(cfg)
+    say("2b_fp4: oracle quantisation and prefill")
+    ref = oracle.Decoder(cfg, W)
+    first, last = ref.prefill_batched(P)
+    ids, rows, _ = ref.decode(4, keep_logits=True)
+    F = synth.make_forced_tokens(cfg, n + 1)
+    m = _model(cfg, W)
+    try:
+        g_first, g_logits, _ = m.prefill(P, logits=True)
+        check_rows(g_logits[-1:], last[None], label="2b_fp4 prefill")
+        if oracle.top2_gap(last) > TOL:
+            assert g_first == first
+        m.rewind(len(P), first)
+        _, g_rows, _ = m.decode(4, force=ids, logits=True)
+        check_rows(g_rows, rows, label="2b_fp4 decode")
+        K, V = synth.make_kv_prefill(cfg, n_pos=1100)
+        ref.set_kv(K, V, int(F[0]))
+        _, drows, _ = ref.decode(4, force=F[1:5], keep_logits=True)
+        m.set_kv(K, V, int(F[0]))
+        _, g_drows, _ = m.decode(4, force=F[1:5], logits=True)
+        check_rows(g_drows, drows, label="2b_fp4 deep")
+        del K, V
+        m.reset()
+        m.prefill(P)
+        say(f"2b_fp4: one teacher-forced launch of {n} passes")
+        m.rewind(len(P), int(F[0]))
+        g_ids, _, _ = m.decode(n, force=F[1:])
+        m.rewind(len(P), int(F[0]))
+        c_ids, c_rows, _ = m.decode(n, force=F[1:], logits=True)
+        assert np.array_equal(g_ids, c_ids)
+        assert np.array_equal(c_ids, np.argmax(c_rows, axis=1))
+    finally:
+        m.close()
+    say(f"2b_fp4: oracle full causal forward over {len(P) + n} tokens")
+    rows = ref.forward_full(list(P) + list(F[:n]))[len(P):]
+    check_rows(c_rows, rows, label="2b_fp4 request-rows")
+    del c_rows
+    checked, total = _ids_agree(g_ids, rows, "2b_fp4 request")
+    assert checked >= total * 0.75
+    report_worst("2b_fp4")
+
+
 # ---- the same decoder after a 32768-position cache, 256-pass requests -------------
 def test_2b_32k_forced_passes_and_request(torch_cuda):
     cfg = synth.get_config("2b_32k")

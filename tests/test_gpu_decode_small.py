@@ -69,6 +69,20 @@ CASES = {
     "fp8_d2048": synth.DecoderConfig(name="fp8_d2048", n_layers=2, d_model=2048, n_heads=16, n_kv_heads=4,
                                      head_dim=128, ffn_dim=1536, vocab=3002, prompt_len=40, decode_steps=12,
                                      weight_format="fp8"),
+    # fp4 (E2M1, one scale per row) weights, rows in fours, gains folded in;
+    # rows of 512 and 1024 (the per-unit input path)
+    "fp4_d512_gains": synth.DecoderConfig(name="fp4_d512_gains", n_layers=2, d_model=512, n_heads=4,
+                                          n_kv_heads=2, head_dim=128, ffn_dim=1024, vocab=2000, prompt_len=12,
+                                          decode_steps=16, gain_sigma=0.2, weight_format="fp4"),
+    # fp4 with rows of 2048 (inputs in registers), a 1536-wide FFN, residual
+    # rows split 8 / 12 per workgroup, and a ragged LM split (751 fours of rows)
+    "fp4_d2048": synth.DecoderConfig(name="fp4_d2048", n_layers=2, d_model=2048, n_heads=16, n_kv_heads=4,
+                                     head_dim=128, ffn_dim=1536, vocab=3004, prompt_len=40, decode_steps=12,
+                                     weight_format="fp4"),
+    # fp4 across head mode into the split over positions (matrix cores)
+    "fp4_long": synth.DecoderConfig(name="fp4_long", n_layers=2, d_model=512, n_heads=4, n_kv_heads=1,
+                                    head_dim=128, ffn_dim=1024, vocab=2048, prompt_len=1140, decode_steps=20,
+                                    weight_format="fp4"),
 }
 
 

@@ -84,6 +84,21 @@ def test_gemv_probe_full_shapes_sampled(torch_cuda, si):
     assert ms > 0
 
 
+def test_e2m1_device_conversion_table(torch_cuda):
+    """The device's fp4 conversion (v_cvt_scalef32_pk_f32_fp4 with scale 1,
+    what the fp4 GEMVs use) gives every E2M1 code exactly the oracle's value,
+    the low nibble of a byte first, each of the four bytes selectable: the
+    layout the loader packs."""
+    from memory_bandwidth_bound_amd import kie
+    dev = kie.e2m1_table_probe().astype(np.float64)
+    ref = oracle.e2m1_decode_table()
+    for l in range(8):
+        for b in range(4):
+            assert dev[l, b, 0] == ref[(2 * l + b) % 16], (l, b)
+            assert dev[l, b, 1] == ref[(2 * l + b + 8) % 16], (l, b)
+            assert np.signbit(dev[l, b, 0]) == np.signbit(ref[(2 * l + b) % 16])
+
+
 def test_e4m3_device_conversion_table(torch_cuda):
     """The device's fp8 conversion (what the fp8 GEMVs use) gives every E4M3
     code exactly the oracle's value from the format's definition (NaN codes

@@ -622,3 +622,87 @@ def test_fp8_decoder_is_the_model_on_dequantised_weights():
     # and it is not the fp16 model
     plain = oracle.Decoder(cfg.with_(weight_format="fp16"), W, dtype=np.float64)
     assert not np.allclose(got, np.stack([plain.step(t) for t in toks]))
+
+
+# ---------------------------------------------------------------- fp4 -------
+def test_e2m1_table_is_the_published_value_set():
+    """E2M1 (the OCP microscaling element type): magnitudes 0, 0.5, 1, 1.5, 2,
+    3, 4, 6 in code order, the same with the sign bit set; every value is also
+    exactly an E4M3 value (the two tables come from different definitions)."""
+    t = oracle.e2m1_decode_table()
+    assert t[:8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(t[8:], -t[:8]) and np.signbit(t[8])
+    e4 = oracle.e4m3_decode_table()
+    assert np.array_equal(e4[oracle.e4m3_encode(t[:8])], t[:8])
+    assert oracle.E2M1_MAX == t.max() == 6.0
+
+
+def test_e2m1_encode_against_brute_force_nearest():
+    t = oracle.e2m1_decode_table()[:8]
+    rng = np.random.default_rng(41)
+    v = np.concatenate([rng.uniform(-8, 8, 4000), (t[1:] + t[:-1]) / 2, -(t[1:] + t[:-1]) / 2,
+                        t, -t, [7.0, -100.0, 6.0001]]).astype(np.float32)
+    got = oracle.e2m1_encode(v)
+    for x, c in zip(v.astype(np.float64), got):
+        a = min(abs(x), 6.0)
+        d = np.abs(t - a)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]   # ties to the even code
+        if np.signbit(x):
+            want |= 8
+        assert c == want, (x, c, want)
+    assert np.array_equal(oracle.e2m1_encode(t), np.arange(8))   # round trip
+
+
+def test_quantize_rows_e2m1_properties():
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((6, 1024)) * 0.02).astype(np.float16)
+    W[1] = 0                                                 # all-zero row: scale 1, codes 0
+    W[2] = 0
+    W[2, 5] = np.float16(-0.25)                              # one non-zero: it is -6 * s
+    g = (1 + rng.standard_normal(1024) * 0.2).astype(np.float16)
+    q, s = oracle.quantize_rows_e2m1(W, g)
+    assert s.dtype == np.float32 and q.dtype == np.uint8 and q.max() < 16
+    assert s[1] == 1.0 and not q[1].any()
+    assert q[2, 5] == 15 and (q[2, :5] == 0).all()
+    v = W.astype(np.float32) * g.astype(np.float32)
+    for r in (0, 3, 4, 5):
+        k = int(np.argmax(np.abs(v[r])))
+        assert q[r, k] & 7 == 7                              # the row's largest magnitude maps to 6
+        assert s[r] == np.float32(np.abs(v[r]).max() / np.float32(6.0))
+    deq = oracle.dequantize_rows_e2m1(q, s)
+    t = oracle.e2m1_decode_table()
+    c = (q & 7).astype(np.int64)
+    up = t[np.minimum(c, 6) + 1] - t[np.minimum(c, 6)]
+    down = t[np.maximum(c, 1)] - t[np.maximum(c, 1) - 1]
+    step = np.maximum(up, down) * s[:, None]
+    assert np.all(np.abs(deq - v) <= step / 2 * (1 + 1e-6))
+
+
+def test_fp4_decoder_is_the_model_on_dequantised_weights():
+    """An fp4 decoder equals the written-out definition with every projection
+    replaced by its row-wise E2M1 quantisation (gain folded in)."""
+    cfg = _tiny(d_model=16, weight_format="fp4")
+    W = make_weights(cfg)
+    names = [n for n, _, _ in tensor_specs(cfg)]
+    T = dict(zip(names, W))
+    deq = []
+    for n, t in zip(names, W):
+        if n.split(".")[-1].startswith("g_"):
+            deq.append(np.ones(t.shape))
+        elif n == "E":
+            deq.append(t.astype(np.float64))
+        else:
+            mat = n.split(".")[-1]
+            g = {"Wq": "g_attn", "Wk": "g_attn", "Wv": "g_attn", "Wg": "g_ffn", "Wu": "g_ffn"}.get(mat)
+            if n == "W_lm":
+                g = T["g_final"]
+            elif g is not None:
+                g = T[n.split(".")[0] + "." + g]
+            deq.append(oracle.dequantize_rows_e2m1(*oracle.quantize_rows_e2m1(t, g)))
+    toks = [3, 17, 0, 22, 9]
+    dec = oracle.Decoder(cfg, W, dtype=np.float64)
+    got = np.stack([dec.step(t) for t in toks])
+    np.testing.assert_allclose(got, _brute_logits(cfg, deq, toks), rtol=1e-10, atol=1e-12)
+    fp8 = oracle.Decoder(cfg.with_(weight_format="fp8"), W, dtype=np.float64)
+    assert not np.allclose(got, np.stack([fp8.step(t) for t in toks]))

@@ -60,6 +60,20 @@ def test_config_sizes():
     assert c3.max_seq == 1152 and synth.get_config("C4").max_seq == 33024
 
 
+def test_quantised_active_bytes_from_tensor_list():
+    """fp8: one byte per projection weight, fp4: half a byte, both plus a
+    4-byte scale per projection row (the LM head's rows too) and one fp16
+    embedding row; counted here from the tensor list."""
+    for name, per in (("2b_fp8", 1.0), ("2b_fp4", 0.5)):
+        c = synth.get_config(name)
+        specs = synth.tensor_specs(c)
+        mats = [(n, s) for n, s, k in specs if k != "gain" and n != "E"]
+        weights = sum(int(np.prod(s)) for _, s in mats)
+        rows = sum(int(s[0]) for _, s in mats)
+        want = int(weights * per) + 4 * rows + 2 * c.d_model
+        assert roofline.active_weight_bytes(c) == want
+
+
 def test_moe_active_bytes_from_tensor_list():
     c5 = synth.get_config("C5")
     specs = synth.tensor_specs(c5)
