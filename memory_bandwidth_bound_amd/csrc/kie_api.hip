@@ -415,15 +415,22 @@ static int run_batched_prefill(kie_model* m, const int32_t* tokens, int n, int32
     r.out = (int32_t*)(ws + L.off_pf_tok) + kPrefillRows;
     float* Y = (float*)(ws + L.off_pf_y);
     auto rows = [&](int op) -> hipError_t { return launch_prefill_rows(op, r, s); };
-    auto gemm = [&](const float* A, int lda, const uint8_t* base, const int32_t* sl, int M, int K, int gran) {
+    // quantised weights: each phase's row scales (per layer: QKV, Wo, gate/up,
+    // down rows; the LM head's after the last layer)
+    const float* sc = D.w8 ? (const float*)(ws + L.off_scales) : nullptr;
+    const int wf = D.w4 ? 2 : D.w8 ? 1 : 0;
+    auto gemm = [&](const float* A, int lda, const uint8_t* base, const int32_t* sl, int ph, const float* scales) {
+        const PhaseShape ps = phase_shape(D, ph);
         GemmRows R;
         R.base = base;
         R.slab = sl;
-        R.M = M;
-        R.K = K;
-        R.gran = gran;
+        R.M = ps.M;
+        R.K = ps.K;
+        R.gran = ps.gran;
         R.dense = 0;
-        return launch_gemm_mfma(A, lda, r.n, R, Y, M, s);
+        R.wf = wf;
+        R.scales = scales;
+        return launch_gemm_mfma(A, lda, r.n, R, Y, ps.M, s);
     };
 #define PF_TRY(call)                                         \
     do {                                                     \
@@ -439,26 +446,28 @@ static int run_batched_prefill(kie_model* m, const int32_t* tokens, int n, int32
         PF_TRY(rows(PF_EMBED));
         for (int l = 0; l < D.L; ++l) {
             const uint8_t* blk = ws + L.off_layers + (size_t)l * L.layer_bytes;
+            const float* ls = sc ? sc + (size_t)l * L.layer_scales : nullptr;
+            const int mo = D.d, mg = 2 * D.F;
             r.layer = l;
             PF_TRY(rows(PF_RMSNORM));
-            PF_TRY(gemm(r.A, D.d, blk, slab + 0 * kGrid, qkvM, D.d, 4));
+            PF_TRY(gemm(r.A, D.d, blk, slab + 0 * kGrid, PH_QKV, ls));
             r.ldy = qkvM;
             PF_TRY(rows(PF_QKV));
             PF_TRY(rows(PF_ATTN));
-            PF_TRY(gemm(r.A, qd, blk, slab + 1 * kGrid, D.d, qd, 2));
+            PF_TRY(gemm(r.A, qd, blk, slab + 1 * kGrid, PH_WO, ls ? ls + qkvM : nullptr));
             r.ldy = D.d;
             PF_TRY(rows(PF_RESIDUAL));
             PF_TRY(rows(PF_RMSNORM));
-            PF_TRY(gemm(r.A, D.d, blk, slab + 2 * kGrid, 2 * D.F, D.d, 4));
+            PF_TRY(gemm(r.A, D.d, blk, slab + 2 * kGrid, PH_GU, ls ? ls + qkvM + mo : nullptr));
             r.ldy = 2 * D.F;
             PF_TRY(rows(PF_SWIGLU));
-            PF_TRY(gemm(r.A, D.F, blk, slab + 3 * kGrid, D.d, D.F, 2));
+            PF_TRY(gemm(r.A, D.F, blk, slab + 3 * kGrid, PH_DOWN, ls ? ls + qkvM + mo + mg : nullptr));
             r.ldy = D.d;
             PF_TRY(rows(PF_RESIDUAL));
         }
         if (!last && !dbg_logits) continue;
         PF_TRY(rows(PF_RMSNORM));
-        PF_TRY(gemm(r.A, D.d, ws + L.off_lm, slab + 4 * kGrid, D.V, D.d, 1));
+        PF_TRY(gemm(r.A, D.d, ws + L.off_lm, slab + 4 * kGrid, PH_LM, sc ? sc + (size_t)D.L * L.layer_scales : nullptr));
         if (dbg_logits)
             PF_TRY(hipMemcpyAsync(dbg_logits + (size_t)c0 * D.V, Y, (size_t)nc * D.V * 4, hipMemcpyDeviceToHost, s));
         if (last) {
@@ -616,6 +625,8 @@ int kie_gemm_probe(const float* A, const void* W, float* Y, int32_t n, int32_t M
     R.K = K;
     R.gran = 1;
     R.dense = 1;
+    R.wf = 0;
+    R.scales = nullptr;
     hipEvent_t e0, e1;
     HIP_TRY(nullptr, hipEventCreate(&e0));
     HIP_TRY(nullptr, hipEventCreate(&e1));

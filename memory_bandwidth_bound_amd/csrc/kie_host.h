@@ -16,7 +16,7 @@ constexpr int kDebugRows = 64;    // logits rows buffered on the device per laun
 constexpr int kPrefillRows = 256; // prompt tokens per batched-prefill chunk
 
 // Does the batched (matrix-core) prefill support this model? Dense fp16.
-inline bool batched_prefill_ok(const Dims& D) { return D.E == 0 && !D.w8; }
+inline bool batched_prefill_ok(const Dims& D) { return D.E == 0; }
 
 // Byte offsets of every region of the caller's device workspace.
 struct Layout {

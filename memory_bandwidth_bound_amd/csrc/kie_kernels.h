@@ -100,6 +100,8 @@ struct GemmRows {
     const uint8_t* base;
     const int32_t* slab;   // [kGrid] units (device memory)
     int32_t M, K, gran, dense;
+    int32_t wf;            // weight format: 0 fp16, 1 fp8 (rows in pairs), 2 fp4 (rows in fours)
+    const float* scales;   // wf != 0: the phase's row scales [M] (device memory)
 };
 
 // Row-wise prefill kernels (kie_prefill.hip).

@@ -46,6 +46,69 @@ __device__ __forceinline__ const uint16_t* row_addr(const GemmRows& R, int m) {
     return (const uint16_t*)(R.base + (size_t)R.slab[w] * kUnitBytes + (size_t)(m - row0) * R.K * 2);
 }
 
+// Quantised weights (fp8: rows in pairs, fp4: rows in fours): the byte
+// address of row m's columns 0..7 in its group's first unit. Columns c of the
+// row sit in unit c / 512 of the group, lane (c % 512) / 8, at byte 8 (fp8:
+// second row of the pair) or 4 r (fp4: row r of the four) of the lane's 16.
+__device__ __forceinline__ const uint8_t* row_qbase(const GemmRows& R, int m) {
+    const int groups = R.M / R.gran, base = groups / kGrid, rem = groups % kGrid;
+    const int g = m / R.gran;
+    int w;
+    if (g < rem * (base + 1)) w = g / (base + 1);
+    else w = rem + (g - rem * (base + 1)) / base;
+    const int row0 = (w * base + (w < rem ? w : rem)) * R.gran;
+    const int rpu = R.wf == 2 ? 4 : 2, lr = m - row0;
+    const size_t unit = (size_t)(lr / rpu) * (R.K / 512);
+    return R.base + (size_t)R.slab[w] * kUnitBytes + unit * kUnitBytes + (lr % rpu) * (R.wf == 2 ? 4 : 8);
+}
+
+// 16 consecutive columns k0 .. k0 + 15 (k0 a multiple of 16) of a quantised
+// row, converted exactly to fp16 (E4M3 and E2M1 values all are fp16 values).
+template <int WF>
+__device__ __forceinline__ void load_w_quant(const uint8_t* qb, int k0, uint4 (&b)[2]) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const uint8_t* p = qb + (size_t)(k0 / 512) * kUnitBytes + ((k0 % 512) / 8) * 16;
+    float f[16];
+    if constexpr (WF == 1) {
+        const uint2 u0 = *(const uint2*)p, u1 = *(const uint2*)(p + 16);
+        const uint32_t d[4] = {u0.x, u0.y, u1.x, u1.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[i], false);
+            const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[i], true);
+            f[4 * i] = lo.x;
+            f[4 * i + 1] = lo.y;
+            f[4 * i + 2] = hi.x;
+            f[4 * i + 3] = hi.y;
+        }
+    } else {
+        const uint32_t d[2] = {*(const uint32_t*)p, *(const uint32_t*)(p + 16)};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const v2f b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 0);
+            const v2f b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 1);
+            const v2f b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 2);
+            const v2f b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], 1.0f, 3);
+            f[8 * i] = b0.x;
+            f[8 * i + 1] = b0.y;
+            f[8 * i + 2] = b1.x;
+            f[8 * i + 3] = b1.y;
+            f[8 * i + 4] = b2.x;
+            f[8 * i + 5] = b2.y;
+            f[8 * i + 6] = b3.x;
+            f[8 * i + 7] = b3.y;
+        }
+    }
+    h8_t h0, h1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h0[e] = (_Float16)f[e];
+        h1[e] = (_Float16)f[8 + e];
+    }
+    b[0] = __builtin_bit_cast(uint4, h0);
+    b[1] = __builtin_bit_cast(uint4, h1);
+}
+
 // One step's share of a thread: 16 consecutive k of one row of A (fp32) and
 // of one row of W (fp16). Thread t loads row t / 4 at k offset 16 (t % 4).
 // Rows past n (A) or M (W) load the last valid row instead: they only feed
@@ -56,7 +119,8 @@ struct GemmStage {
     uint4 b[2];
 };
 
-__device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const uint16_t* bp, int k0) {
+template <int WF>
+__device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const void* bp, int k0, int kq0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float4 u = *(const float4*)(ap + k0 + 4 * q);
@@ -65,8 +129,12 @@ __device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const 
         st.a[4 * q + 2] = u.z;
         st.a[4 * q + 3] = u.w;
     }
+    if constexpr (WF == 0) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) st.b[q] = *(const uint4*)(bp + k0 + 8 * q);
+        for (int q = 0; q < 2; ++q) st.b[q] = *(const uint4*)((const uint16_t*)bp + k0 + 8 * q);
+    } else {
+        load_w_quant<WF>((const uint8_t*)bp, k0 + kq0, st.b);
+    }
 }
 
 // Three K steps are in flight per thread (registers) while a fourth is
@@ -74,6 +142,7 @@ __device__ __forceinline__ void gemm_load(GemmStage& st, const float* ap, const 
 // latency to arrive, so one step in flight left the matrix cores idle most
 // of the time. Loads past the last step re-read the last step (in bounds,
 // unused), so every wait the compiler places covers exactly the step needed.
+template <int WF>
 __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict__ A, int lda, int n, GemmRows R,
                                                         float* __restrict__ Y, int ldy) {
     __shared__ __attribute__((aligned(16))) _Float16 ahi[kTile * kLdsStride];
@@ -85,7 +154,12 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict_
     const int lr = tid >> 2, lk = (tid & 3) * 16;
     const int pa = p0 + lr < n ? p0 + lr : n - 1, mb = m0 + lr < R.M ? m0 + lr : R.M - 1;
     const float* ap = A + (size_t)pa * lda + lk;
-    const uint16_t* bp = row_addr(R, mb) + lk;
+    // fp16: this thread's 16 columns start at bp; quantised: the row's group
+    // base (the column offset lk is added per step)
+    const void* bp;
+    if constexpr (WF == 0) bp = row_addr(R, mb) + lk;
+    else bp = row_qbase(R, mb);
+    const int kq0 = WF == 0 ? 0 : lk;
     const int klast = R.K - kTk;
     f16x_t acc = {};
     auto stage_in = [&](const GemmStage& st) {
@@ -120,20 +194,20 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict_
     };
     auto kat = [&](int k) { return k < klast ? k : klast; };
     GemmStage s0, s1, s2;
-    gemm_load(s0, ap, bp, 0);
-    gemm_load(s1, ap, bp, kat(kTk));
-    gemm_load(s2, ap, bp, kat(2 * kTk));
+    gemm_load<WF>(s0, ap, bp, 0, kq0);
+    gemm_load<WF>(s1, ap, bp, kat(kTk), kq0);
+    gemm_load<WF>(s2, ap, bp, kat(2 * kTk), kq0);
     for (int k0 = 0; k0 < R.K; k0 += 3 * kTk) {
         stage_in(s0);
-        gemm_load(s0, ap, bp, kat(k0 + 3 * kTk));
+        gemm_load<WF>(s0, ap, bp, kat(k0 + 3 * kTk), kq0);
         multiply();
         if (k0 + kTk >= R.K) break;
         stage_in(s1);
-        gemm_load(s1, ap, bp, kat(k0 + 4 * kTk));
+        gemm_load<WF>(s1, ap, bp, kat(k0 + 4 * kTk), kq0);
         multiply();
         if (k0 + 2 * kTk >= R.K) break;
         stage_in(s2);
-        gemm_load(s2, ap, bp, kat(k0 + 5 * kTk));
+        gemm_load<WF>(s2, ap, bp, kat(k0 + 5 * kTk), kq0);
         multiply();
     }
     // D[i][j]: lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8)
@@ -141,14 +215,18 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const float* __restrict_
     for (int v = 0; v < 16; ++v) {
         const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
         const int p = p0 + wr + i, m = m0 + wc + j;
-        if (p < n && m < R.M) Y[(size_t)p * ldy + m] = acc[v];
+        if (p < n && m < R.M) Y[(size_t)p * ldy + m] = WF == 0 ? acc[v] : acc[v] * R.scales[m];
     }
 }
 
 hipError_t launch_gemm_mfma(const float* A, int lda, int n, const GemmRows& R, float* Y, int ldy, hipStream_t s) {
     if (R.K % kTk || lda % 4 || n < 1 || R.M < 1) return hipErrorInvalidValue;
     dim3 grid((unsigned)ceil_div(R.M, kTile), (unsigned)ceil_div(n, kTile));
-    hipLaunchKernelGGL(gemm_mfma_kernel, grid, dim3(256), 0, s, A, lda, n, R, Y, ldy);
+    if (R.wf != 0 && (R.dense || !R.scales || R.K % 512 || R.gran % (R.wf == 2 ? 4 : 2)))
+        return hipErrorInvalidValue;
+    if (R.wf == 1) hipLaunchKernelGGL(gemm_mfma_kernel<1>, grid, dim3(256), 0, s, A, lda, n, R, Y, ldy);
+    else if (R.wf == 2) hipLaunchKernelGGL(gemm_mfma_kernel<2>, grid, dim3(256), 0, s, A, lda, n, R, Y, ldy);
+    else hipLaunchKernelGGL(gemm_mfma_kernel<0>, grid, dim3(256), 0, s, A, lda, n, R, Y, ldy);
     return hipGetLastError();
 }
 

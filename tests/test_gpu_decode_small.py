@@ -418,13 +418,15 @@ def test_host_watchdog_reports_overrun_then_recovery(torch_cuda):
 
 
 # ---- the batched (matrix-core) prefill ---------------------------------------------
-@pytest.mark.parametrize("name", ["tiny_gains", "gqa5_chunks_hd128", "gqa8_hd64"])
+@pytest.mark.parametrize("name", ["tiny_gains", "gqa5_chunks_hd128", "gqa8_hd64", "fp8_d512_gains", "fp8_d2048",
+                                  "fp4_d2048", "fp4_long"])
 def test_batched_prefill_rows_and_modes(torch_cuda, name):
     """Every prompt row's logits from the batched prefill against the oracle's
-    full causal forward, element by element (the 760-token prompt spans
-    three chunks of 256); the same prompt prefilled pass by pass gives the same
-    first token wherever the gap decides it, and decoding after either
-    prefill matches the oracle."""
+    full causal forward, element by element (the 760- and 1140-token prompts
+    span three and five chunks of 256; fp8 and fp4 weights go through the
+    GEMM converted to fp16 with their row scales on the outputs); the same
+    prompt prefilled pass by pass gives the same first token wherever the gap
+    decides it, and decoding after either prefill matches the oracle."""
     cfg = CASES[name]
     W = synth.make_weights(cfg)
     P = synth.make_prompt(cfg)
