@@ -136,10 +136,13 @@ def cpu_baseline_decode(cfg, W, prompt, target_s: float):
 def bench_decode(cfg, args):
     import torch
     from memory_bandwidth_bound_amd import kie
+    if args.tokens:
+        cfg = cfg.with_(decode_steps=args.tokens)
     t_setup = time.perf_counter()
     W = synth.make_weights(cfg)
     prompt = synth.make_prompt(cfg)
     m = kie.Model(cfg, W, device="cuda:0")
+    m.set_attention_mode(args.attention)
     if cfg.kv_prefill:
         K, V = synth.make_kv_prefill(cfg)
         pend = synth.make_pending_token(cfg)
@@ -183,7 +186,8 @@ def bench_decode(cfg, args):
         "dtype": DTYPE[getattr(cfg, "weight_format", "fp16")],
         "data": "synthetic",
         "config": {"workload": describe(cfg), "global_batch": 1, "seq_len": pos0 + n,
-                   "decode_tokens_per_step": n, "parallelism": "single GPU, one persistent launch per request"},
+                   "decode_tokens_per_step": n, "parallelism": "single GPU, one persistent launch per request",
+                   "attention": args.attention},
         "mbu": round(per_tok * tok_s / roofline.HBM_PEAK_BYTES_PER_S, 4),
         "bytes_per_token": per_tok,
         "kernel_ms_mean": round(k_ms, 3),
@@ -342,6 +346,11 @@ def main():
                     help="2b (default), 2b_32k, 2b_fp8, 2b_fp4, moe, moe_fp8, tiny, gemv, prefill, "
                          "or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attention", choices=("global", "xcd_local"), default="global",
+                    help="decode configs: attention at short context on the whole grid (default) or "
+                         "recomputed on every XCD")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="decode configs: passes per request (default: the workload's request length)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     args = ap.parse_args()

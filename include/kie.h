@@ -215,6 +215,32 @@ enum { KIE_PREFILL_AUTO = 0, KIE_PREFILL_PASSES = 1 };
  * an unknown mode or a null model. */
 int kie_set_prefill_mode(kie_model* m, int32_t mode);
 
+enum { KIE_ATTN_GLOBAL = 0, KIE_ATTN_XCD_LOCAL = 1 };
+/*
+ * Choose how later persistent launches (kie_decode; kie_prefill in passes
+ * mode) run attention at short context.
+ *  - KIE_ATTN_GLOBAL (the default): one workgroup of the grid per (query
+ *    head, chunk of positions); the attention output crosses the chip to the
+ *    workgroups of the output projection.
+ *  - KIE_ATTN_XCD_LOCAL: attention recomputed on every XCD instead of
+ *    exchanged between dies, with its exchange buffers replicated per XCD
+ *    (news.creeta.com monokernel article: "Inside the monokernel", attention
+ *    recompute; "MI300X die topology and the 256-CU mapping", work grouped by
+ *    die and buffers replicated per die). While a pass's head-mode work items
+ *    (query heads x chunks of at most 384 positions) fit the 32 workgroups of
+ *    one XCD, every XCD computes all of them and its output-projection
+ *    workgroups read the result from their own XCD's copy (32 readers per
+ *    copy instead of the whole grid on one buffer). Other passes run as in
+ *    KIE_ATTN_GLOBAL. The arithmetic and its order
+ *    are those of KIE_ATTN_GLOBAL, so the results are identical.
+ * Errors: KIE_ERR_ARG (null model, unknown mode); KIE_ERR_CONFIG
+ * (KIE_ATTN_XCD_LOCAL needs 2 to 8 query heads per KV head and at most 32
+ * query heads). In KIE_ATTN_XCD_LOCAL every workgroup checks at the start of
+ * a launch that it runs on XCD (its index mod 8); if one does not, the launch
+ * exits early and returns KIE_ERR_DEVICE.
+ */
+int kie_set_attention_mode(kie_model* m, int32_t mode);
+
 /*
  * Store already-rotated keys and values for positions 0..n_pos-1 directly in
  * the cache (host fp16 arrays [n_layers][n_pos][n_kv_heads][head_dim], each

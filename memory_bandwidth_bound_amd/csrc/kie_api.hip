@@ -30,6 +30,7 @@ struct kie_model {
     int32_t watchdog_ms;    // host limit per launch: 0 automatic, < 0 none
     uint32_t* hstatus;      // pinned host word: the kernel's status (the host's watchdog writes it too)
     int32_t prefill_mode;   // KIE_PREFILL_AUTO or KIE_PREFILL_PASSES
+    int32_t attn_mode;      // KIE_ATTN_GLOBAL or KIE_ATTN_XCD_LOCAL
     std::string err;
 };
 
@@ -166,6 +167,7 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
     m->watchdog_ms = 0;
     m->hstatus = nullptr;
     m->prefill_mode = KIE_PREFILL_AUTO;
+    m->attn_mode = KIE_ATTN_GLOBAL;
     if (ws_bytes < m->lay.total) {
         rc = fail(nullptr, KIE_ERR_WORKSPACE, "workspace smaller than kie_workspace_bytes()");
         delete m;
@@ -300,6 +302,8 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.ex.qkv = (uint64_t*)(m->ws + L.off_ex_qkv);
         a.ex.part = (uint64_t*)(m->ws + L.off_ex_part);
         a.ex.o = (uint64_t*)(m->ws + L.off_ex_o);
+        a.ex.part_copy = (int64_t)L.ex_part_copy;
+        a.ex.o_copy = (int64_t)L.ex_o_copy;
         a.ex.h = (uint64_t*)(m->ws + L.off_ex_h);
         a.ex.r = (uint64_t*)(m->ws + L.off_ex_r);
         a.ex.am = (uint64_t*)(m->ws + L.off_ex_am);
@@ -319,7 +323,8 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         a.pending = tok;
         a.n_steps = nc;
         a.flags = (force ? F_FORCE : 0) | (dbg_logits ? F_DBG_LOGITS : 0) | ((dbg_experts || dbg_router) ? F_DBG_EXPERTS : 0) |
-                  ((skip_lm && !debug) ? F_SKIP_LM : 0) | ((trace && s0 == 0) ? F_TRACE : 0);
+                  ((skip_lm && !debug) ? F_SKIP_LM : 0) | ((trace && s0 == 0) ? F_TRACE : 0) |
+                  (m->attn_mode == KIE_ATTN_XCD_LOCAL ? F_XCD_ATTN : 0);
         a.id0 = m->id_next;
         m->id_next += nphase;
         static_assert(sizeof(DecodeArgs) <= 4096, "argument block");
@@ -358,6 +363,11 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         if (fired) {
             m->pending = -1;
             return fail(m, KIE_ERR_TIMEOUT, "the launch exceeded the host watchdog's wall-clock limit");
+        }
+        if (status == kStatusWrongXcd) {
+            m->pending = -1;
+            return fail(m, KIE_ERR_DEVICE,
+                        "XCD-local attention: a workgroup did not run on XCD (its index mod 8); the launch exited");
         }
         if (status != 0) {
             m->pending = -1;
@@ -611,6 +621,16 @@ int kie_set_prefill_mode(kie_model* m, int32_t mode) {
     if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
     if (mode != KIE_PREFILL_AUTO && mode != KIE_PREFILL_PASSES) return fail(m, KIE_ERR_ARG, "unknown prefill mode");
     m->prefill_mode = mode;
+    return KIE_OK;
+}
+
+int kie_set_attention_mode(kie_model* m, int32_t mode) {
+    if (!m) return fail(nullptr, KIE_ERR_ARG, "null model");
+    if (mode != KIE_ATTN_GLOBAL && mode != KIE_ATTN_XCD_LOCAL) return fail(m, KIE_ERR_ARG, "unknown attention mode");
+    if (mode == KIE_ATTN_XCD_LOCAL && !xcd_attention_ok(m->lay.D))
+        return fail(m, KIE_ERR_CONFIG,
+                    "XCD-local attention needs 2 to 8 query heads per KV head and at most 32 query heads");
+    m->attn_mode = mode;
     return KIE_OK;
 }
 

@@ -32,6 +32,8 @@
 namespace kie {
 
 constexpr int kGrid = 256;                 // persistent workgroups: one per MI355X compute unit
+constexpr int kXcds = 8;                   // XCDs of MI355X: workgroup w of the grid runs on XCD w % kXcds
+constexpr int kXcdGrid = kGrid / kXcds;    // workgroups per XCD
 constexpr int kUnitBytes = 1024;           // one 16-byte-per-lane load of a wave
 constexpr int kUnitHalves = 512;           // fp16 elements per unit
 constexpr int kMaxGroup = 8;               // query heads per KV head supported
@@ -90,6 +92,14 @@ KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 KIE_HD bool head_mode_at(const Dims& D, int c) {
     const int Gq = D.H / D.Hkv;
     return Gq >= 2 && Gq <= kMaxGroup && D.H <= kGrid && c <= kAttnHeadModeMax;
+}
+
+// Can every XCD compute all query heads' attention itself (XCD-local
+// attention)? It needs head mode and at most one XCD's workgroups' worth of
+// query heads; at a given context it runs while the heads' chunks fit too.
+KIE_HD bool xcd_attention_ok(const Dims& D) {
+    const int Gq = D.H / D.Hkv;
+    return Gq >= 2 && Gq <= kMaxGroup && D.H <= kXcdGrid;
 }
 
 // Units of a slab of nrows rows of K fp16 each, padded to whole units.

@@ -128,6 +128,27 @@ __device__ __forceinline__ int attn_items(const DecodeArgs& a, int c) {
     return a.D.Hkv * attn_split(c, a.items_per_head, &CH);
 }
 
+// XCD-local attention (F_XCD_ATTN; attention recomputed per die instead of
+// exchanged between dies, its buffers replicated per die): while the
+// head-mode items fit one XCD's workgroups, every XCD computes all of them
+// for itself, workgroup w taking item w / kXcds, and writes its own copy
+// (w % kXcds) of the chunk states and of o, which only the workgroups of the
+// same XCD read. The words stay device-scope: an XCD's L2 is reached only by
+// workgroup-scope accesses, and those may be served by a compute unit's own
+// L1, which does not see the other units' stores. The kernel checks at its
+// start that workgroup w runs on XCD w % kXcds.
+__device__ __forceinline__ bool xcd_attention(const DecodeArgs& a, int c) {
+    return (a.flags & F_XCD_ATTN) && head_mode(a.D, c) && a.D.H * head_chunks(a, c) <= kXcdGrid;
+}
+// This workgroup's attention work item at c positions, and the copy of the
+// attention exchange buffers (part, o) it writes and reads.
+__device__ __forceinline__ int attn_item(const DecodeArgs& a, int c, int wg) {
+    return xcd_attention(a, c) ? wg / kXcds : wg;
+}
+__device__ __forceinline__ int attn_copy(const DecodeArgs& a, int c, int wg) {
+    return xcd_attention(a, c) ? wg % kXcds : 0;
+}
+
 __device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
     return (a.flags & F_SKIP_LM) && step != a.n_steps - 1;
 }
@@ -135,7 +156,7 @@ __device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
 // Do this workgroup's waves meet at the two barriers of a phase? Every wave
 // evaluates the same test, so the barrier sequences match.
 __device__ __forceinline__ bool phase_bars(const DecodeArgs& a, int kind, int step, int wg) {
-    if (kind == K_ATTN) return wg < attn_items(a, a.pos0 + step + 1);
+    if (kind == K_ATTN) return attn_item(a, a.pos0 + step + 1, wg) < attn_items(a, a.pos0 + step + 1);
     if (kind == K_LM) return !lm_skipped(a, step);
     return is_gemv(kind);
 }
@@ -272,12 +293,14 @@ __device__ __forceinline__ void stage1(KIE_LDS Smem* S, int i, float v) {
 // (x, o or h as flagged fp32 words; all of a wave's loads are in flight at
 // once), stages it and leaves the slice's sum of squares in ssp[w]. The RMS
 // norm scale is applied to the row sums afterwards, which is the same product
-// since a GEMV is linear. Returns 0, or 1 (this wave timed out) / 2 (another
-// workgroup reported a failure).
+// since a GEMV is linear. c: positions the pass attends (with XCD-local
+// attention, Wo reads its own XCD's copy of o). Returns 0, or 1 (this wave
+// timed out) / 2 (another workgroup reported a failure).
 template <bool W8>
 __device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S, int kind, int n, uint32_t id,
-                                            int w) {
-    const uint64_t* src = kind == K_WO ? a.ex.o : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
+                                            int w, int c) {
+    const uint64_t* src = kind == K_WO ? a.ex.o + (size_t)attn_copy(a, c, blockIdx.x) * a.ex.o_copy
+                                       : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
     const int i0 = n * w / kWaves, i1 = n * (w + 1) / kWaves;
     float ss = 0.f;
     const int r = fw_gather(src + i0, i1 - i0, id, a.spin, a.status, [&](int i, uint32_t v) {
@@ -309,11 +332,14 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
     int CH;
     const bool hm = head_mode(D, pos + 1);
     const int nch = hm ? head_chunks(a, pos + 1) : 1;
-    // head mode: this workgroup holds chunk wg / H of query head wg % H; chunks
+    // head mode: this workgroup holds chunk it / H of query head it % H; chunks
     // 1 .. nch-1 publish their states, chunk 0 combines them
     const int nper = hm ? nch : attn_split(pos + 1, a.items_per_head, &CH);
-    const int g = wg % D.Hkv, chunk = hm ? wg / D.H : wg / D.Hkv;
-    const int i0 = hm ? ((wg % D.H) / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
+    const int it = attn_item(a, pos + 1, wg);
+    uint64_t* const part = a.ex.part + (size_t)attn_copy(a, pos + 1, wg) * a.ex.part_copy;
+    uint64_t* const ob = a.ex.o + (size_t)attn_copy(a, pos + 1, wg) * a.ex.o_copy;
+    const int g = it % D.Hkv, chunk = hm ? it / D.H : it / D.Hkv;
+    const int i0 = hm ? ((it % D.H) / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
     for (int idx = i0 + 2 * (w8 * 64 + lane); idx < i1; idx += 2 * 64 * kWaves) {
         const int j = idx / HD, dd = idx % HD;
         float M = -3.0e38f;
@@ -340,7 +366,7 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         if (u < kn) {
-                            const uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + k0 + u) * (HD + 2);
+                            const uint64_t* pp = part + ((size_t)head * a.items_per_head + k0 + u) * (HD + 2);
                             wv[u][0] = fw_load(pp);
                             wv[u][1] = fw_load(pp + 1);
                             wv[u][2] = fw_load(pp + 2 + dd);
@@ -376,10 +402,10 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
         }
         if (nper == 1 || (hm && chunk == 0)) {
             // the whole row is here: publish o under the combine phase's id
-            fw_store(a.ex.o + head * HD + dd, __builtin_bit_cast(uint32_t, O0 / L), id + 1);
-            fw_store(a.ex.o + head * HD + dd + 1, __builtin_bit_cast(uint32_t, O1 / L), id + 1);
+            fw_store(ob + head * HD + dd, __builtin_bit_cast(uint32_t, O0 / L), id + 1);
+            fw_store(ob + head * HD + dd + 1, __builtin_bit_cast(uint32_t, O1 / L), id + 1);
         } else {
-            uint64_t* pp = a.ex.part + ((size_t)head * a.items_per_head + chunk) * (HD + 2);
+            uint64_t* pp = part + ((size_t)head * a.items_per_head + chunk) * (HD + 2);
             fw_store(pp + 2 + dd, __builtin_bit_cast(uint32_t, O0), id);
             fw_store(pp + 3 + dd, __builtin_bit_cast(uint32_t, O1), id);
             if (dd == 0) {
@@ -401,6 +427,7 @@ struct Comm {
     KIE_LDS Smem* S;
     WgPlan W;
     int wg, lane, tok;
+    int att_c;     // positions the current pass attends
     bool dead;
     float rq[4];   // QKV epilogue: (cos, sin) of this lane's two rotary pairs, loaded before the input gather
     float rs[4];   // fp8 weights: scales of the rows this lane's epilogue handles, loaded before the input gather
@@ -411,6 +438,7 @@ struct Comm {
         wg = blockIdx.x;
         lane = lane_id();
         tok = a.pending;
+        att_c = a.pos0 + 1;
         dead = false;
     }
 
@@ -437,7 +465,7 @@ struct Comm {
     __device__ __forceinline__ void input_share(int kind, uint32_t id) {
         if (dead) return;
         const int n = S->geo[kind].gin;
-        const int r = gather_input<W8>(a, S, kind, n, id, 0);
+        const int r = gather_input<W8>(a, S, kind, n, id, 0, att_c);
         if (r) fail(r);
     }
 
@@ -600,6 +628,7 @@ struct Comm {
         const Dims& D = a.D;
         if (dead) return;
         const int q = it.q;
+        att_c = a.pos0 + it.step + 1;
         load_row_scales(kind, it.layer);
         switch (kind) {
         case K_QKV: {
@@ -623,7 +652,7 @@ struct Comm {
             break;
         }
         case K_ATTN: {
-            const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = wg % D.Hkv;
+            const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = attn_item(a, att_c, wg) % D.Hkv;
             const float qs = kLog2e / sqrtf((float)HD);
             const bool q16 = mfma_attention<MS>(D, a.pos0 + it.step + 1);
             gather(a.ex.qkv + (size_t)g * GW, GW, id_of(q - 1), [&](int i, uint32_t v) {
@@ -1288,7 +1317,8 @@ struct Compute {
             wg_barrier();   // the communication wave is done with the previous phases
             if (!stop) {
                 const int n = __builtin_amdgcn_readfirstlane(S->geo[kind].gin);
-                const int r = gather_input<W8>(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1);
+                const int r = gather_input<W8>(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1,
+                                               a.pos0 + cc.step + 1);
                 if (r && lane == 0) {
                     if (r == 1) sys_store32(a.status, (uint32_t)kStatusTimeout);
                     S->abort = 1u;
@@ -1304,7 +1334,8 @@ struct Compute {
         const int kind = kind_of(a.D, cc);
         if (!phase_bars(a, kind, cc.step, wg)) return;
         if (kind == K_ATTN && !stop && head_mode(a.D, a.pos0 + cc.step + 1)) {
-            attention<1>(cc.layer, a.pos0 + cc.step, (wg % a.D.H) / a.D.Hkv);   // one head, one chunk
+            const int it = attn_item(a, a.pos0 + cc.step + 1, wg);
+            attention<1>(cc.layer, a.pos0 + cc.step, (it % a.D.H) / a.D.Hkv);   // one head, one chunk
         } else if (kind == K_ATTN && !stop) {
             const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
             // register arrays sized for the group (1, 2, 4 or 5 heads; 6 to 8
@@ -1908,7 +1939,8 @@ struct Compute {
         if (hm) CH = ceil_div(c, head_chunks(a, c));
         else attn_split(c, a.items_per_head, &CH);
         const int Gq = (D.H / D.Hkv - h0 < GB) ? D.H / D.Hkv - h0 : GB;   // heads h0 .. h0 + Gq - 1
-        const int g = wg % D.Hkv, chunk = hm ? wg / D.H : wg / D.Hkv;
+        const int it = attn_item(a, c, wg);
+        const int g = it % D.Hkv, chunk = hm ? it / D.H : it / D.Hkv;
         const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
         const int gi = lane / LPP, dl = (lane % LPP) * 8;
         float qv[GB][8];
@@ -2035,6 +2067,12 @@ __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S
         if (threadIdx.x == 0) {
             S->abort = 0u;
             write_geo(a, W, blockIdx.x, S->geo);
+            if ((a.flags & F_XCD_ATTN) && xcc_id() != (int)blockIdx.x % kXcds) {
+                // XCD-local attention would exchange words between XCDs
+                // through L2 caches that do not see each other: refuse
+                sys_store32(a.status, kStatusWrongXcd);
+                S->abort = 1u;
+            }
         }
     }
     __syncthreads();

@@ -195,6 +195,13 @@ __device__ __forceinline__ uint64_t fw_load(const uint64_t* p) {
     return __hip_atomic_load(gptr(const_cast<uint64_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool fw_ok(uint64_t w, uint32_t id) { return (uint32_t)(w >> 32) == id; }
+
+// The XCD (accelerator complex die) this wave runs on, from the hardware.
+__device__ __forceinline__ int xcc_id() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+    return (int)v;
+}
 __device__ __forceinline__ uint32_t fw_val(uint64_t w) { return (uint32_t)w; }
 
 // Device-scope plain data (the KV cache): 8-byte loads and stores that are

@@ -152,8 +152,11 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_v = take(Y.kv_bytes);
     Y.off_ex_x = take((size_t)D.d * 8);
     Y.off_ex_qkv = take((size_t)(D.H + D.Hkv) * D.hd * 8);
-    Y.off_ex_part = take((size_t)D.H * Y.attn_items_per_head * (D.hd + 2) * 8);
-    Y.off_ex_o = take((size_t)D.H * D.hd * 8);
+    // one copy per XCD (XCD-local attention), each on its own 4 KiB
+    Y.ex_part_copy = align_up((size_t)D.H * Y.attn_items_per_head * (D.hd + 2), A / 8);
+    Y.ex_o_copy = align_up((size_t)D.H * D.hd, A / 8);
+    Y.off_ex_part = take(Y.ex_part_copy * 8 * kXcds);
+    Y.off_ex_o = take(Y.ex_o_copy * 8 * kXcds);
     size_t hlen = D.E ? (size_t)D.topk * D.F : (size_t)D.F;
     Y.off_ex_h = take(hlen * 8);
     Y.off_ex_r = take((size_t)(D.E ? D.E : 1) * 8);

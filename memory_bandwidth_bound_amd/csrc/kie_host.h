@@ -34,8 +34,10 @@ struct Layout {
     // flagged-word exchange buffers (64-bit words), zeroed at load
     size_t off_ex_x;              // [d/2]
     size_t off_ex_qkv;            // [Hkv][(H/Hkv + 1) * hd]
-    size_t off_ex_part;           // [H][items per kv head][hd + 2]
-    size_t off_ex_o;              // [H*hd/2]
+    size_t off_ex_part;           // kXcds copies of [H][items per kv head][hd + 2]
+    size_t off_ex_o;              // kXcds copies of [H*hd]
+    size_t ex_part_copy;          // words from one copy of part (or o) to the next
+    size_t ex_o_copy;
     size_t off_ex_h;              // [max(F, topk*F)/2]
     size_t off_ex_r;              // [max(E, 1)]
     size_t off_ex_am;             // [kGrid][2]

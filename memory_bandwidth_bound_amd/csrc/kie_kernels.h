@@ -32,8 +32,12 @@ enum : int {
     F_DBG_LOGITS = 2,   // write every pass's logits to dbg_logits
     F_DBG_EXPERTS = 4,  // write every pass's expert ids and router logits to dbg_experts, dbg_router
     F_SKIP_LM = 8,      // skip the LM head on every pass but the last (prefill)
-    F_TRACE = 16        // record the phase timeline in trace
+    F_TRACE = 16,       // record the phase timeline in trace
+    F_XCD_ATTN = 32     // XCD-local attention where it fits (every XCD computes all heads for itself)
 };
+
+// Status word values (0: running or done).
+constexpr uint32_t kStatusWrongXcd = 3;   // XCD-local attention: a workgroup found itself off XCD w % kXcds
 
 // Flagged-word exchange buffers (64-bit words: phase id << 32 | payload).
 struct Exchange {
@@ -44,6 +48,10 @@ struct Exchange {
                      //          as pairs (v[2i], v[2i+1]), fp16
     uint64_t* part;  // [H][items][hd+2] split attention partials (m, l, o), fp32
     uint64_t* o;     // [H*hd]   attention output, fp32
+                     // part and o hold kXcds copies (XCD-local attention: copy x
+                     // is written and read by the workgroups of XCD x only)
+    int64_t part_copy;   // words from one copy of part to the next
+    int64_t o_copy;      // words from one copy of o to the next
     uint64_t* h;     // [F or topk*F] SwiGLU output (MoE: times pi), fp32
     uint64_t* r;     // [E] router logits, fp32
     uint64_t* am;    // [grid][2] per-workgroup argmax value, index

@@ -156,12 +156,6 @@ __global__ void __launch_bounds__(256) gemv_direct_kernel(GemvArgs a) {
 }
 
 // ------------------------------------------------------------ exchange probe
-// The XCD (accelerator complex die) this wave runs on, from the hardware.
-__device__ __forceinline__ int xcc_id() {
-    uint32_t v;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
-    return (int)v;
-}
 
 
 // XCD-aware barrier state in the probe's scratch (bytes from the scratch base).

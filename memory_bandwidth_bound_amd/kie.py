@@ -86,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kie_barrier_probe_noalloc": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_float), POINTER(c_int32)]),
         "kie_xcd_map": (c_int32, [POINTER(c_int32), c_void_p]),
         "kie_set_prefill_mode": (c_int32, [c_void_p, c_int32]),
+        "kie_set_attention_mode": (c_int32, [c_void_p, c_int32]),
         "kie_gemm_probe": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                      POINTER(c_float)]),
         "kie_e4m3_table_probe": (c_int32, [POINTER(c_float), c_void_p]),
@@ -297,6 +298,13 @@ class Model:
         (one decode pass per prompt token in one persistent launch)."""
         code = {"auto": 0, "passes": 1}[mode]
         _check(self._lib.kie_set_prefill_mode(self._h, code), self._h)
+
+    def set_attention_mode(self, mode: str):
+        """"global" (one workgroup of the grid per head-mode work item) or
+        "xcd_local" (every XCD recomputes the attention its output-projection
+        rows read, while the items fit one XCD's workgroups)."""
+        code = {"global": 0, "xcd_local": 1}[mode]
+        _check(self._lib.kie_set_attention_mode(self._h, code), self._h)
 
     def set_limits(self, spin_limit: int = 0, watchdog_ms: int = 0):
         """Device wait limit (polls; 0 = default) and host watchdog per launch

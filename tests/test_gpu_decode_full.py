@@ -122,6 +122,38 @@ def test_2b_request_launch_teacher_forced(torch_cuda):
     report_worst("2b")
 
 
+def test_2b_xcd_local_attention(torch_cuda):
+    """XCD-local attention on the full decoder: passes at 129..416 attended
+    positions, all heads' attention on every XCD up to 384, global head mode
+    after. Every logits row equals the global mode's bit for bit and is
+    compared with the oracle's full causal forward element by element."""
+    cfg = synth.get_config("2b")
+    n = 288
+    W = _weights("2b")
+    P = synth.make_prompt(cfg)
+    F = synth.make_forced_tokens(cfg, n + 1)
+    m = _model(cfg, W)
+    try:
+        m.prefill(P)
+        say(f"2b: {n} teacher-forced passes, global attention then XCD-local")
+        m.rewind(len(P), int(F[0]))
+        _, g_rows, _ = m.decode(n, force=F[1:], logits=True)
+        m.set_attention_mode("xcd_local")
+        m.rewind(len(P), int(F[0]))
+        x_ids, x_rows, _ = m.decode(n, force=F[1:], logits=True)
+        assert np.array_equal(x_rows, g_rows), "XCD-local logits differ from the global mode's"
+        del g_rows
+        m.rewind(len(P), int(F[0]))
+        s_ids, _, _ = m.decode(n, force=F[1:])
+        assert np.array_equal(s_ids, x_ids)
+    finally:
+        m.close()
+    say(f"2b: oracle full causal forward over {len(P) + n} tokens")
+    rows = oracle.Decoder(cfg, W).forward_full(list(P) + list(F[:n]))[len(P):]
+    check_rows(x_rows, rows, label="2b xcd_local request-rows")
+    report_worst("2b xcd_local")
+
+
 # ---- the same decoder with fp8 (E4M3, one scale per row) weights -------------------
 def test_2b_fp8_prompt_deep_and_request(torch_cuda):
     """The ~2.1B decoder with every projection quantised to row-scaled E4M3 at
