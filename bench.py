@@ -343,7 +343,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="2b",
-                    help="2b (default), 2b_32k, 2b_fp8, 2b_fp4, moe, moe_fp8, tiny, gemv, prefill, "
+                    help="2b (default), 2b_32k, 2b_fp8, 2b_fp4, moe, moe_fp8, moe_fp4, tiny, gemv, prefill, "
                          "or copy (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attention", choices=("global", "xcd_local"), default="global",

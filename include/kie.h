@@ -81,9 +81,9 @@ enum {
  *    row, the FP4 of the same passage, quantized like FP8 with 6 in place of
  *    448: s = fp32(max_k |v_k| / 6) (1 for an all-zero row), q_k = E2M1
  *    nearest to fp32(v_k / s), ties to the even code, saturating at 6
- *    (kie_quantize_e2m1_rows). Dense models only (no MoE); head_dim 128;
- *    d_model, ffn_dim and n_heads*head_dim multiples of 512; vocab a multiple
- *    of 4.
+ *    (kie_quantize_e2m1_rows). MoE as for FP8. head_dim 128; d_model,
+ *    ffn_dim and n_heads*head_dim multiples of 512; vocab and n_experts
+ *    multiples of 4.
  */
 typedef struct kie_config {
     int32_t n_layers;

@@ -204,7 +204,7 @@ int kie_load(const kie_config* cfg, const void* const* host_tensors, int32_t n_t
             std::vector<float> esc(D.w8 ? (size_t)(2 * D.F + D.d) : 0);
             for (int e = 0; e < D.E; ++e) {
                 if (D.w8) {
-                    repack_expert_fp8(*cfg, L, T, l, e, stage.data(), esc.data());
+                    repack_expert_quant(*cfg, L, T, l, e, stage.data(), esc.data());
                     size_t so = L.off_escales + ((size_t)l * D.E + e) * esc.size() * 4;
                     if ((rc = upload(m, so, esc.data(), esc.size() * 4)) != KIE_OK) return bail(rc);
                 } else {

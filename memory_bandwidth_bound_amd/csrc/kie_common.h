@@ -131,7 +131,7 @@ KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
     case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: rows in pairs
     case PH_LM: s.M = D.V; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: pairs, fp4: fours
     case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 4; break;
-    case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = 2; break;   // K per selected expert
+    case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = D.w4 ? 4 : 2; break;   // K per selected expert; = PH_WO
     default: s.M = 0; s.K = 0; s.gran = 1; break;
     }
     return s;

@@ -1235,10 +1235,11 @@ struct Compute {
                         const int u = iu + s;
                         size_t off;
                         int k;
-                        // fp8: units hold pairs of rows (one byte per weight), so
-                        // unit counts run over pairs and byte offsets halve
-                        constexpr int rpu = W8 ? 2 : 1;   // rows per unit column
-                        constexpr int wb = W8 ? 1 : 2;    // bytes per weight
+                        // fp8: units hold pairs of rows (one byte per weight), fp4
+                        // fours (half a byte): unit counts run over pairs or fours
+                        // and byte offsets shrink with the weight
+                        constexpr int rpu = W4 ? 4 : W8 ? 2 : 1;   // rows per unit column
+                        constexpr int wb2 = W4 ? 1 : W8 ? 2 : 4;   // twice the bytes per weight
                         if (kind == K_EGU) {
                             // virtual rows k * 2F + r: row r of the gate/up block of expert k
                             const int vr = ig.row0 + rpu * (u / upr), c = u - (u / upr) * upr;
@@ -1247,14 +1248,14 @@ struct Compute {
                             int vend = (k + 1) * 2 * D.F;
                             if (vend > ig.row0 + ig.nrows) vend = ig.row0 + ig.nrows;
                             run = ((vend - vr) / rpu) * upr - c;
-                            off = (size_t)rr * D.d * wb + (size_t)c * kUnitBytes;
+                            off = (size_t)rr * D.d * wb2 / 2 + (size_t)c * kUnitBytes;
                         } else {
                             // expert-major: the workgroup's down rows of expert 0, then 1, ...
                             const int per = (ig.nrows / rpu) * upr;
                             k = u / per;
                             const int rem = u - k * per;
                             run = per - rem;
-                            off = (size_t)2 * D.F * D.d * wb + (size_t)ig.row0 * D.F * wb + (size_t)rem * kUnitBytes;
+                            off = ((size_t)2 * D.F * D.d + (size_t)ig.row0 * D.F) * wb2 / 2 + (size_t)rem * kUnitBytes;
                         }
                         const int e = __builtin_amdgcn_readfirstlane(S->sel[k]);
                         p = lb + (size_t)e * a.expert_bytes + off;
@@ -1635,11 +1636,13 @@ struct Compute {
         }
     }
 
-    // fp4 weights, any row length (dense models): the inputs of each unit read
-    // from LDS, fours of rows per unit.
+    // fp4 weights, any row length: the inputs of each unit read from LDS, fours
+    // of rows per unit; MoE down as in consume_fp8 (ck = selected expert, its
+    // row partial sums scaled by that expert's row scales).
     __device__ __forceinline__ void consume_fp4(uint32_t src, const Slot& sl) {
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
-        const int upr = cg.upr;
+        const int upr = cg.upr, nquad = cg.nrows / 4;
+        const bool edown = cg.kind == K_EDOWN;
         uint4 wv[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; ++s)
@@ -1649,12 +1652,19 @@ struct Compute {
         for (int s = 0; s < kNB; ++s) {
             if (s < sl.n) {
                 float x[8];
-                load_xf(S, cseg * kUnitHalves + lane * 8, x);
+                load_xf(S, ck * cg.K + cseg * kUnitHalves + lane * 8, x);
                 dot8_fp4(wv[s], x, acc, acc2, acc3, acc4);
                 const bool seg_done = cseg + 1 == upr;
                 if (seg_done || s == last) {
-                    const float r0 = wave_sum_to_lane63(acc), r1 = wave_sum_to_lane63(acc2);
-                    const float r2 = wave_sum_to_lane63(acc3), r3 = wave_sum_to_lane63(acc4);
+                    float r0 = wave_sum_to_lane63(acc), r1 = wave_sum_to_lane63(acc2);
+                    float r2 = wave_sum_to_lane63(acc3), r3 = wave_sum_to_lane63(acc4);
+                    if (edown) {
+                        const KIE_LDS float* e = S->esc + ck * cg.nrows + 4 * crow;
+                        r0 *= e[0];
+                        r1 *= e[1];
+                        r2 *= e[2];
+                        r3 *= e[3];
+                    }
                     if (lane == 63) {
                         S->part[(4 * crow) * kCompute + w] += r0;
                         S->part[(4 * crow + 1) * kCompute + w] += r1;
@@ -1665,7 +1675,10 @@ struct Compute {
                 }
                 if (seg_done) {
                     cseg = 0;
-                    ++crow;
+                    if (++crow == nquad) {
+                        crow = 0;
+                        ++ck;
+                    }
                 } else {
                     ++cseg;
                 }

@@ -77,7 +77,7 @@ int validate_config(const kie_config& c, std::string* err) {
         c.weight_format != KIE_WEIGHTS_FP4)
         return fail("weight_format must be KIE_WEIGHTS_FP16, KIE_WEIGHTS_FP8 or KIE_WEIGHTS_FP4");
     if (c.weight_format == KIE_WEIGHTS_FP4) {
-        if (c.n_experts) return fail("fp4 weights are supported for dense models only");
+        if (c.n_experts % 4) return fail("fp4 weights need a multiple of 4 experts (router rows come in fours)");
         if (c.head_dim != 128) return fail("fp4 weights are supported for head_dim 128 only");
         if (c.d_model % 512 || c.ffn_dim % 512 || (c.n_heads * c.head_dim) % 512)
             return fail("fp4 weights need d_model, ffn_dim and n_heads*head_dim multiples of 512");
@@ -144,7 +144,8 @@ void make_layout(const kie_config& c, Layout* lay) {
     Y.off_layers = take(Y.layer_bytes * D.L);
     Y.off_lm = take(Y.lm_bytes);
     Y.off_emb = take((size_t)D.V * D.d * 2);
-    Y.expert_bytes = D.E ? (size_t)(2 * D.F * D.d + D.d * D.F) * (D.w8 ? 1 : 2) : 0;
+    // fp16: 2 bytes per weight, fp8: 1, fp4: 1/2
+    Y.expert_bytes = D.E ? (size_t)(2 * D.F * D.d + D.d * D.F) * (D.w4 ? 1 : D.w8 ? 2 : 4) / 2 : 0;
     Y.off_experts = take(Y.expert_bytes * D.E * D.L);
     Y.off_rope = take((size_t)D.max_seq * (D.hd / 2) * 8);
     Y.kv_bytes = (size_t)D.L * D.Hkv * D.max_seq * D.hd * 2;
@@ -515,7 +516,7 @@ void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* co
     }
 }
 
-void repack_expert_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int l, int e, uint8_t* dst,
+void repack_expert_quant(const kie_config& c, const Layout& lay, const uint16_t* const* t, int l, int e, uint8_t* dst,
                        float* scales) {
     const Dims& D = lay.D;
     const uint16_t* g = t[tidx_layer(c, l, 5)];
@@ -523,6 +524,27 @@ void repack_expert_fp8(const kie_config& c, const Layout& lay, const uint16_t* c
     const uint16_t* Wu = t[tidx_expert(c, l, e, 1)];
     const uint16_t* Wd = t[tidx_expert(c, l, e, 2)];
     std::vector<uint8_t> qa(kMaxInput), qb(kMaxInput);
+    if (D.w4) {
+        // fp4: rows in fours. Gate/up four p = rows (g_2p, u_2p, g_2p+1, u_2p+1)
+        // at 2 d bytes per four; down rows r .. r+3 at 2 F bytes per four.
+        std::vector<uint8_t> q4[4] = {std::vector<uint8_t>(kMaxInput), std::vector<uint8_t>(kMaxInput),
+                                      std::vector<uint8_t>(kMaxInput), std::vector<uint8_t>(kMaxInput)};
+        const uint8_t* qr[4] = {q4[0].data(), q4[1].data(), q4[2].data(), q4[3].data()};
+        for (int p = 0; p < D.F; p += 2) {
+            for (int i = 0; i < 4; ++i) {
+                const uint16_t* W = (i & 1) ? Wu : Wg;
+                quantize_row_e2m1(W + (size_t)(p + i / 2) * D.d, g, D.d, q4[i].data(), &scales[2 * p + i]);
+            }
+            put_quad_fp4(dst + (size_t)(p / 2) * D.d * 2, qr, D.d);
+        }
+        uint8_t* down = dst + (size_t)D.F * D.d;
+        for (int r = 0; r < D.d; r += 4) {
+            for (int i = 0; i < 4; ++i)
+                quantize_row_e2m1(Wd + (size_t)(r + i) * D.F, nullptr, D.F, q4[i].data(), &scales[2 * D.F + r + i]);
+            put_quad_fp4(down + (size_t)(r / 4) * D.F * 2, qr, D.F);
+        }
+        return;
+    }
     // gate/up rows interleaved (g_p, u_p): pair p is units p * d / 512 ..
     for (int p = 0; p < D.F; ++p) {
         quantize_row_e4m3(Wg + (size_t)p * D.d, g, D.d, qa.data(), &scales[2 * p]);

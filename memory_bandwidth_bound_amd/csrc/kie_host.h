@@ -102,9 +102,10 @@ void quantize_row_e4m3(const uint16_t* w, const uint16_t* gain, int K, uint8_t* 
 void repack_layer_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, uint8_t* dst,
                       float* scales);
 void repack_lm_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, uint8_t* dst, float* scales);
-// fp8 MoE: one expert block (gate/up row pairs (g_p, u_p), then down row
-// pairs; expert_bytes) and its 2F + d row scales.
-void repack_expert_fp8(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, int expert,
+// Quantised MoE: one expert block and its 2F + d row scales. fp8: gate/up
+// row pairs (g_p, u_p), then down row pairs; fp4: gate/up rows in fours
+// (g_p, u_p, g_p+1, u_p+1), then down rows in fours (expert_bytes).
+void repack_expert_quant(const kie_config& c, const Layout& lay, const uint16_t* const* t, int layer, int expert,
                        uint8_t* dst, float* scales);
 
 // Canonical tensor index helpers (same order as kie.h documents).

@@ -91,6 +91,11 @@ CONFIGS: Dict[str, object] = {
         name="moe_fp8", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
         ffn_dim=1024, vocab=32768, n_experts=64, top_k=8, prompt_len=128,
         decode_steps=512, weight_format="fp8"),
+    # The MoE decoder with router and experts in row-scaled FP4 (E2M1).
+    "moe_fp4": DecoderConfig(
+        name="moe_fp4", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,
+        ffn_dim=1024, vocab=32768, n_experts=64, top_k=8, prompt_len=128,
+        decode_steps=512, weight_format="fp4"),
     # Top-8 of 64 experts MoE decoder: only the selected experts are streamed.
     "moe": DecoderConfig(
         name="moe", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128,

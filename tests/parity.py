@@ -176,10 +176,10 @@ def moe_request_parity(m, cfg, W, P, n, trials, label, deep=32):
     import synth
     k = cfg.top_k
     compared, ties = 0, 0
-    fp8 = getattr(cfg, "weight_format", "fp16") == "fp8"
-    # fp8: one decoder for everything, its quantised experts cached (quantising
+    quant = getattr(cfg, "weight_format", "fp16") in ("fp8", "fp4")
+    # fp8 / fp4: one decoder for everything, its quantised experts cached (quantising
     # them again for a second decoder would cost minutes)
-    ref = oracle.Decoder(cfg, W, cache_experts=fp8)
+    ref = oracle.Decoder(cfg, W, cache_experts=quant)
     g_first, g_logits, g_exp = m.prefill(P, logits=True, experts=True, router=True)
     device_topk_exact(g_exp, m.last_router, k, label=f"{label} prompt")
     say(f"{label}: oracle batched prefill of {len(P)} tokens with the device's expert sets")
@@ -196,7 +196,7 @@ def moe_request_parity(m, cfg, W, P, n, trials, label, deep=32):
         last64 = oracle.Decoder(cfg, W, dtype=np.float64).prefill_batched(P, expert_overrides=g_exp)[1]
         conditioned_check(g_logits[-1], last, last64, f"{label} prefill")
     compared += 1
-    if fp8:
+    if quant:
         dec = ref
     else:
         del ref

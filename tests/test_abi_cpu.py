@@ -249,8 +249,8 @@ def test_host_fp4_quantizer_matches_oracle(lib):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(weight_format=2, n_experts=4, top_k=2, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4,
-         head_dim=128),                          # MoE
+    dict(weight_format=2, n_experts=6, top_k=2, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4,
+         head_dim=128),                          # MoE with experts not in fours
     dict(weight_format=2, head_dim=64, d_model=512, n_heads=8, n_kv_heads=4, ffn_dim=512, vocab=1000),
     dict(weight_format=2, d_model=512, ffn_dim=512, n_heads=4, n_kv_heads=4, head_dim=128, vocab=1002),
     dict(weight_format=2),                       # the tiny decoder: d_model 256
@@ -261,6 +261,17 @@ def test_fp4_configs_rejected(lib, bad):
         setattr(kc, k, v)
     assert lib.kie_workspace_bytes(ctypes.byref(kc)) == 0
     assert lib.kie_last_error(None).decode()
+
+
+def test_fp4_moe_config_accepted_and_experts_quartered(lib):
+    """fp4 MoE: experts in fours load, and each expert block takes a quarter
+    of its fp16 bytes."""
+    moe = synth.get_config("moe")
+    a = kie.workspace_bytes(moe)
+    b = kie.workspace_bytes(moe.with_(weight_format="fp4"))
+    assert b > 0
+    expert16 = (2 * moe.ffn_dim * moe.d_model + moe.d_model * moe.ffn_dim) * 2 * moe.n_experts * moe.n_layers
+    assert a - b >= 0.75 * expert16 * 0.99   # at least the experts' three quarters saved
 
 
 def test_fp4_workspace_is_about_a_quarter(lib):

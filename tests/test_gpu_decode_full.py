@@ -150,8 +150,8 @@ def test_2b_xcd_local_attention(torch_cuda):
         m.close()
     say(f"2b: oracle full causal forward over {len(P) + n} tokens")
     rows = oracle.Decoder(cfg, W).forward_full(list(P) + list(F[:n]))[len(P):]
-    check_rows(x_rows, rows, label="2b xcd_local request-rows")
-    report_worst("2b xcd_local")
+    check_rows(x_rows, rows, label="2b/xcd request-rows")
+    report_worst("2b/xcd")
 
 
 # ---- the same decoder with fp8 (E4M3, one scale per row) weights -------------------
@@ -328,6 +328,21 @@ def test_moe_fp8_prompt_routing_and_forced_request(torch_cuda):
     m = _model(cfg, W)
     try:
         done, ties = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 4, "moe_fp8", deep=16)
+    finally:
+        m.close()
+    assert done >= 8 + 16
+
+
+def test_moe_fp4_prompt_routing_and_forced_request(torch_cuda):
+    """The MoE decoder with router and experts in row-scaled E2M1 (the oracle
+    quantises the fp16 experts itself): the prompt, 4 two-pass trials, 16
+    passes deep in the cache and the 512-pass request, as for fp8."""
+    cfg = synth.get_config("moe_fp4")
+    W = _weights("moe")          # the same fp16 tensors as the moe workload
+    P = synth.make_prompt(cfg)
+    m = _model(cfg, W)
+    try:
+        done, ties = moe_request_parity(m, cfg, W, P, cfg.decode_steps, 4, "moe_fp4", deep=16)
     finally:
         m.close()
     assert done >= 8 + 16
