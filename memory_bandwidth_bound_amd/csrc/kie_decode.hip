@@ -998,6 +998,11 @@ struct Comm {
     __device__ __forceinline__ void run() {
         const Dims& D = a.D;
         const int Q = a.n_steps * pps_of(D);
+        // The exchange (polls, publications) is the critical path: let this
+        // wave's instructions issue ahead of the compute waves' (their weight
+        // DMA keeps the memory pipeline busy). Measured on the ~2.1B decoder:
+        // +1.0% tok/s fp16, +0.1% fp8; MoE +0.3%.
+        __builtin_amdgcn_s_setprio(3);
         PIter it{0, 0, 0, 0};
         for (; it.q < Q; advance(D, it)) {
             const int kind = kind_of(D, it);
