@@ -336,7 +336,7 @@ static int run_passes(kie_model* m, int n, const int32_t* force, int32_t* out_id
         // of this launch (the last attends pos0 + nc positions) leaves head mode
         const bool ms = D.hd == 128 && !head_mode_at(D, a.pos0 + nc);
         HIP_TRY(m, launch_decode((const DecodeArgs*)(m->ws + L.off_args), D.hd, D.w4 ? 2 : D.w8 ? 1 : 0, ms,
-                                 skip_lm, kGrid, m->stream));
+                                 (a.flags & F_XCD_ATTN) != 0, skip_lm, kGrid, m->stream));
         HIP_TRY(m, hipEventRecord(m->ev1, m->stream));
         // Host watchdog: poll the launch's end event against a wall-clock
         // limit. Past it, set the status word the kernel's long waits read

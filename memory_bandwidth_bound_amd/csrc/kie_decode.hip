@@ -137,16 +137,20 @@ __device__ __forceinline__ int attn_items(const DecodeArgs& a, int c) {
 // workgroup-scope accesses, and those may be served by a compute unit's own
 // L1, which does not see the other units' stores. The kernel checks at its
 // start that workgroup w runs on XCD w % kXcds.
+template <bool XA>
 __device__ __forceinline__ bool xcd_attention(const DecodeArgs& a, int c) {
+    if constexpr (!XA) return false;   // kernels built without it (the host picks the variant)
     return (a.flags & F_XCD_ATTN) && head_mode(a.D, c) && a.D.H * head_chunks(a, c) <= kXcdGrid;
 }
 // This workgroup's attention work item at c positions, and the copy of the
 // attention exchange buffers (part, o) it writes and reads.
+template <bool XA>
 __device__ __forceinline__ int attn_item(const DecodeArgs& a, int c, int wg) {
-    return xcd_attention(a, c) ? wg / kXcds : wg;
+    return xcd_attention<XA>(a, c) ? wg / kXcds : wg;
 }
+template <bool XA>
 __device__ __forceinline__ int attn_copy(const DecodeArgs& a, int c, int wg) {
-    return xcd_attention(a, c) ? wg % kXcds : 0;
+    return xcd_attention<XA>(a, c) ? wg % kXcds : 0;
 }
 
 __device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
@@ -155,8 +159,9 @@ __device__ __forceinline__ bool lm_skipped(const DecodeArgs& a, int step) {
 
 // Do this workgroup's waves meet at the two barriers of a phase? Every wave
 // evaluates the same test, so the barrier sequences match.
+template <bool XA>
 __device__ __forceinline__ bool phase_bars(const DecodeArgs& a, int kind, int step, int wg) {
-    if (kind == K_ATTN) return attn_item(a, a.pos0 + step + 1, wg) < attn_items(a, a.pos0 + step + 1);
+    if (kind == K_ATTN) return attn_item<XA>(a, a.pos0 + step + 1, wg) < attn_items(a, a.pos0 + step + 1);
     if (kind == K_LM) return !lm_skipped(a, step);
     return is_gemv(kind);
 }
@@ -296,10 +301,10 @@ __device__ __forceinline__ void stage1(KIE_LDS Smem* S, int i, float v) {
 // since a GEMV is linear. c: positions the pass attends (with XCD-local
 // attention, Wo reads its own XCD's copy of o). Returns 0, or 1 (this wave
 // timed out) / 2 (another workgroup reported a failure).
-template <bool W8>
+template <bool W8, bool XA>
 __device__ __forceinline__ int gather_input(const DecodeArgs& a, KIE_LDS Smem* S, int kind, int n, uint32_t id,
                                             int w, int c) {
-    const uint64_t* src = kind == K_WO ? a.ex.o + (size_t)attn_copy(a, c, blockIdx.x) * a.ex.o_copy
+    const uint64_t* src = kind == K_WO ? a.ex.o + (size_t)attn_copy<XA>(a, c, blockIdx.x) * a.ex.o_copy
                                        : ((kind == K_DOWN || kind == K_EDOWN) ? a.ex.h : a.ex.x);
     const int i0 = n * w / kWaves, i1 = n * (w + 1) / kWaves;
     float ss = 0.f;
@@ -324,7 +329,7 @@ __device__ __forceinline__ bool shared_gather(KIE_LDS Smem* S, int kind, int lay
 // Merge the compute waves' attention states of this chunk and publish o (the
 // whole row is here) or the chunk's partial state. Wave w8 of 8 takes every
 // 8th block of 64 (head, dim pair) slots.
-template <int HD>
+template <int HD, bool XA>
 __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, int pos, uint32_t id, int w8) {
     const Dims& D = a.D;
     const int lane = lane_id(), wg = blockIdx.x;
@@ -335,9 +340,9 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
     // head mode: this workgroup holds chunk it / H of query head it % H; chunks
     // 1 .. nch-1 publish their states, chunk 0 combines them
     const int nper = hm ? nch : attn_split(pos + 1, a.items_per_head, &CH);
-    const int it = attn_item(a, pos + 1, wg);
-    uint64_t* const part = a.ex.part + (size_t)attn_copy(a, pos + 1, wg) * a.ex.part_copy;
-    uint64_t* const ob = a.ex.o + (size_t)attn_copy(a, pos + 1, wg) * a.ex.o_copy;
+    const int it = attn_item<XA>(a, pos + 1, wg);
+    uint64_t* const part = a.ex.part + (size_t)attn_copy<XA>(a, pos + 1, wg) * a.ex.part_copy;
+    uint64_t* const ob = a.ex.o + (size_t)attn_copy<XA>(a, pos + 1, wg) * a.ex.o_copy;
     const int g = it % D.Hkv, chunk = hm ? it / D.H : it / D.Hkv;
     const int i0 = hm ? ((it % D.H) / D.Hkv) * HD : 0, i1 = hm ? i0 + HD : Gq * HD;
     for (int idx = i0 + 2 * (w8 * 64 + lane); idx < i1; idx += 2 * 64 * kWaves) {
@@ -420,7 +425,7 @@ __device__ __forceinline__ int attn_merge(const DecodeArgs& a, KIE_LDS Smem* S, 
 // ------------------------------------------------------------------------
 // Communication wave.
 // ------------------------------------------------------------------------
-template <int HD, int WF, bool MS>
+template <int HD, int WF, bool MS, bool XA>
 struct Comm {
     static constexpr bool W8 = WF != 0;   // quantised weights (fp8 or fp4): fp32 inputs, row scales
     const DecodeArgs& a;
@@ -465,7 +470,7 @@ struct Comm {
     __device__ __forceinline__ void input_share(int kind, uint32_t id) {
         if (dead) return;
         const int n = S->geo[kind].gin;
-        const int r = gather_input<W8>(a, S, kind, n, id, 0, att_c);
+        const int r = gather_input<W8, XA>(a, S, kind, n, id, 0, att_c);
         if (r) fail(r);
     }
 
@@ -652,7 +657,7 @@ struct Comm {
             break;
         }
         case K_ATTN: {
-            const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = attn_item(a, att_c, wg) % D.Hkv;
+            const int Gq = D.H / D.Hkv, GW = (Gq + 1) * HD, g = attn_item<XA>(a, att_c, wg) % D.Hkv;
             const float qs = kLog2e / sqrtf((float)HD);
             const bool q16 = mfma_attention<MS>(D, a.pos0 + it.step + 1);
             gather(a.ex.qkv + (size_t)g * GW, GW, id_of(q - 1), [&](int i, uint32_t v) {
@@ -768,7 +773,7 @@ struct Comm {
             break;
         }
         case K_ATTN: {
-            const int r = attn_merge<HD>(a, S, pos, id, 0);   // the compute waves merge the other slices
+            const int r = attn_merge<HD, XA>(a, S, pos, id, 0);   // the compute waves merge the other slices
             if (r) fail(r);
             break;
         }
@@ -1008,7 +1013,7 @@ struct Comm {
             const int kind = kind_of(D, it);
             const int pos = a.pos0 + it.step;
             stamp(it.q, 0);
-            if (phase_bars(a, kind, it.step, wg)) {
+            if (phase_bars<XA>(a, kind, it.step, wg)) {
                 if (shared_gather(S, kind, it.layer)) wg_barrier();   // the previous phases are done
                 pre(kind, it);
                 wg_barrier();   // every wave's share of the input is staged
@@ -1151,7 +1156,7 @@ __device__ __forceinline__ void load_xf(KIE_LDS Smem* S, int off, float (&x)[8])
     x[7] = __builtin_bit_cast(float, u1.w);
 }
 
-template <int HD, int WF, bool MS>
+template <int HD, int WF, bool MS, bool XA>
 struct Compute {
     static constexpr bool W8 = WF != 0;   // quantised weights (fp8 or fp4)
     static constexpr bool W4 = WF == 2;   // fp4: four rows per unit
@@ -1318,12 +1323,12 @@ struct Compute {
 
     __device__ __forceinline__ void enter() {
         const int kind = kind_of(a.D, cc);
-        if (!phase_bars(a, kind, cc.step, wg)) return;
+        if (!phase_bars<XA>(a, kind, cc.step, wg)) return;
         if (shared_gather(S, kind, cc.layer)) {
             wg_barrier();   // the communication wave is done with the previous phases
             if (!stop) {
                 const int n = __builtin_amdgcn_readfirstlane(S->geo[kind].gin);
-                const int r = gather_input<W8>(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1,
+                const int r = gather_input<W8, XA>(a, S, kind, n, a.id0 + (uint32_t)(cc.q - 1), w + 1,
                                                a.pos0 + cc.step + 1);
                 if (r && lane == 0) {
                     if (r == 1) sys_store32(a.status, (uint32_t)kStatusTimeout);
@@ -1338,9 +1343,9 @@ struct Compute {
 
     __device__ __forceinline__ void finish() {
         const int kind = kind_of(a.D, cc);
-        if (!phase_bars(a, kind, cc.step, wg)) return;
+        if (!phase_bars<XA>(a, kind, cc.step, wg)) return;
         if (kind == K_ATTN && !stop && head_mode(a.D, a.pos0 + cc.step + 1)) {
-            const int it = attn_item(a, a.pos0 + cc.step + 1, wg);
+            const int it = attn_item<XA>(a, a.pos0 + cc.step + 1, wg);
             attention<1>(cc.layer, a.pos0 + cc.step, (it % a.D.H) / a.D.Hkv);   // one head, one chunk
         } else if (kind == K_ATTN && !stop) {
             const int G = a.D.H / a.D.Hkv, l = cc.layer, pos = a.pos0 + cc.step;
@@ -1359,7 +1364,7 @@ struct Compute {
         }
         wg_barrier();   // partial sums / attention states are in LDS
         if (kind == K_ATTN) {
-            if (!stop) (void)attn_merge<HD>(a, S, a.pos0 + cc.step, a.id0 + (uint32_t)cc.q, w + 1);   // no polls here
+            if (!stop) (void)attn_merge<HD, XA>(a, S, a.pos0 + cc.step, a.id0 + (uint32_t)cc.q, w + 1);   // no polls here
             wg_barrier();
         }
     }
@@ -1372,7 +1377,7 @@ struct Compute {
         static_assert(kNS >= 2, "the ring holds at least two batches");
         if (entered && sq[0].n > 0 && !stop && sq[0].q == cc.q && sq[1].q != cc.q) {
             // a GEMV phase (the batch had units): finishing it is its second barrier
-            if (phase_bars(a, kind_of(a.D, cc), cc.step, wg)) wg_barrier();
+            if (phase_bars<XA>(a, kind_of(a.D, cc), cc.step, wg)) wg_barrier();
             advance(a.D, cc);
             entered = false;
         }
@@ -1642,12 +1647,12 @@ struct Compute {
     }
 
     // fp4 weights, any row length: the inputs of each unit read from LDS, fours
-    // of rows per unit; MoE down as in consume_fp8 (ck = selected expert, its
-    // row partial sums scaled by that expert's row scales).
+    // of rows per unit. ED (MoE down) as in consume_fp8: ck = selected expert,
+    // its input segment and its row scales on the row partial sums.
+    template <bool ED>
     __device__ __forceinline__ void consume_fp4(uint32_t src, const Slot& sl) {
         const KIE_LDS uint8_t* wb = (const KIE_LDS uint8_t*)(uintptr_t)src + lane * 16;
         const int upr = cg.upr, nquad = cg.nrows / 4;
-        const bool edown = cg.kind == K_EDOWN;
         uint4 wv[kNB];
 #pragma unroll
         for (int s = 0; s < kNB; ++s)
@@ -1657,13 +1662,13 @@ struct Compute {
         for (int s = 0; s < kNB; ++s) {
             if (s < sl.n) {
                 float x[8];
-                load_xf(S, ck * cg.K + cseg * kUnitHalves + lane * 8, x);
+                load_xf(S, (ED ? ck * cg.K : 0) + cseg * kUnitHalves + lane * 8, x);
                 dot8_fp4(wv[s], x, acc, acc2, acc3, acc4);
                 const bool seg_done = cseg + 1 == upr;
                 if (seg_done || s == last) {
                     float r0 = wave_sum_to_lane63(acc), r1 = wave_sum_to_lane63(acc2);
                     float r2 = wave_sum_to_lane63(acc3), r3 = wave_sum_to_lane63(acc4);
-                    if (edown) {
+                    if constexpr (ED) {
                         const KIE_LDS float* e = S->esc + ck * cg.nrows + 4 * crow;
                         r0 *= e[0];
                         r1 *= e[1];
@@ -1680,7 +1685,8 @@ struct Compute {
                 }
                 if (seg_done) {
                     cseg = 0;
-                    if (++crow == nquad) {
+                    ++crow;
+                    if (ED && crow == nquad) {
                         crow = 0;
                         ++ck;
                     }
@@ -1694,7 +1700,8 @@ struct Compute {
     __device__ __forceinline__ void consume(uint32_t src, const Slot& sl) {
         if (cg.q != sl.q) enter_geo(sl);
         if constexpr (W4) {
-            consume_fp4(src, sl);
+            if (cg.kind == K_EDOWN) consume_fp4<true>(src, sl);
+            else consume_fp4<false>(src, sl);
             return;
         } else if constexpr (W8) {
             consume_fp8(src, sl);
@@ -1957,7 +1964,7 @@ struct Compute {
         if (hm) CH = ceil_div(c, head_chunks(a, c));
         else attn_split(c, a.items_per_head, &CH);
         const int Gq = (D.H / D.Hkv - h0 < GB) ? D.H / D.Hkv - h0 : GB;   // heads h0 .. h0 + Gq - 1
-        const int it = attn_item(a, c, wg);
+        const int it = attn_item<XA>(a, c, wg);
         const int g = it % D.Hkv, chunk = hm ? it / D.H : it / D.Hkv;
         const int p0 = chunk * CH, p1 = (p0 + CH < c) ? p0 + CH : c;
         const int gi = lane / LPP, dl = (lane % LPP) * 8;
@@ -2076,7 +2083,7 @@ struct Compute {
     }
 };
 
-template <int HD, int WF, bool MS>
+template <int HD, int WF, bool MS, bool XA>
 __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WgPlan W;
@@ -2085,7 +2092,7 @@ __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S
         if (threadIdx.x == 0) {
             S->abort = 0u;
             write_geo(a, W, blockIdx.x, S->geo);
-            if ((a.flags & F_XCD_ATTN) && xcc_id() != (int)blockIdx.x % kXcds) {
+            if (XA && xcc_id() != (int)blockIdx.x % kXcds) {
                 // XCD-local attention would exchange words between XCDs
                 // through L2 caches that do not see each other: refuse
                 sys_store32(a.status, kStatusWrongXcd);
@@ -2095,31 +2102,33 @@ __device__ __forceinline__ void kernel_body(const DecodeArgs& a, KIE_LDS Smem* S
     }
     __syncthreads();
     if (wave == 0) {
-        Comm<HD, WF, MS> cm(a, S, W);
+        Comm<HD, WF, MS, XA> cm(a, S, W);
         cm.run();
     } else {
-        Compute<HD, WF, MS> cp(a, S, wave - 1);
+        Compute<HD, WF, MS, XA> cp(a, S, wave - 1);
         cp.run();
     }
 }
 
 // Two symbols for the same code, so that profiles keep the prompt's passes
-// apart from the generation requests.
-template <int HD, int WF, bool MS>
+// apart from the generation requests. XA: built with the attention recomputed
+// per XCD (launched only in that mode; the other kernels carry none of it).
+template <int HD, int WF, bool MS, bool XA>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD, WF, MS>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, WF, MS, XA>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
 template <int HD, int WF, bool MS>
 __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(const DecodeArgs* __restrict__ ap) {
     __shared__ Smem smem_;
-    kernel_body<HD, WF, MS>(*ap, (KIE_LDS Smem*)&smem_);
+    kernel_body<HD, WF, MS, false>(*ap, (KIE_LDS Smem*)&smem_);
 }
 
-// The fp8-weight kernels are built for head_dim 128 only (the decoders whose
-// widths fp8 needs: every projection width a multiple of 512).
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bool prefill, int grid,
+// The quantised-weight kernels are built for head_dim 128 only (the decoders
+// whose widths fp8 and fp4 need: every projection width a multiple of 512).
+// With XCD-local attention (xa) the prompt's passes run the decode symbol.
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bool xa, bool prefill, int grid,
                          hipStream_t s) {
     void* args[] = {&dev_args};
     if ((wf != 0 || ms) && hd != 128) return hipErrorInvalidValue;
@@ -2127,16 +2136,22 @@ hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bo
     // hd 64: fp16 without the matrix-core split; hd 128: [weight format][ms]
     const void* fn;
     if (hd == 64) {
-        fn = prefill ? (const void*)prefill_kernel<64, 0, false> : (const void*)decode_kernel<64, 0, false>;
+        fn = xa ? (const void*)decode_kernel<64, 0, false, true>
+                : prefill ? (const void*)prefill_kernel<64, 0, false> : (const void*)decode_kernel<64, 0, false, false>;
+    } else if (xa) {
+        const void* t[3][2] = {{(const void*)decode_kernel<128, 0, false, true>, (const void*)decode_kernel<128, 0, true, true>},
+                               {(const void*)decode_kernel<128, 1, false, true>, (const void*)decode_kernel<128, 1, true, true>},
+                               {(const void*)decode_kernel<128, 2, false, true>, (const void*)decode_kernel<128, 2, true, true>}};
+        fn = t[wf][ms ? 1 : 0];
     } else if (prefill) {
         const void* t[3][2] = {{(const void*)prefill_kernel<128, 0, false>, (const void*)prefill_kernel<128, 0, true>},
                                {(const void*)prefill_kernel<128, 1, false>, (const void*)prefill_kernel<128, 1, true>},
                                {(const void*)prefill_kernel<128, 2, false>, (const void*)prefill_kernel<128, 2, true>}};
         fn = t[wf][ms ? 1 : 0];
     } else {
-        const void* t[3][2] = {{(const void*)decode_kernel<128, 0, false>, (const void*)decode_kernel<128, 0, true>},
-                               {(const void*)decode_kernel<128, 1, false>, (const void*)decode_kernel<128, 1, true>},
-                               {(const void*)decode_kernel<128, 2, false>, (const void*)decode_kernel<128, 2, true>}};
+        const void* t[3][2] = {{(const void*)decode_kernel<128, 0, false, false>, (const void*)decode_kernel<128, 0, true, false>},
+                               {(const void*)decode_kernel<128, 1, false, false>, (const void*)decode_kernel<128, 1, true, false>},
+                               {(const void*)decode_kernel<128, 2, false, false>, (const void*)decode_kernel<128, 2, true, false>}};
         fn = t[wf][ms ? 1 : 0];
     }
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);

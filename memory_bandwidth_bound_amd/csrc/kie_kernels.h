@@ -142,8 +142,10 @@ inline int phases_per_step(const Dims& D) { return D.L * phases_per_layer(D) + 2
 // wf (0 fp16, 1 FP8, 2 FP4; quantised formats with hd 128 only), and, for hd
 // 128, with the matrix-core split attention (ms) or without: the host takes
 // ms only for launches with a pass beyond head mode (head_mode_at), since
-// carrying that code costs the short-context passes about 1%.
-hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bool prefill, int grid,
+// carrying that code costs the short-context passes about 1%. xa: the
+// variant with attention recomputed per XCD (F_XCD_ATTN set), likewise kept
+// out of the other kernels.
+hipError_t launch_decode(const DecodeArgs* dev_args, int hd, int wf, bool ms, bool xa, bool prefill, int grid,
                          hipStream_t s);
 // Persistent GEMV with the decode kernel's LDS-DMA weight streaming (8 waves
 // per workgroup, a contiguous range of units per wave, row sums added into y,

@@ -317,6 +317,10 @@ XCD_CASES = {
     "gqa2_chunks_hd64": CASES["gqa2_chunks_hd64"],
     # 8 query heads per KV head (attention in two passes of 4 heads)
     "gqa8_hd64": CASES["gqa8_hd64"],
+    # 4 query heads at 1137..1168 positions: three chunks per head (12 items
+    # per XCD), then past 1152 the split over positions on the matrix cores
+    # (the kernel variant with it, launched with the XCD-local flag set)
+    "gqa4_long_hd128": CASES["gqa4_long_hd128"],
     # quantised weights: fp8 (16 query heads) and fp4 with folded gains
     "fp8_d2048": CASES["fp8_d2048"],
     "fp4_d512_gains": CASES["fp4_d512_gains"],
