@@ -74,6 +74,40 @@ def test_quantised_active_bytes_from_tensor_list():
         assert roofline.active_weight_bytes(c) == want
 
 
+def test_quantised_moe_active_bytes_from_tensor_list():
+    """fp8 / fp4 MoE: every non-expert projection and top_k of the n_experts
+    experts per layer at one byte or half a byte a weight, plus a 4-byte scale
+    per row read and one fp16 embedding row; counted from the tensor list."""
+    for name, per in (("moe_fp8", 1.0), ("moe_fp4", 0.5)):
+        c = synth.get_config(name)
+        weights = rows = 0.0
+        for n, s, k in synth.tensor_specs(c):
+            if k == "gain" or n == "E":
+                continue
+            share = c.top_k / c.n_experts if ".e" in n else 1.0   # expert matrices: the selected share
+            weights += share * int(np.prod(s))
+            rows += share * int(s[0])
+        want = int(round(weights * per)) + 4 * int(round(rows)) + 2 * c.d_model
+        assert roofline.active_weight_bytes(c) == want
+    # fp4 experts are a quarter of the fp16 bytes, so the fp4 MoE reads less
+    # than a third of the fp16 MoE's bytes per token
+    assert roofline.active_weight_bytes(synth.get_config("moe_fp4")) < \
+        roofline.active_weight_bytes(synth.get_config("moe")) / 3
+
+
+def test_bench_options_parse(root_dir):
+    """--attention takes only the two modes; --tokens and the attention mode
+    are accepted without touching a device (the GPU check comes later)."""
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, "bench.py", "--attention", "per_die"], cwd=root_dir, capture_output=True,
+                       text=True, timeout=300)
+    assert p.returncode == 2 and "--attention" in p.stderr
+    p = subprocess.run([sys.executable, "bench.py", "--help"], cwd=root_dir, capture_output=True, text=True,
+                       timeout=300)
+    assert p.returncode == 0 and "xcd_local" in p.stdout and "--tokens" in p.stdout and "moe_fp4" in p.stdout
+
+
 def test_moe_active_bytes_from_tensor_list():
     c5 = synth.get_config("C5")
     specs = synth.tensor_specs(c5)
