@@ -1773,17 +1773,9 @@ struct Compute {
         int head = 0;
 #pragma unroll
         for (int i = 0; i < kNS; ++i) sq[i] = fill(ring0 + i * kBatchBytes);
-#ifdef KIE_CTRACE
-        uint64_t tacc[4] = {0, 0, 0, 0};
-#define KIE_T(i) { const uint64_t t_ = __builtin_readcyclecounter(); tacc[i] += t_ - tlast; tlast = t_; }
-        uint64_t tlast = __builtin_readcyclecounter();
-#else
-#define KIE_T(i)
-#endif
         while (cc.q < Q) {
             const uint32_t at = ring0 + head * kBatchBytes;
             goto_phase(sq[0].q);   // sq[0].q == Q once nothing is left: finishes every phase
-            KIE_T(0)
             if (sq[0].n > 0 && !stop && sq[0].kind != K_EDOWN) {
                 // rows of at most 5 units share one input segment set: keep it in registers
                 const int upr = __builtin_amdgcn_readfirstlane(S->geo[sq[0].kind].K) / kUnitHalves;
@@ -1791,25 +1783,16 @@ struct Compute {
                 if (upr == 4) { stream_phase<4>(sq, head); continue; }
             }
             wait_vm<(kNS - 1) * kNB>();
-            KIE_T(1)
             if (sq[0].n > 0 && !stop) consume(at, sq[0]);
             wait_lgkm0();          // this batch's LDS reads are done before it is overwritten
             finish_if_done(sq);
-            KIE_T(2)
             const Slot t = fill(at);
-            KIE_T(3)
 #pragma unroll
             for (int i = 0; i + 1 < kNS; ++i) sq[i] = sq[i + 1];
             sq[kNS - 1] = t;
             head = (head + 1 == kNS) ? 0 : head + 1;
         }
         wait_vm0();
-#ifdef KIE_CTRACE
-        if ((a.flags & F_TRACE) && lane == 0)
-            for (int i = 0; i < 4; ++i)
-                gptr(a.trace)[((size_t)(kTracePhases - 8 + w) * kGrid + wg) * 4 + i] = (int64_t)tacc[i];
-#endif
-#undef KIE_T
     }
 
     // Split attention on the matrix cores (head_dim 128, at most 8 query heads
