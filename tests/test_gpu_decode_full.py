@@ -12,6 +12,9 @@ computes (dense: every logits row of the request compared element by element),
 the leading passes of a request (32K context, MoE), and the properties that
 hold at any size (a single launch equals the same passes split over several
 launches, bit for bit; MoE experts are the exact top-k of the router logits).
+The same checks run on the decoders with FP8 and FP4 weights (dense and MoE),
+and the ~2.1B decoder runs once more with attention recomputed per XCD, whose
+logits must equal the grid-wide mode's bit for bit.
 
 Teacher forcing uses the seeded token stream of `synth.make_forced_tokens`:
 pass i of a request is fed token i of the stream whatever pass i-1 produced.
