@@ -3,7 +3,7 @@
 //
 // For a dense and a top-k MoE configuration, with random fp16 weights and
 // non-unit RMSNorm gains, it unpacks every streaming block the repacker wrote
-// and checks, element by element:
+// and checks, element by element (quantised MoE experts: check_expert_quant):
 //  * every weight row lands exactly once, at the place this file works out on
 //    its own from the layout rules (rows split over 256 workgroups, each
 //    workgroup's rows of a layer contiguous in phase order; QKV rows with each
@@ -276,6 +276,76 @@ static int check_model(const kie_config& c, bool unit_gains) {
     return g_fail;
 }
 
+// Quantised MoE experts (repack_expert_quant): for every expert, each row's
+// codes and scale equal the row quantizer's output on that row (gate/up rows
+// with the folded gain, down rows without), at the place this file works out
+// from the unit rules: fp8 rows in pairs (unit column s of a pair: lane l
+// holds 8 codes of row a, then 8 of row b, columns 512 s + 8 l ..), fp4 rows in
+// fours (lane l holds 4 bytes per row, byte b = columns 512 s + 8 l + 2 b
+// (low nibble) and + 1 (high nibble)); gate/up rows interleaved g_p, u_p; the
+// down rows after the 2F gate/up rows; nothing written past expert_bytes.
+static int check_expert_quant(const kie_config& c) {
+    Model M = make_model(c, false);
+    std::string err;
+    CHECK(validate_config(c, &err) == KIE_OK, "quantised MoE config rejected: %s", err.c_str());
+    Layout* L = new Layout;
+    make_layout(c, L);
+    const int d = c.d_model, F = c.ffn_dim;
+    const bool fp4 = c.weight_format == KIE_WEIGHTS_FP4;
+    const int rpu = fp4 ? 4 : 2;                       // rows per unit column
+    const size_t want_bytes = (size_t)3 * F * d / (fp4 ? 2 : 1);
+    CHECK(L->expert_bytes == want_bytes, "expert_bytes %zu, want %zu", L->expert_bytes, want_bytes);
+    const int per_layer = 6 + 1 + 3 * c.n_experts;
+    std::vector<uint8_t> blk(L->expert_bytes + 4096);
+    std::vector<float> sc(2 * F + d + 16);
+    std::vector<uint8_t> q(8192);
+    for (int l = 0; l < c.n_layers; ++l)
+        for (int e = 0; e < c.n_experts; ++e) {
+            std::fill(blk.begin(), blk.end(), 0xA5);
+            std::fill(sc.begin(), sc.end(), -7.f);
+            repack_expert_quant(c, *L, M.p.data(), l, e, blk.data(), sc.data());
+            const uint16_t* g = M.t[1 + l * per_layer + 5].data();
+            const uint16_t* W[3];
+            for (int i = 0; i < 3; ++i) W[i] = M.t[1 + l * per_layer + 7 + 3 * e + i].data();
+            // virtual row v: gate/up v < 2F (g_{v/2} or u_{v/2}), down 2F + r
+            for (int v = 0; v < 2 * F + d; ++v) {
+                const bool gu = v < 2 * F;
+                const int K = gu ? d : F;
+                const uint16_t* src = gu ? W[v % 2] + (size_t)(v / 2) * d : W[2] + (size_t)(v - 2 * F) * F;
+                float s;
+                if (fp4) quantize_row_e2m1(src, gu ? g : nullptr, K, q.data(), &s);
+                else quantize_row_e4m3(src, gu ? g : nullptr, K, q.data(), &s);
+                CHECK(sc[v] == s, "layer %d expert %d row %d scale %g, want %g", l, e, v, sc[v], s);
+                const int local = gu ? v : v - 2 * F;            // row within its matrix block
+                const size_t base = gu ? 0 : (size_t)2 * F * d / (fp4 ? 2 : 1);
+                const size_t group = (size_t)(local / rpu) * K * rpu / (fp4 ? 2 : 1);   // bytes before its group
+                const int r = local % rpu;
+                for (int k = 0; k < K; ++k) {
+                    const int su = k / 512, ln = (k % 512) / 8, c8 = k % 8;
+                    uint8_t got;
+                    if (fp4) {
+                        const uint8_t byte = blk[base + group + ((size_t)su * 64 + ln) * 16 + 4 * r + c8 / 2];
+                        got = (c8 % 2) ? (byte >> 4) : (byte & 15);
+                    } else {
+                        got = blk[base + group + ((size_t)su * 64 + ln) * 16 + 8 * r + c8];
+                    }
+                    if (got != q[k]) {
+                        CHECK(false, "layer %d expert %d row %d col %d code %d, want %d", l, e, v, k, got, q[k]);
+                        break;
+                    }
+                }
+            }
+            CHECK(sc[2 * F + d] == -7.f, "scale written past the expert's rows");
+            for (size_t i = L->expert_bytes; i < blk.size(); ++i)
+                if (blk[i] != 0xA5) {
+                    CHECK(false, "byte %zu written past the expert block", i);
+                    break;
+                }
+        }
+    delete L;
+    return g_fail;
+}
+
 int main() {
     // fp16 <-> fp32
     for (uint32_t h = 0; h < 65536; ++h) {
@@ -300,6 +370,13 @@ int main() {
         check_model(moe, unit);
         check_model(tiny, unit);
     }
+    // quantised experts: fp8 (even expert count) and fp4 (experts in fours)
+    kie_config moe8 = {1, 512, 4, 2, 128, 1024, 700, 6, 2, 1e-5f, 1e4f, 64};
+    moe8.weight_format = KIE_WEIGHTS_FP8;
+    kie_config moe4 = {1, 1024, 8, 2, 128, 512, 704, 8, 2, 1e-5f, 1e4f, 64};
+    moe4.weight_format = KIE_WEIGHTS_FP4;
+    check_expert_quant(moe8);
+    check_expert_quant(moe4);
     if (g_fail) {
         std::printf("%d mismatches\n", g_fail);
         return 1;
