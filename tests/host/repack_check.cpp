@@ -346,6 +346,130 @@ static int check_expert_quant(const kie_config& c) {
     return g_fail;
 }
 
+// The codes of virtual row r (within its group of rpu rows, r % rpu) at
+// column k of a group that starts at byte base of blk, for a row length K:
+// the unit rules stated once more, as in check_expert_quant.
+static uint8_t code_at(const std::vector<uint8_t>& blk, size_t base, bool fp4, int r, int k) {
+    const int su = k / 512, ln = (k % 512) / 8, c8 = k % 8;
+    if (fp4) {
+        const uint8_t byte = blk[base + ((size_t)su * 64 + ln) * 16 + 4 * r + c8 / 2];
+        return (c8 % 2) ? (byte >> 4) : (byte & 15);
+    }
+    return blk[base + ((size_t)su * 64 + ln) * 16 + 8 * r + c8];
+}
+
+// Quantised layer blocks and LM head (repack_layer_fp8, repack_lm_fp8, both
+// formats): each workgroup's rows of each phase, in phase order and whole
+// groups (fp8 pairs, fp4 fours: QKV and gate/up in fours of rows, Wo, down and
+// the router and LM head in the format's group), carry the row quantizer's
+// codes of the row the layout rules name (gains folded as for fp16) and its
+// scale at the phase's offset in the layer's scale block; padding is zero and
+// nothing is written past a block.
+static int check_layer_quant(const kie_config& c) {
+    Model M = make_model(c, false);
+    std::string err;
+    CHECK(validate_config(c, &err) == KIE_OK, "quantised config rejected: %s", err.c_str());
+    Layout* L = new Layout;
+    make_layout(c, L);
+    const bool fp4 = c.weight_format == KIE_WEIGHTS_FP4;
+    const int rpu = fp4 ? 4 : 2, d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, hd = c.head_dim, F = c.ffn_dim;
+    const int per_layer = 6 + (c.n_experts ? 1 + 3 * c.n_experts : 3);
+    auto T = [&](int l, int which) { return M.t[1 + l * per_layer + which].data(); };
+    struct Ph { int M, K, gran, kind; };
+    std::vector<Ph> phases;
+    phases.push_back({(H + 2 * Hkv) * hd, d, 4, 0});
+    phases.push_back({d, H * hd, rpu, 1});
+    if (c.n_experts) phases.push_back({c.n_experts, d, rpu, 4});
+    else {
+        phases.push_back({2 * F, d, 4, 2});
+        phases.push_back({d, F, rpu, 3});
+    }
+    std::vector<uint8_t> q(8192);
+    const size_t guard = 1024;
+    std::vector<uint8_t> blk(L->layer_bytes + guard);
+    std::vector<float> sc(L->layer_scales + 16);
+    for (int l = 0; l < c.n_layers; ++l) {
+        std::fill(blk.begin(), blk.end(), 0xA5);
+        std::fill(sc.begin(), sc.end(), -7.f);
+        repack_layer_fp8(c, *L, M.p.data(), l, blk.data(), sc.data());
+        size_t pos = 0;   // bytes, walking the pieces in workgroup order
+        for (int w = 0; w < 256; ++w) {
+            CHECK(pos == (size_t)L->piece_off[w] * 1024, "piece %d starts at %zu", w, pos);
+            size_t sbase = 0;
+            for (const Ph& ph : phases) {
+                int r0, n;
+                my_split(ph.M, ph.gran, w, &r0, &n);
+                for (int j = 0; j < n; ++j) {
+                    const int r = r0 + j;
+                    const uint16_t* src;
+                    const uint16_t* g = nullptr;
+                    if (ph.kind == 0) {
+                        int mat, row;
+                        my_qkv_source(H, Hkv, hd, r, &mat, &row);
+                        src = T(l, 1 + mat) + (size_t)row * d;
+                        g = T(l, 0);
+                    } else if (ph.kind == 1) {
+                        src = T(l, 4) + (size_t)r * ph.K;
+                    } else if (ph.kind == 2) {
+                        src = T(l, (r % 2) ? 7 : 6) + (size_t)(r / 2) * d;
+                        g = T(l, 5);
+                    } else if (ph.kind == 3) {
+                        src = T(l, 8) + (size_t)r * ph.K;
+                    } else {
+                        src = T(l, 6) + (size_t)r * d;
+                        g = T(l, 5);
+                    }
+                    float s;
+                    if (fp4) quantize_row_e2m1(src, g, ph.K, q.data(), &s);
+                    else quantize_row_e4m3(src, g, ph.K, q.data(), &s);
+                    CHECK(sc[sbase + r] == s, "layer %d phase %d row %d scale %g, want %g", l, ph.kind, r,
+                          sc[sbase + r], s);
+                    const size_t gbase = pos + (size_t)(j / rpu) * ph.K * rpu / (fp4 ? 2 : 1);
+                    for (int k = 0; k < ph.K; ++k)
+                        if (code_at(blk, gbase, fp4, j % rpu, k) != q[k]) {
+                            CHECK(false, "layer %d wg %d phase %d row %d col %d", l, w, ph.kind, r, k);
+                            break;
+                        }
+                }
+                const size_t used = (size_t)n * ph.K / (fp4 ? 2 : 1), padded = (used + 1023) / 1024 * 1024;
+                for (size_t k = used; k < padded; ++k) CHECK(blk[pos + k] == 0, "padding not zero");
+                pos += padded;
+                sbase += ph.M;
+            }
+        }
+        CHECK(pos == L->layer_bytes, "layer block is %zu bytes, layout says %zu", pos, L->layer_bytes);
+        for (size_t k = 0; k < guard; ++k) CHECK(blk[L->layer_bytes + k] == 0xA5, "write past the layer block");
+        CHECK(sc[L->layer_scales] == -7.f, "scale written past the layer's scale block");
+    }
+    // LM head: rows in the format's groups, the final norm's gain folded
+    std::vector<uint8_t> lm(L->lm_bytes + guard, 0xA5);
+    std::vector<float> lsc(c.vocab + 16, -7.f);
+    repack_lm_fp8(c, *L, M.p.data(), lm.data(), lsc.data());
+    const uint16_t* Wlm = M.t.back().data();
+    const uint16_t* gf = M.t[M.t.size() - 2].data();
+    for (int w = 0; w < 256; ++w) {
+        int r0, n;
+        my_split(c.vocab, rpu, w, &r0, &n);
+        const size_t piece = (size_t)L->lm_off[w] * 1024;
+        for (int j = 0; j < n; ++j) {
+            float s;
+            if (fp4) quantize_row_e2m1(Wlm + (size_t)(r0 + j) * d, gf, d, q.data(), &s);
+            else quantize_row_e4m3(Wlm + (size_t)(r0 + j) * d, gf, d, q.data(), &s);
+            CHECK(lsc[r0 + j] == s, "LM row %d scale", r0 + j);
+            const size_t gbase = piece + (size_t)(j / rpu) * d * rpu / (fp4 ? 2 : 1);
+            for (int k = 0; k < d; ++k)
+                if (code_at(lm, gbase, fp4, j % rpu, k) != q[k]) {
+                    CHECK(false, "LM wg %d row %d col %d", w, r0 + j, k);
+                    break;
+                }
+        }
+    }
+    for (size_t k = 0; k < guard; ++k) CHECK(lm[L->lm_bytes + k] == 0xA5, "write past the LM block");
+    CHECK(lsc[c.vocab] == -7.f, "scale written past the LM rows");
+    delete L;
+    return g_fail;
+}
+
 int main() {
     // fp16 <-> fp32
     for (uint32_t h = 0; h < 65536; ++h) {
@@ -377,6 +501,16 @@ int main() {
     moe4.weight_format = KIE_WEIGHTS_FP4;
     check_expert_quant(moe8);
     check_expert_quant(moe4);
+    // quantised layer blocks and LM head: dense and MoE, both formats
+    kie_config dense8 = {2, 1024, 8, 2, 128, 1536, 1002, 0, 0, 1e-5f, 1e4f, 64};
+    dense8.weight_format = KIE_WEIGHTS_FP8;
+    kie_config dense4 = dense8;
+    dense4.vocab = 1004;
+    dense4.weight_format = KIE_WEIGHTS_FP4;
+    check_layer_quant(dense8);
+    check_layer_quant(dense4);
+    check_layer_quant(moe8);
+    check_layer_quant(moe4);
     if (g_fail) {
         std::printf("%d mismatches\n", g_fail);
         return 1;

@@ -3,7 +3,9 @@ AddressSanitizer and UndefinedBehaviorSanitizer and checked by
 tests/host/repack_check.cpp: every row lands once where the layout rules put
 it, the RMSNorm gains fold as W diag(g) rounded to fp16, padding is zero,
 nothing is written past a block, the rotary table and the fp16 conversions
-are exact. No GPU."""
+are exact; with FP8 and FP4 weights (dense and MoE layer blocks, the LM head
+and the experts) every row's codes and scale sit where the pair and four-row
+unit rules put them. No GPU."""
 import os
 import shutil
 import subprocess
