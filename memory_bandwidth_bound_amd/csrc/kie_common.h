@@ -8,7 +8,8 @@
 //    projection, so each residual element has exactly one owner),
 //  * the streaming unit: 1 KiB = one wave-wide 16-byte-per-lane load (fp16
 //    weights: 512 columns of one row; fp8 weights: 512 columns of a pair of
-//    rows, lane l holding 8 bytes of each),
+//    rows, lane l holding 8 bytes of each; fp4 weights: 512 columns of four
+//    rows, lane l holding 4 bytes of each),
 //  * the per-workgroup weight stream: for every layer, one contiguous piece
 //    holding that workgroup's rows of every phase in phase order, then its
 //    rows of the LM head.
@@ -128,7 +129,7 @@ KIE_HD PhaseShape phase_shape(const Dims& D, int ph) {
     case PH_WO: s.M = D.d; s.K = D.H * D.hd; s.gran = D.w4 ? 4 : 2; break;   // fp4: rows in fours
     case PH_GU: s.M = 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_DOWN: s.M = D.d; s.K = D.F; s.gran = D.w4 ? 4 : 2; break;
-    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: rows in pairs
+    case PH_ROUTER: s.M = D.E; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: pairs, fp4: fours
     case PH_LM: s.M = D.V; s.K = D.d; s.gran = D.w4 ? 4 : D.w8 ? 2 : 1; break;   // fp8: pairs, fp4: fours
     case PH_EGU: s.M = D.topk * 2 * D.F; s.K = D.d; s.gran = 4; break;
     case PH_EDOWN: s.M = D.d; s.K = D.F; s.gran = D.w4 ? 4 : 2; break;   // K per selected expert; = PH_WO

@@ -12,10 +12,12 @@
 //     workgroups through flagged words, normalises it into LDS, runs the
 //     phase epilogue (RoPE, KV-cache append, SwiGLU, residual add, argmax) and
 //     publishes the outputs as flagged words;
-//   waves 1..7 (compute): stream this workgroup's weights from HBM into
-//     registers with non-temporal 16-byte loads, two 12-unit batches in
-//     flight per wave, and take v_dot2 products against the LDS input; they
-//     also run the attention of the workgroups that hold an attention item.
+//   waves 1..7 (compute): stream this workgroup's weights from HBM into a
+//     per-wave LDS ring by LDS DMA (non-temporal 16-byte loads per lane), two
+//     batches of 8 units of 1 KiB in flight per wave, and take the dot
+//     products (v_dot2 on fp16, converted FP8 / FP4) against the LDS input;
+//     they also run the attention of the workgroups that hold an attention
+//     item.
 //     A batch is refilled as soon as it is consumed, with the next units in
 //     phase order, so weight streaming runs on across phase boundaries while
 //     the communication wave waits for the next input.
@@ -241,7 +243,7 @@ struct Smem {
     float own_x[kMaxOwnRows];                   // this workgroup's residual rows (fp32)
     uint32_t sel[16];                           // MoE: experts selected for the current layer
     float pi[16];                               //      and their router probabilities
-    float esc[16 * kMaxOwnRows];                // fp8 MoE: down-row scales [selected expert][own row]
+    float esc[16 * kMaxOwnRows];                // quantised MoE: down-row scales [selected expert][own row]
     Geo geo[K_COUNT];
     float ssp[kWaves];                          // per wave: sum of squares of its share of the input
     uint32_t abort;                             // set when the communication wave gave up
@@ -279,9 +281,9 @@ __device__ __forceinline__ void write_geo(const DecodeArgs& a, const WgPlan& W, 
 
 // Stage input element i in LDS as two fp16 terms: xin = fp16(v), xlo =
 // fp16(v - xin). A GEMV sums the products with both, so its input keeps about
-// 22 significant bits while every product is a v_dot2 of fp16 pairs. With fp8
-// weights (W8) the input is staged as fp32 over the same bytes (xf) and the
-// products are fp32 multiply-adds of converted weights.
+// 22 significant bits while every product is a v_dot2 of fp16 pairs. With
+// quantised weights (W8: fp8 or fp4) the input is staged as fp32 over the same
+// bytes (xf) and the products are fp32 multiply-adds of converted weights.
 __device__ __forceinline__ KIE_LDS float* xf_of(KIE_LDS Smem* S) { return (KIE_LDS float*)S->xin; }
 template <bool W8>
 __device__ __forceinline__ void stage1(KIE_LDS Smem* S, int i, float v) {
@@ -435,8 +437,8 @@ struct Comm {
     int att_c;     // positions the current pass attends
     bool dead;
     float rq[4];   // QKV epilogue: (cos, sin) of this lane's two rotary pairs, loaded before the input gather
-    float rs[4];   // fp8 weights: scales of the rows this lane's epilogue handles, loaded before the input gather
-    float esr[8];  // fp8 MoE: down-row scales of the selected experts (entry lane + 64 j), loaded after routing
+    float rs[4];   // quantised weights: scales of the rows this lane's epilogue handles, loaded before the gather
+    float esr[8];  // quantised MoE: down-row scales of the selected experts (entry lane + 64 j), after routing
 
     __device__ __forceinline__ Comm(const DecodeArgs& args, KIE_LDS Smem* s, const WgPlan& plan)
         : a(args), S(s), W(plan) {
@@ -474,7 +476,7 @@ struct Comm {
         if (r) fail(r);
     }
 
-    // fp8 weights: the row scales this lane's epilogue multiplies by. Row
+    // quantised weights: the row scales this lane's epilogue multiplies by. Row
     // r of lane e-th slot: QKV and gate/up 4 lane + e, Wo and down 2 lane + e,
     // LM lane + 64 e (the epilogues' row loops below). Read before the input
     // gather, so the trip overlaps it; rows past the phase read scale 1.
@@ -501,7 +503,7 @@ struct Comm {
             }
         }
     }
-    // fp8 MoE, right after routing: the gate/up row scales of this lane's
+    // quantised MoE, right after routing: the gate/up row scales of this lane's
     // epilogue rows (4 lane + e of the workgroup's virtual rows) and the
     // down-row scales of every selected expert (staged in LDS before the down
     // phase, for the compute waves).
@@ -1592,7 +1594,7 @@ struct Compute {
     __device__ __forceinline__ void enter_geo(const Slot& sl) {
         load_geo(cg, sl.q, sl.kind, sl.layer, sl.step);
         if (cg.upr) {
-            // crow counts rows (fp8: pairs of rows, two per unit)
+            // crow counts rows (fp8: pairs of rows, two per unit; fp4: fours)
             const int per_seg = (W4 ? cg.nrows / 4 : W8 ? cg.nrows / 2 : cg.nrows) * cg.upr;
             ck = cg.lo / per_seg;
             const int rem = cg.lo - ck * per_seg;

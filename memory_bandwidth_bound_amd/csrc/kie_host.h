@@ -52,7 +52,7 @@ struct Layout {
     size_t off_args;              // kernel argument block (4 KiB)
     size_t off_idle;              // 16 KiB read by weight batches that have nothing to stream
     size_t off_trace;             // i64 [kTracePhases][kGrid][4] phase timeline
-    size_t off_scales;            // fp8: f32 per layer [QKV rows][Wo rows][gate/up rows][down rows], then [V] LM
+    size_t off_scales;            // fp8/fp4: f32 per layer [QKV rows][Wo rows][gate/up rows][down rows], then [V] LM
     // batched prefill (dense fp16 models), chunks of kPrefillRows tokens
     size_t off_pf_x;              // f32 [R][d] residual
     size_t off_pf_a;              // f32 [R][max(d, H hd, F)] GEMM input
@@ -61,7 +61,7 @@ struct Layout {
     size_t off_pf_tok;            // i32 [R] tokens, then i32 [4] argmax
     size_t off_pf_slab;           // i32 [5][kGrid] slab offsets: QKV, Wo, gate/up, down (layer block), LM
     size_t layer_scales;          // floats per layer
-    size_t off_escales;           // fp8 MoE: f32 per (layer, expert) [2F gate/up rows][d down rows]
+    size_t off_escales;           // fp8/fp4 MoE: f32 per (layer, expert) [2F gate/up rows][d down rows]
     size_t total;
     int piece_off[kGrid + 1];     // units: start of workgroup w's piece in a layer block
     int lm_off[kGrid + 1];        // units: start of workgroup w's LM slab

@@ -81,9 +81,9 @@ struct DecodeArgs {
     const int32_t* plan;     // piece_off[kGrid+1], lm_off[kGrid+1]
     const uint8_t* idle;     // kIdleBytes of zeros: target of loads that keep a batch slot busy
     int64_t* trace;          // [kTracePhases][kGrid][4] phase timeline (F_TRACE)
-    const float* scales;     // fp8 weights: per layer [QKV][Wo][gate/up][down] row scales, then [V] LM
+    const float* scales;     // fp8/fp4 weights: per layer [QKV][Wo][gate/up][down] row scales, then [V] LM
     int32_t layer_scales;    // floats per layer in scales
-    const float* escales;    // fp8 MoE: per (layer, expert) [2F gate/up rows][d down rows] row scales
+    const float* escales;    // fp8/fp4 MoE: per (layer, expert) [2F gate/up rows][d down rows] row scales
     int32_t pos0;
     int32_t pending;
     int32_t n_steps;
