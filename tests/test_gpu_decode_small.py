@@ -326,6 +326,11 @@ XCD_CASES = {
     "fp4_d512_gains": CASES["fp4_d512_gains"],
     # MoE: 8 experts, top-2
     "moe_e8k2": MOE_CASES["moe_e8k2"],
+    # the most query heads the mode takes: 32, one item on every workgroup of
+    # each XCD (8 query heads per KV head)
+    "xcd_h32_hd128": synth.DecoderConfig(name="xcd_h32_hd128", n_layers=1, d_model=4096, n_heads=32,
+                                         n_kv_heads=4, head_dim=128, ffn_dim=512, vocab=2048, prompt_len=20,
+                                         decode_steps=12),
 }
 
 
